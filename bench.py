@@ -1,0 +1,238 @@
+"""Benchmark: keyed BLAKE3 of one device-resident buffer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload gib4|gib16|fp32_8192|mib1|batch64k]
+
+A step is one full hash (leaf pass + level passes, ROOT) of the workload's bytes, which
+are already in HBM when the timed region starts. Prints ONE JSON line on stdout:
+  value         input bytes / 1e9 / seconds per step (GB/s), whole job, one GPU
+  roofline      the dominant kernel (the leaf pass: chunk compression + fused in-workgroup
+                tree), timed alone with HIP events on the stream it runs on, against the
+                integer-VALU peak (it is ALU-bound; the HBM figure is reported beside it)
+  cpu_baseline  the CPU oracle on host threads over a bounded sample of the same bytes
+Everything else goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GB/s hashed, single keyed BLAKE3 of 4 GiB input; % of VALU/HBM roofline"
+
+# Integer VALU peak of MI355X: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz
+# = 39.32e12 32-bit lane operations per second (no packed 32-bit integer add exists).
+VALU_INT_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+HBM_PEAK_GBS = 8000.0
+# VALU lane-ops per compression on gfx950: 7 rounds x 8 quarter-rounds x 12 (2 v_add3_u32,
+# 2 v_add_u32, 4 v_xor_b32, 4 v_alignbit_b32) + 8 v_xor_b32 for the output fold.
+OPS_PER_COMPRESSION = 7 * 8 * 12 + 8
+LEAF_LANES = 256
+CPU_SHARE = 16  # host threads of one GPU's share on the benchmark machines
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def leaf_compressions(length):
+    """Compressions the leaf pass performs: every block of every chunk, plus the parents
+    inside each workgroup (a workgroup of k chunks has k-1)."""
+    if length == 0:
+        return 1
+    full, tail = divmod(length, 1024)
+    blocks = full * 16 + (0 if tail == 0 else (tail + 63) // 64)
+    n = full + (1 if tail else 0)
+    groups = (n + LEAF_LANES - 1) // LEAF_LANES
+    return blocks + (n - groups)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in ("b3_device.h", "b3_kernels.hip", "b3_kernels.h"):
+        with open(os.path.join(ROOT, "blake3_merkle_tree_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per leaf launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"leaf_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gib4")
+    ap.add_argument("--cpu-sample-gib", type=float, default=2.0)
+    ap.add_argument("--no-check", action="store_true", help="skip the full-digest oracle check")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the hash of one buffer "
+              "runs on a single device here. See the sharding notes in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import blake3_merkle_tree_amd as b3
+    from blake3_merkle_tree_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    batch = args.workload == "batch64k"
+    if batch:
+        base, offs, lengths, keys_cpu = workloads.uniform_batch(65536, 65536, dev)
+        keys = keys_cpu.to(dev)
+        nbytes = sum(lengths)
+        out = torch.empty((len(lengths), 32), dtype=torch.uint8, device=dev)
+
+        def step():
+            b3.keyed_hash_batch(base, offs, lengths, keys, out=out)
+        data = base
+    else:
+        data, key_t = workloads.single(args.workload, dev)
+        key = bytes(key_t.tolist())
+        nbytes = data.numel() * data.element_size()
+        out = torch.empty(32, dtype=torch.uint8, device=dev)
+
+        def step():
+            b3.keyed_hash(data, key, out=out)
+    torch.cuda.synchronize()
+    log(f"workload {args.workload}: {nbytes} bytes")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    value = nbytes / 1e9 / (ms_per_step / 1e3)
+    log(f"chain: {ms_per_step:.4f} ms/step ({value:.1f} GB/s), wall {wall:.3f} s for {args.steps} steps")
+
+    # the dominant kernel alone: the leaf pass, launched on the same stream
+    roofline = None
+    if not batch:
+        cvs = torch.empty(((nbytes + 1023) // 1024 + LEAF_LANES - 1) // LEAF_LANES, 8, dtype=torch.int32, device=dev)
+        for _ in range(args.warmup):
+            b3.group_cvs(data, key, out=cvs)
+        k0 = torch.cuda.Event(enable_timing=True)
+        k1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        k0.record(stream)
+        for _ in range(args.steps):
+            b3.group_cvs(data, key, out=cvs)
+        k1.record(stream)
+        torch.cuda.synchronize()
+        leaf_ms = k0.elapsed_time(k1) / args.steps
+        ops = leaf_compressions(nbytes) * OPS_PER_COMPRESSION
+        achieved = ops / (leaf_ms / 1e3) / 1e12
+        roofline = {
+            "bound": "alu",
+            "achieved": round(achieved, 3),
+            "peak": round(VALU_INT_PEAK_TOPS, 3),
+            "unit": "Tops/s (int32 VALU lane-ops)",
+            "frac": round(achieved / VALU_INT_PEAK_TOPS, 4),
+            "traffic": measured_traffic(args.workload),
+            "kernel": "leaf_single_kernel",
+            "kernel_ms": round(leaf_ms, 4),
+            "ops_per_launch": ops,
+            "hbm_gbs": round(nbytes / 1e9 / (leaf_ms / 1e3), 1),
+            "hbm_frac": round(nbytes / 1e9 / (leaf_ms / 1e3) / HBM_PEAK_GBS, 4),
+        }
+        log(f"leaf kernel: {leaf_ms:.4f} ms, {achieved:.2f} Tops/s = {achieved / VALU_INT_PEAK_TOPS:.1%} "
+            f"of the int-VALU peak; {nbytes / 1e9 / (leaf_ms / 1e3):.0f} GB/s")
+
+    digest_match = None
+    cpu = None
+    if not args.no_check or not args.no_cpu:
+        import oracle
+        cores = min(CPU_SHARE, os.cpu_count() or 1)
+        host = data.contiguous().view(torch.uint8).reshape(-1).cpu().numpy()
+        if not args.no_cpu:
+            sample = min(len(host), int(args.cpu_sample_gib * (1 << 30)))
+            c0 = time.perf_counter()
+            if batch:
+                per = 65536
+                oracle.hash_batch(host[:sample], [i * per for i in range(sample // per)], [per] * (sample // per),
+                                  keys_cpu.numpy().tobytes()[:32 * (sample // per)], nthreads=cores)
+            else:
+                oracle.hash_mt(host[:sample], key, cores)
+            c_s = time.perf_counter() - c0
+            cpu = {"value": round(sample / 1e9 / c_s, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                   "sample": f"first {sample} bytes of the same {args.workload} input, plain scalar C oracle "
+                             f"(multi-threaded aligned-subtree form), {c_s:.2f} s wall"}
+            log(f"cpu oracle: {cpu['value']} GB/s on {cores} threads ({sample} bytes)")
+        if not args.no_check:
+            if batch:
+                want = oracle.hash_batch(host, offs, lengths, keys_cpu.numpy().tobytes(), nthreads=cores)
+                digest_match = [bytes(r) for r in out.cpu().numpy()] == want
+            else:
+                digest_match = bytes(out.cpu().tolist()) == oracle.hash_mt(host, key, cores)
+            log(f"digest matches the oracle: {digest_match}")
+
+    cfg = {
+        "workload": {
+            "gib4": "one keyed BLAKE3 of 4 GiB + 1000 uniform random bytes (seed 3, key seed 13)",
+            "gib16": "one keyed BLAKE3 of 16 GiB + 777 uniform random bytes (seed 4, key seed 14)",
+            "fp32_8192": "one keyed BLAKE3 of an 8192x8192 fp32 N(0,1) tensor's bytes (seed 2, key seed 12)",
+            "mib1": "one keyed BLAKE3 of 1 MiB uniform random bytes (seed 0, key seed 1)",
+            "batch64k": "65,536 keyed BLAKE3 hashes of 64 KiB each (seed 4, key seed 14)",
+        }[args.workload],
+        "bytes": nbytes,
+        "chunks": (nbytes + 1023) // 1024,
+        "leaf_workgroup_chunks": LEAF_LANES,
+        "level_workgroup_cvs": 256,
+    }
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": cfg,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "digest_match": digest_match,
+        "hbm_frac_chain": round(value / HBM_PEAK_GBS, 4),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+"""BLAKE3 Merkle-tree hashing of GPU-resident buffers on MI355X (gfx950).
+
+Thin ctypes binding of ``libblake3_gpu.so`` (the C ABI in ``include/blake3_gpu.h``).
+PyTorch supplies device memory and streams only: every step of the hash runs in the
+library's HIP kernels. The functions mirror the C entry points:
+
+    hash(t)                              -> 32-byte digest tensor on t's device
+    keyed_hash(t, key)                   -> 32-byte digest tensor (key: 32 bytes)
+    keyed_hash_batch(base, offsets, lengths, keys=None) -> (n, 32) digest tensor
+
+A tensor is hashed as its raw bytes in memory order (a contiguous fp32 tensor as its
+little-endian element bytes). There is no CPU fallback: if the library is missing or
+no HIP device is present the calls raise.
+"""
+import ctypes
+import os
+import struct
+
+import torch
+
+__all__ = ["hash", "keyed_hash", "keyed_hash_batch", "group_cvs", "strerror", "version", "Blake3GpuError",
+           "library_path", "debug_plan_batch", "GROUP_CHUNKS"]
+
+GROUP_CHUNKS = 256
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libblake3_gpu.so")
+_lib = None
+
+OK, EINVAL, EALIGN, ENOMEM, EHIP, ETOOBIG = 0, -1, -2, -3, -4, -5
+
+
+class Blake3GpuError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python blake3_merkle_tree_amd/build.py")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, u64 = ctypes.c_void_p, ctypes.c_uint64
+    lib.blake3_gpu_hash.argtypes = [vp, u64, vp, vp]
+    lib.blake3_gpu_keyed_hash.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
+    lib.blake3_gpu_keyed_hash_batch.argtypes = [vp, ctypes.POINTER(u64), ctypes.POINTER(u64), vp, vp, u64, vp]
+    lib.blake3_gpu_group_cvs.argtypes = [vp, u64, u64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
+    lib.blake3_gpu_strerror.argtypes = [ctypes.c_int]
+    lib.blake3_gpu_strerror.restype = ctypes.c_char_p
+    lib.blake3_gpu_version.argtypes = []
+    lib.debug_plan = lib.blake3_gpu_debug_plan_batch
+    lib.debug_plan.argtypes = [ctypes.POINTER(u64), u64, ctypes.POINTER(u64), u64]
+    lib.debug_plan.restype = ctypes.c_int64
+    for f in ("blake3_gpu_hash", "blake3_gpu_keyed_hash", "blake3_gpu_keyed_hash_batch", "blake3_gpu_group_cvs",
+              "blake3_gpu_version"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return _load().blake3_gpu_strerror(int(status)).decode()
+
+
+def version() -> int:
+    return int(_load().blake3_gpu_version())
+
+
+def _check(rc, where):
+    if rc != OK:
+        raise Blake3GpuError(rc, where)
+
+
+def _device_bytes(t: torch.Tensor) -> torch.Tensor:
+    """The tensor's bytes as a contiguous, 16-byte-aligned device tensor (no copy if it
+    already is one)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError("the tensor must be on a HIP device")
+    if not t.is_contiguous():
+        t = t.contiguous()
+    if t.numel() and t.data_ptr() % 16 != 0:
+        t = t.clone()  # fresh allocations are 256-byte aligned
+    return t
+
+
+def _stream_handle(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _key_words(key):
+    if isinstance(key, torch.Tensor):
+        key = bytes(key.detach().to("cpu", torch.uint8).contiguous().numpy().tobytes())
+    key = bytes(key)
+    if len(key) != 32:
+        raise ValueError("BLAKE3 keys are 32 bytes")
+    return (ctypes.c_uint32 * 8)(*struct.unpack("<8I", key))
+
+
+def _out(out, device, n):
+    if out is None:
+        return torch.empty(n, dtype=torch.uint8, device=device)
+    if out.device != device or out.dtype != torch.uint8 or out.numel() != n or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous uint8 tensor of {n} bytes on {device}")
+    return out
+
+
+def hash(t: torch.Tensor, out=None, stream=None) -> torch.Tensor:  # noqa: A001
+    """Default-mode BLAKE3 of the tensor's bytes; returns a 32-byte uint8 device tensor."""
+    t = _device_bytes(t)
+    out = _out(out, t.device, 32)
+    nbytes = t.numel() * t.element_size()
+    with torch.cuda.device(t.device):
+        rc = _load().blake3_gpu_hash(ctypes.c_void_p(t.data_ptr() if nbytes else 0), nbytes,
+                                     ctypes.c_void_p(out.data_ptr()), _stream_handle(t.device, stream))
+    _check(rc, "blake3_gpu_hash")
+    return out
+
+
+def keyed_hash(t: torch.Tensor, key, out=None, stream=None) -> torch.Tensor:
+    """Keyed-mode BLAKE3 (key: 32 bytes) of the tensor's bytes; 32-byte device tensor."""
+    t = _device_bytes(t)
+    kw = _key_words(key)
+    out = _out(out, t.device, 32)
+    nbytes = t.numel() * t.element_size()
+    with torch.cuda.device(t.device):
+        rc = _load().blake3_gpu_keyed_hash(ctypes.c_void_p(t.data_ptr() if nbytes else 0), nbytes, kw,
+                                           ctypes.c_void_p(out.data_ptr()), _stream_handle(t.device, stream))
+    _check(rc, "blake3_gpu_keyed_hash")
+    return out
+
+
+def keyed_hash_batch(base: torch.Tensor, offsets, lengths, keys=None, out=None, stream=None) -> torch.Tensor:
+    """Hash messages base[offsets[i] : offsets[i] + lengths[i]] (byte offsets into the
+    tensor's bytes, multiples of 16). keys: None (default mode) or a device tensor with 32
+    bytes per message, shape (n, 32) uint8 or (n, 8) int32. Returns (n, 32) uint8."""
+    if not isinstance(base, torch.Tensor) or base.device.type != "cuda":
+        raise ValueError("base must be a tensor on a HIP device")
+    if not base.is_contiguous():
+        raise ValueError("base must be contiguous (offsets address its bytes)")
+    offs = (ctypes.c_uint64 * len(offsets))(*[int(x) for x in offsets])
+    lens = (ctypes.c_uint64 * len(lengths))(*[int(x) for x in lengths])
+    n = len(offs)
+    if len(lens) != n:
+        raise ValueError("offsets and lengths differ in size")
+    nbytes = base.numel() * base.element_size()
+    for o, l in zip(offs, lens):
+        if o + l > nbytes:
+            raise ValueError("a message runs past the end of base")
+    kp = ctypes.c_void_p(0)
+    if keys is not None:
+        if not isinstance(keys, torch.Tensor) or keys.device != base.device or not keys.is_contiguous():
+            raise ValueError("keys must be a contiguous tensor on base's device")
+        if keys.numel() * keys.element_size() != 32 * n:
+            raise ValueError("keys must hold 32 bytes per message")
+        kp = ctypes.c_void_p(keys.data_ptr())
+    out = _out(out, base.device, 32 * n).view(n, 32) if n else torch.empty((0, 32), dtype=torch.uint8,
+                                                                           device=base.device)
+    with torch.cuda.device(base.device):
+        rc = _load().blake3_gpu_keyed_hash_batch(ctypes.c_void_p(base.data_ptr() if nbytes else 0), offs, lens,
+                                                 kp, ctypes.c_void_p(out.data_ptr()),
+                                                 n, _stream_handle(base.device, stream))
+    _check(rc, "blake3_gpu_keyed_hash_batch")
+    return out
+
+
+def group_cvs(t: torch.Tensor, key=None, chunk_base: int = 0, out=None, stream=None) -> torch.Tensor:
+    """CVs (no ROOT) of the aligned 256-chunk groups of the tensor's bytes, chunk counters
+    starting at chunk_base: a (groups, 8) int32 device tensor of little-endian words."""
+    t = _device_bytes(t)
+    nbytes = t.numel() * t.element_size()
+    if nbytes == 0:
+        raise ValueError("group_cvs needs at least one byte")
+    groups = ((nbytes + 1023) // 1024 + GROUP_CHUNKS - 1) // GROUP_CHUNKS
+    if out is None:
+        out = torch.empty((groups, 8), dtype=torch.int32, device=t.device)
+    elif out.device != t.device or out.numel() * out.element_size() != 32 * groups or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous device tensor of {32 * groups} bytes")
+    kw = _key_words(key) if key is not None else None
+    with torch.cuda.device(t.device):
+        rc = _load().blake3_gpu_group_cvs(ctypes.c_void_p(t.data_ptr()), nbytes, int(chunk_base), kw,
+                                          ctypes.c_void_p(out.data_ptr()), _stream_handle(t.device, stream))
+    _check(rc, "blake3_gpu_group_cvs")
+    return out
+
+
+def debug_plan_batch(lengths):
+    """The batch planner's launch plan for messages of these byte lengths (no GPU work):
+    a list of passes, each a dict with lanes, in_cvs, out_cvs, wg_first_seg, wg_levels and
+    segs as (msg, first, dst, lane_start, count, final) tuples."""
+    lib = _load()
+    lens = (ctypes.c_uint64 * len(lengths))(*[int(x) for x in lengths])
+    need = lib.debug_plan(lens, len(lens), None, 0)
+    if need < 0:
+        raise Blake3GpuError(int(need), "blake3_gpu_debug_plan_batch")
+    buf = (ctypes.c_uint64 * need)()
+    lib.debug_plan(lens, len(lens), buf, need)
+    words = list(buf)
+    pos = 1
+    passes = []
+    for _ in range(words[0]):
+        lanes, nwg, nseg, in_cvs, out_cvs = words[pos:pos + 5]
+        pos += 5
+        first = words[pos:pos + nwg + 1]
+        pos += nwg + 1
+        levels = words[pos:pos + nwg]
+        pos += nwg
+        segs = []
+        for i in range(nseg):
+            msg, f, dst, info = words[pos + 4 * i:pos + 4 * i + 4]
+            segs.append((msg, f, dst, info & 0xFFF, ((info >> 12) & 0xFFF) + 1, bool(info >> 31)))
+        pos += 4 * nseg
+        passes.append(dict(lanes=lanes, in_cvs=in_cvs, out_cvs=out_cvs, wg_first_seg=first,
+                           wg_levels=levels, segs=segs))
+    return passes

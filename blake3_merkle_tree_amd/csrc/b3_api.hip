@@ -1,0 +1,327 @@
+// b3_api.hip - the C ABI (include/blake3_gpu.h): argument checks, launch planning,
+// stream-ordered scratch, kernel launches.
+//
+// The chain of launches is the one of the page "BLAKE3 on GPU: 400x faster hashing"
+// (qfminer.top), sections "Our implementation" and "Kernels 2 and 3": a leaf pass that
+// compresses every chunk and reduces each workgroup's chunks to one chaining value,
+// then level passes over those values until a single ROOT-flagged compression remains.
+// All launches go to the caller's stream; nothing here waits for the device.
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/blake3_gpu.h"
+#include "b3_device.h"
+#include "b3_kernels.h"
+#include "b3_plan.h"
+
+namespace b3g {
+namespace {
+
+constexpr int kAbiVersion = 1 * 10000 + 0 * 100 + 0;
+
+// Stream-ordered scratch comes from one memory pool per device, created on first use and
+// kept for the life of the process, with a release threshold of "never" so that freed
+// blocks are reused by the next call instead of being returned to the driver. Falls
+// back to the device's default pool if a pool cannot be created.
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[kMaxDevices] = {};
+bool g_pool_tried[kMaxDevices] = {};
+
+hipMemPool_t device_pool() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    if (!g_pool_tried[dev]) {
+        g_pool_tried[dev] = true;
+        hipMemPoolProps props{};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
+            uint64_t keep = UINT64_MAX;
+            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+            g_pools[dev] = pool;
+        } else {
+            (void)hipGetLastError();
+        }
+    }
+    return g_pools[dev];
+}
+
+// Scratch of one call: allocated and released in stream order on the caller's stream.
+class StreamScratch {
+  public:
+    explicit StreamScratch(hipStream_t s) : s_(s) {}
+    ~StreamScratch() {
+        if (p_) (void)hipFreeAsync(p_, s_);
+    }
+    int alloc(size_t bytes) {
+        if (bytes == 0) return B3G_OK;
+        hipMemPool_t pool = device_pool();
+        const hipError_t e = pool ? hipMallocFromPoolAsync(&p_, bytes, pool, s_) : hipMallocAsync(&p_, bytes, s_);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            p_ = nullptr;
+            return B3G_ENOMEM;
+        }
+        return B3G_OK;
+    }
+    uint8_t *get() const { return static_cast<uint8_t *>(p_); }
+
+  private:
+    hipStream_t s_;
+    void *p_ = nullptr;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int launched(hipError_t e) {
+    if (e == hipSuccess) return B3G_OK;
+    (void)hipGetLastError();
+    return B3G_EHIP;
+}
+
+// One message: leaf pass over ceil(n/256) workgroups, then level passes of 256 CVs per
+// workgroup until one remains. Pass outputs ping-pong between two CV arrays.
+int hash_single(const void *in, uint64_t len, const uint32_t key[8], uint32_t mode, void *out, void *stream) {
+    if (out == nullptr || (in == nullptr && len > 0)) return B3G_EINVAL;
+    if (reinterpret_cast<uintptr_t>(in) % 16 != 0) return B3G_EALIGN;
+    if (len > kMaxMessageBytes) return B3G_ETOOBIG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    const uint64_t n = chunks_of(len);
+    const uint64_t w0 = (n + kLeafLanes - 1) / kLeafLanes;
+    const uint64_t w1 = (w0 + kLevelLanes - 1) / kLevelLanes;
+
+    StreamScratch scratch(s);
+    uint32_t *cv_a = nullptr, *cv_b = nullptr;
+    if (w0 > 1) {
+        const size_t a_bytes = align256(w0 * 32);
+        int rc = scratch.alloc(a_bytes + align256(w1 * 32));
+        if (rc != B3G_OK) return rc;
+        cv_a = reinterpret_cast<uint32_t *>(scratch.get());
+        cv_b = reinterpret_cast<uint32_t *>(scratch.get() + a_bytes);
+    }
+
+    SingleLeafArgs la{};
+    la.in = static_cast<const uint8_t *>(in);
+    la.len = len;
+    la.n_chunks = n;
+    la.chunk_base = 0;
+    memcpy(la.key, key, sizeof(la.key));
+    la.mode = mode;
+    la.may_root = 1;
+    la.cv_out = cv_a;
+    la.digest = static_cast<uint8_t *>(out);
+    int rc = launched(launch_single_leaf(la, static_cast<uint32_t>(w0), s));
+    if (rc != B3G_OK) return rc;
+
+    uint64_t m = w0;
+    const uint32_t *src = cv_a;
+    uint32_t *dst = cv_b;
+    while (m > 1) {
+        const uint64_t w = (m + kLevelLanes - 1) / kLevelLanes;
+        SingleLevelArgs lv{};
+        lv.cv_in = src;
+        lv.m = m;
+        memcpy(lv.key, key, sizeof(lv.key));
+        lv.mode = mode;
+        lv.cv_out = dst;
+        lv.digest = static_cast<uint8_t *>(out);
+        rc = launched(launch_single_level(lv, static_cast<uint32_t>(w), s));
+        if (rc != B3G_OK) return rc;
+        m = w;
+        uint32_t *next_dst = const_cast<uint32_t *>(src);
+        src = dst;
+        dst = next_dst;
+    }
+    return B3G_OK;
+}
+
+// Leaf pass only: the CV of every aligned group of kLeafLanes chunks, chunk counters
+// starting at chunk_base, no ROOT anywhere.
+int group_cvs(const void *in, uint64_t len, uint64_t chunk_base, const uint32_t *key, void *out, void *stream) {
+    if (out == nullptr || len == 0 || in == nullptr) return B3G_EINVAL;
+    if (reinterpret_cast<uintptr_t>(in) % 16 != 0) return B3G_EALIGN;
+    if (len > kMaxMessageBytes) return B3G_ETOOBIG;
+    if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return B3G_EALIGN;
+    const uint64_t n = chunks_of(len);
+    if (chunk_base + n < chunk_base) return B3G_EINVAL;
+    SingleLeafArgs la{};
+    la.in = static_cast<const uint8_t *>(in);
+    la.len = len;
+    la.n_chunks = n;
+    la.chunk_base = chunk_base;
+    if (key) memcpy(la.key, key, sizeof(la.key));
+    else memcpy(la.key, kIV, sizeof(la.key));
+    la.mode = key ? kKeyedHash : 0u;
+    la.may_root = 0;
+    la.cv_out = static_cast<uint32_t *>(out);
+    la.digest = nullptr;
+    return launched(launch_single_leaf(la, static_cast<uint32_t>((n + kLeafLanes - 1) / kLeafLanes),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+template <class T>
+void append_bytes(std::vector<uint8_t> &img, size_t at, const std::vector<T> &v) {
+    if (!v.empty()) memcpy(img.data() + at, v.data(), v.size() * sizeof(T));
+}
+
+int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *lengths, const uint32_t *keys,
+               void *out, uint64_t n, void *stream) {
+    if (n == 0) return B3G_OK;
+    if (offsets == nullptr || lengths == nullptr || out == nullptr) return B3G_EINVAL;
+    if (reinterpret_cast<uintptr_t>(base) % 16 != 0) return B3G_EALIGN;
+    for (uint64_t i = 0; i < n; ++i) {
+        if (offsets[i] % 16 != 0) return B3G_EALIGN;
+        if (lengths[i] > kMaxMessageBytes) return B3G_ETOOBIG;
+        if (lengths[i] > 0 && base == nullptr) return B3G_EINVAL;
+        if (offsets[i] + lengths[i] < offsets[i]) return B3G_EINVAL;
+    }
+    BatchPlan plan;
+    int rc = plan_batch(lengths, n, kLeafLanes, kLevelLanes, &plan);
+    if (rc != B3G_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    // Scratch layout: message table, then per pass (segments, first-segment index, levels),
+    // then one CV array per pass output. Everything but the CV arrays is built on the host
+    // and copied with one transfer.
+    const size_t off_bytes = align256(n * 8);
+    size_t at = 0;
+    const size_t msg_off_at = at;
+    at += off_bytes;
+    const size_t msg_len_at = at;
+    at += off_bytes;
+    struct PassLayout {
+        size_t segs, first, levels, cv_out;
+    };
+    std::vector<PassLayout> lay(plan.passes.size());
+    for (size_t p = 0; p < plan.passes.size(); ++p) {
+        const PassPlan &pp = plan.passes[p];
+        lay[p].segs = at;
+        at += align256(pp.segs.size() * sizeof(Seg));
+        lay[p].first = at;
+        at += align256(pp.wg_first_seg.size() * sizeof(uint32_t));
+        lay[p].levels = at;
+        at += align256(pp.wg_levels.size());
+    }
+    const size_t table_bytes = at;
+    for (size_t p = 0; p < plan.passes.size(); ++p) {
+        lay[p].cv_out = at;
+        at += align256(plan.passes[p].out_cvs * 32);
+    }
+    std::vector<uint8_t> img(table_bytes, 0);
+    memcpy(img.data() + msg_off_at, offsets, n * 8);
+    memcpy(img.data() + msg_len_at, lengths, n * 8);
+    for (size_t p = 0; p < plan.passes.size(); ++p) {
+        append_bytes(img, lay[p].segs, plan.passes[p].segs);
+        append_bytes(img, lay[p].first, plan.passes[p].wg_first_seg);
+        append_bytes(img, lay[p].levels, plan.passes[p].wg_levels);
+    }
+
+    StreamScratch scratch(s);
+    rc = scratch.alloc(at);
+    if (rc != B3G_OK) return rc;
+    uint8_t *d = scratch.get();
+    if (hipMemcpyAsync(d, img.data(), table_bytes, hipMemcpyHostToDevice, s) != hipSuccess)
+        return launched(hipErrorUnknown);
+
+    for (size_t p = 0; p < plan.passes.size(); ++p) {
+        const PassPlan &pp = plan.passes[p];
+        const auto *segs = reinterpret_cast<const Seg *>(d + lay[p].segs);
+        const auto *first = reinterpret_cast<const uint32_t *>(d + lay[p].first);
+        const auto *levels = reinterpret_cast<const uint8_t *>(d + lay[p].levels);
+        auto *cv_out = reinterpret_cast<uint32_t *>(d + lay[p].cv_out);
+        if (p == 0) {
+            BatchLeafArgs a{static_cast<const uint8_t *>(base),
+                            reinterpret_cast<const uint64_t *>(d + msg_off_at),
+                            reinterpret_cast<const uint64_t *>(d + msg_len_at),
+                            keys, first, levels, segs, cv_out, static_cast<uint8_t *>(out)};
+            rc = launched(launch_batch_leaf(a, pp.workgroups(), s));
+        } else {
+            const auto *cv_in = reinterpret_cast<const uint32_t *>(d + lay[p - 1].cv_out);
+            BatchLevelArgs a{cv_in, keys, first, levels, segs, cv_out, static_cast<uint8_t *>(out)};
+            rc = launched(launch_batch_level(a, pp.workgroups(), s));
+        }
+        if (rc != B3G_OK) return rc;
+    }
+    return B3G_OK;
+}
+
+}  // namespace
+}  // namespace b3g
+
+extern "C" {
+
+int blake3_gpu_hash(const void *dev_in, uint64_t len, void *dev_out32, void *stream) {
+    return b3g::hash_single(dev_in, len, b3g::kIV, 0, dev_out32, stream);
+}
+
+int blake3_gpu_keyed_hash(const void *dev_in, uint64_t len, const uint32_t key[8], void *dev_out32,
+                          void *stream) {
+    if (key == nullptr) return B3G_EINVAL;
+    return b3g::hash_single(dev_in, len, key, b3g::kKeyedHash, dev_out32, stream);
+}
+
+int blake3_gpu_keyed_hash_batch(const void *dev_base, const uint64_t *host_offsets,
+                                const uint64_t *host_lengths, const uint32_t *dev_keys, void *dev_out,
+                                uint64_t n, void *stream) {
+    return b3g::hash_batch(dev_base, host_offsets, host_lengths, dev_keys, dev_out, n, stream);
+}
+
+int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, const uint32_t key[8],
+                         void *dev_cvs, void *stream) {
+    return b3g::group_cvs(dev_in, len, chunk_base, key, dev_cvs, stream);
+}
+
+const char *blake3_gpu_strerror(int status) {
+    switch (status) {
+        case B3G_OK: return "success";
+        case B3G_EINVAL: return "invalid argument (NULL pointer or offset overflow)";
+        case B3G_EALIGN: return "device input or batch offset is not 16-byte aligned";
+        case B3G_ENOMEM: return "scratch allocation failed";
+        case B3G_EHIP: return "HIP runtime call or kernel launch failed";
+        case B3G_ETOOBIG: return "request exceeds the supported size";
+        default: return "unknown status";
+    }
+}
+
+int blake3_gpu_version(void) { return b3g::kAbiVersion; }
+
+int64_t blake3_gpu_debug_plan_batch(const uint64_t *host_lengths, uint64_t n, uint64_t *out,
+                                    uint64_t out_words) {
+    if (n > 0 && host_lengths == nullptr) return B3G_EINVAL;
+    b3g::BatchPlan plan;
+    const int rc = b3g::plan_batch(host_lengths, n, b3g::kLeafLanes, b3g::kLevelLanes, &plan);
+    if (rc != B3G_OK) return rc;
+    std::vector<uint64_t> w;
+    w.push_back(plan.passes.size());
+    for (const b3g::PassPlan &p : plan.passes) {
+        w.push_back(p.lanes);
+        w.push_back(p.workgroups());
+        w.push_back(p.segs.size());
+        w.push_back(p.in_cvs);
+        w.push_back(p.out_cvs);
+        for (uint32_t f : p.wg_first_seg) w.push_back(f);
+        for (uint8_t l : p.wg_levels) w.push_back(l);
+        for (const b3g::Seg &g : p.segs) {
+            w.push_back(g.msg);
+            w.push_back(g.first);
+            w.push_back(g.dst);
+            w.push_back(g.info);
+        }
+    }
+    if (out != nullptr && out_words >= w.size()) memcpy(out, w.data(), w.size() * sizeof(uint64_t));
+    return static_cast<int64_t>(w.size());
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// b3_device.h - BLAKE3 compression on one gfx950 lane.
+//
+// The compression function of the page "BLAKE3 on GPU: 400x faster hashing" (qfminer.top),
+// section "Compression function": a 16-word state built from a 32-byte chaining value,
+// four IV words, the 64-bit counter, the block length and the flags, run through seven
+// rounds of add/xor/rotate quarter-rounds with the message words permuted from round to
+// round, then folded to an 8-word chaining value. Like the page's kernel, one lane runs a
+// whole compression in registers; the constants are the BLAKE3 specification's.
+//
+// gfx950 mapping: pure 32-bit integer VALU work. a+b+m is one v_add3_u32, each rotation
+// one v_alignbit_b32 (or v_perm_b32 for the byte-multiple amounts), each xor one
+// v_xor_b32: 12 VALU instructions per quarter-round, 680 per compression including the
+// final fold. Nothing here is a contraction, so the matrix cores are not used.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace b3g {
+
+constexpr uint32_t kChunkBytes = 1024;
+constexpr uint32_t kBlockBytes = 64;
+constexpr uint32_t kBlocksPerChunk = kChunkBytes / kBlockBytes;
+
+// Domain-separation flag bits (BLAKE3 specification's flag table).
+constexpr uint32_t kChunkStart = 1u << 0;
+constexpr uint32_t kChunkEnd = 1u << 1;
+constexpr uint32_t kParent = 1u << 2;
+constexpr uint32_t kRoot = 1u << 3;
+constexpr uint32_t kKeyedHash = 1u << 4;
+
+// Initial value: the first 32 bits of the fractional parts of the square roots of the
+// first eight primes.
+constexpr uint32_t kIV[8] = {0x6A09E667u, 0xBB67AE85u, 0x3C6EF372u, 0xA54FF53Au,
+                             0x510E527Fu, 0x9B05688Cu, 0x1F83D9ABu, 0x5BE0CD19u};
+
+// Message schedule. Between rounds BLAKE3 permutes the 16 message words (new word i is
+// old word kPerm[i]). Instead of moving registers, round r reads message word
+// kSchedule.at[r][i] at slot i, where at[0] is the identity and at[r+1][i] =
+// at[r][kPerm[i]]; after unrolling every index is a compile-time constant, so the
+// permutation costs no instructions.
+struct Schedule {
+    uint8_t at[7][16];
+};
+constexpr Schedule make_schedule() {
+    constexpr uint8_t kPerm[16] = {2, 6, 3, 10, 7, 0, 4, 13, 1, 11, 12, 5, 9, 14, 15, 8};
+    Schedule s{};
+    for (int i = 0; i < 16; ++i) s.at[0][i] = static_cast<uint8_t>(i);
+    for (int r = 1; r < 7; ++r)
+        for (int i = 0; i < 16; ++i) s.at[r][i] = s.at[r - 1][kPerm[i]];
+    return s;
+}
+constexpr Schedule kSchedule = make_schedule();
+
+__device__ __forceinline__ uint32_t rotr(uint32_t x, uint32_t k) {
+    return __builtin_amdgcn_alignbit(x, x, k);
+}
+
+// Quarter-round on (a, b, c, d) with message words x, y.
+__device__ __forceinline__ void quarter(uint32_t &a, uint32_t &b, uint32_t &c, uint32_t &d, uint32_t x,
+                                        uint32_t y) {
+    a = a + b + x;
+    d = rotr(d ^ a, 16);
+    c = c + d;
+    b = rotr(b ^ c, 12);
+    a = a + b + y;
+    d = rotr(d ^ a, 8);
+    c = c + d;
+    b = rotr(b ^ c, 7);
+}
+
+// Message word read at slot I of round R (a compile-time index, see kSchedule).
+template <int R, int I>
+__device__ __forceinline__ uint32_t mw(const uint32_t (&m)[16]) {
+    constexpr int k = kSchedule.at[R][I];
+    return m[k];
+}
+
+template <int R>
+__device__ __forceinline__ void round_r(uint32_t (&v)[16], const uint32_t (&m)[16]) {
+    // columns
+    quarter(v[0], v[4], v[8], v[12], mw<R, 0>(m), mw<R, 1>(m));
+    quarter(v[1], v[5], v[9], v[13], mw<R, 2>(m), mw<R, 3>(m));
+    quarter(v[2], v[6], v[10], v[14], mw<R, 4>(m), mw<R, 5>(m));
+    quarter(v[3], v[7], v[11], v[15], mw<R, 6>(m), mw<R, 7>(m));
+    // diagonals
+    quarter(v[0], v[5], v[10], v[15], mw<R, 8>(m), mw<R, 9>(m));
+    quarter(v[1], v[6], v[11], v[12], mw<R, 10>(m), mw<R, 11>(m));
+    quarter(v[2], v[7], v[8], v[13], mw<R, 12>(m), mw<R, 13>(m));
+    quarter(v[3], v[4], v[9], v[14], mw<R, 14>(m), mw<R, 15>(m));
+}
+
+// cv <- first half of compress(cv, m, counter, block_len, flags).
+__device__ __forceinline__ void compress(uint32_t (&cv)[8], const uint32_t (&m)[16], uint32_t counter_lo,
+                                         uint32_t counter_hi, uint32_t block_len, uint32_t flags) {
+    uint32_t v[16] = {cv[0],  cv[1],  cv[2],  cv[3],      cv[4],      cv[5],     cv[6],     cv[7],
+                      kIV[0], kIV[1], kIV[2], kIV[3], counter_lo, counter_hi, block_len, flags};
+    round_r<0>(v, m);
+    round_r<1>(v, m);
+    round_r<2>(v, m);
+    round_r<3>(v, m);
+    round_r<4>(v, m);
+    round_r<5>(v, m);
+    round_r<6>(v, m);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cv[i] = v[i] ^ v[i + 8];
+}
+
+}  // namespace b3g

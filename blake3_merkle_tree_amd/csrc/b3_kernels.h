@@ -1,0 +1,82 @@
+// b3_kernels.h - host-side view of the gfx950 kernels (argument blocks and launchers).
+//
+// Two kernel families, following the split of the page "BLAKE3 on GPU: 400x faster
+// hashing" (qfminer.top), sections "Our implementation", "Kernel 1" and "Kernels 2 and 3":
+//   leaf   - every lane compresses one 1 KiB chunk, then the workgroup reduces its chunk
+//            chaining values (CVs) as a fused partial Merkle tree and writes one CV per
+//            segment (or the digest, when the segment is a whole message).
+//   level  - every lane loads one CV of the previous level; the same in-workgroup tree
+//            reduction yields one CV per segment; the last launch sets ROOT.
+// A "segment" is an aligned group of consecutive tree nodes of one message that a
+// workgroup reduces to a single node. Because every split of the BLAKE3 tree over more
+// than 2^k nodes falls on a multiple of 2^k (left subtrees are complete powers of two),
+// reducing aligned power-of-two groups level by level reproduces the tree exactly.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "b3_plan.h"
+
+namespace b3g {
+
+// Lanes (= tree nodes) per workgroup. Both kernels use 256 lanes (4 wave64s).
+constexpr uint32_t kLeafLanes = 256;
+constexpr uint32_t kLevelLanes = 256;
+
+// Single message: segment geometry follows from blockIdx; the key is a kernel argument.
+struct SingleLeafArgs {
+    const uint8_t *in;     // message bytes (16-byte aligned)
+    uint64_t len;          // message length in bytes
+    uint64_t n_chunks;     // max(1, ceil(len / 1024))
+    uint64_t chunk_base;   // counter of chunk 0 (0 for a whole message)
+    uint32_t key[8];       // starting chaining value (key words, or the IV)
+    uint32_t mode;         // kKeyedHash or 0
+    uint32_t may_root;     // 1: a single workgroup is the whole message and emits the digest
+    uint32_t *cv_out;      // one 8-word CV per workgroup (subtree roots, never ROOT-flagged)
+    uint8_t *digest;       // 32-byte digest (when may_root and gridDim.x == 1)
+};
+
+struct SingleLevelArgs {
+    const uint32_t *cv_in; // m CVs, 8 words each
+    uint64_t m;
+    uint32_t key[8];
+    uint32_t mode;
+    uint32_t *cv_out;      // one CV per workgroup (when gridDim.x > 1)
+    uint8_t *digest;       // when gridDim.x == 1
+};
+
+// Batch mode: workgroups read their segments (struct Seg, b3_plan.h) from a task table.
+__host__ __device__ inline uint32_t seg_lane(uint32_t info) { return info & 0xFFFu; }
+__host__ __device__ inline uint32_t seg_count(uint32_t info) { return ((info >> 12) & 0xFFFu) + 1u; }
+__host__ __device__ inline bool seg_final(uint32_t info) { return (info & kSegFinal) != 0; }
+
+struct BatchLeafArgs {
+    const uint8_t *base;          // message buffer (16-byte aligned)
+    const uint64_t *msg_off;      // per message: byte offset from base
+    const uint64_t *msg_len;      // per message: byte length
+    const uint32_t *keys;         // per message 8 key words, or nullptr for default mode
+    const uint32_t *wg_first_seg; // workgroup w owns segments [wg_first_seg[w], wg_first_seg[w+1])
+    const uint8_t *wg_levels;     // workgroup w runs wg_levels[w] tree levels
+    const Seg *segs;
+    uint32_t *cv_out;             // next level array
+    uint8_t *digests;             // out + 32*msg for final segments
+};
+
+struct BatchLevelArgs {
+    const uint32_t *cv_in;        // current level array
+    const uint32_t *keys;
+    const uint32_t *wg_first_seg;
+    const uint8_t *wg_levels;
+    const Seg *segs;
+    uint32_t *cv_out;
+    uint8_t *digests;
+};
+
+hipError_t launch_single_leaf(const SingleLeafArgs &a, uint32_t grid, hipStream_t s);
+hipError_t launch_single_level(const SingleLevelArgs &a, uint32_t grid, hipStream_t s);
+hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t grid, hipStream_t s);
+hipError_t launch_batch_level(const BatchLevelArgs &a, uint32_t grid, hipStream_t s);
+
+}  // namespace b3g

@@ -1,0 +1,123 @@
+// b3_plan.cpp - batch planner (see b3_plan.h).
+//
+// Grouping. Pass 0 cuts message i (n_i chunks) into groups of L0 consecutive chunks
+// starting at chunk 0; pass t cuts the m_i CVs left by pass t-1 into groups of L
+// consecutive CVs. Every group is a complete power-of-two subtree except possibly the
+// last, and because the BLAKE3 tree splits any node over more than 2^k leaves at a
+// multiple of 2^k (page "BLAKE3 on GPU: 400x faster hashing", section "BLAKE3": the left
+// subtree is complete and at least as large as the right), the tree over the group
+// roots is the BLAKE3 tree of the message, one level up.
+//
+// Packing. A full group fills a workgroup alone. Smaller groups are sorted by the next
+// power of two R of their size (largest first) and laid out back to back; because the
+// sizes are non-increasing powers of two, every group then starts at a multiple of its
+// own R, which keeps the in-workgroup pairing from mixing groups.
+#include "b3_plan.h"
+
+#include <algorithm>
+
+namespace b3g {
+
+namespace {
+constexpr int kOk = 0;
+constexpr int kTooBig = -5;
+
+uint32_t next_pow2(uint32_t n) {
+    uint32_t r = 1;
+    while (r < n) r <<= 1;
+    return r;
+}
+
+struct Group {
+    uint32_t msg, first, count, dst;
+    bool final;
+};
+
+// Lays groups out over workgroups of `lanes` lanes.
+int pack(std::vector<Group> &groups, uint32_t lanes, PassPlan *p) {
+    p->lanes = lanes;
+    std::vector<Group> partial;
+    for (const Group &g : groups) {
+        if (g.count == lanes) {
+            p->wg_first_seg.push_back(static_cast<uint32_t>(p->segs.size()));
+            p->wg_levels.push_back(static_cast<uint8_t>(ceil_log2_host(g.count)));
+            p->segs.push_back(Seg{g.msg, g.first, g.dst, seg_info(0, g.count, g.final)});
+        } else {
+            partial.push_back(g);
+        }
+    }
+    std::stable_sort(partial.begin(), partial.end(),
+                     [](const Group &a, const Group &b) { return next_pow2(a.count) > next_pow2(b.count); });
+    uint32_t offset = lanes;  // forces a new workgroup for the first partial group
+    for (const Group &g : partial) {
+        const uint32_t r = next_pow2(g.count);
+        if (offset + r > lanes) {
+            p->wg_first_seg.push_back(static_cast<uint32_t>(p->segs.size()));
+            p->wg_levels.push_back(0);
+            offset = 0;
+        }
+        p->segs.push_back(Seg{g.msg, g.first, g.dst, seg_info(offset, g.count, g.final)});
+        uint8_t &lv = p->wg_levels.back();
+        lv = std::max<uint8_t>(lv, static_cast<uint8_t>(ceil_log2_host(g.count)));
+        offset += r;
+    }
+    if (p->segs.size() >= (1ull << 32) || p->wg_levels.size() >= (1ull << 31)) return kTooBig;
+    p->wg_first_seg.push_back(static_cast<uint32_t>(p->segs.size()));
+    return kOk;
+}
+}  // namespace
+
+uint64_t chunks_of(uint64_t len) { return len == 0 ? 1 : (len + 1023) / 1024; }
+
+uint32_t ceil_log2_host(uint64_t n) {
+    uint32_t r = 0;
+    while ((1ull << r) < n) ++r;
+    return r;
+}
+
+int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_t level_lanes,
+               BatchPlan *out) {
+    out->passes.clear();
+    if (n == 0) return kOk;
+    if (n >= (1ull << 32)) return kTooBig;
+    // nodes[i]: node count of message i entering the current pass (0 once finished)
+    std::vector<uint64_t> nodes(n);
+    for (uint64_t i = 0; i < n; ++i) {
+        if (lengths[i] > kMaxMessageBytes) return kTooBig;
+        nodes[i] = chunks_of(lengths[i]);
+    }
+    // in_base[i]: where message i's input CVs start in the current pass's input array
+    std::vector<uint64_t> in_base(n, 0), out_base(n, 0);
+    for (uint32_t pass = 0;; ++pass) {
+        const uint64_t lanes = pass == 0 ? leaf_lanes : level_lanes;
+        std::vector<Group> groups;
+        uint64_t out_cvs = 0;
+        for (uint64_t i = 0; i < n; ++i) {
+            if (nodes[i] == 0) continue;
+            const uint64_t ngroups = (nodes[i] + lanes - 1) / lanes;
+            const bool final = ngroups == 1;
+            out_base[i] = out_cvs;
+            if (!final) out_cvs += ngroups;
+            for (uint64_t k = 0; k < ngroups; ++k) {
+                const uint64_t first = (pass == 0 ? 0 : in_base[i]) + k * lanes;
+                const uint64_t count = std::min<uint64_t>(lanes, nodes[i] - k * lanes);
+                if (first >= (1ull << 32) || out_base[i] + k >= (1ull << 32)) return kTooBig;
+                groups.push_back(Group{static_cast<uint32_t>(i), static_cast<uint32_t>(first),
+                                       static_cast<uint32_t>(count),
+                                       final ? 0u : static_cast<uint32_t>(out_base[i] + k), final});
+            }
+            nodes[i] = final ? 0 : ngroups;
+        }
+        if (groups.empty()) break;
+        PassPlan p;
+        p.in_cvs = pass == 0 ? 0 : out->passes.back().out_cvs;
+        p.out_cvs = out_cvs;
+        const int rc = pack(groups, static_cast<uint32_t>(lanes), &p);
+        if (rc != kOk) return rc;
+        out->passes.push_back(std::move(p));
+        in_base.swap(out_base);
+    }
+    return kOk;
+}
+
+}  // namespace b3g

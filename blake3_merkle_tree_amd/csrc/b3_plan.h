@@ -1,0 +1,55 @@
+// b3_plan.h - host planner: how a hash (or a batch of hashes) maps onto kernel launches.
+//
+// Pure C++ (no HIP): the planner decides, for every launch ("pass"), which aligned
+// segments of tree nodes each workgroup reduces. Pass 0 is the leaf pass over chunks,
+// pass t > 0 reduces the chaining values written by pass t-1. A message whose segment in
+// some pass covers all of its remaining nodes is finished by that pass (its top
+// compression carries ROOT and its digest is written).
+#pragma once
+
+#include <stdint.h>
+
+#include <vector>
+
+namespace b3g {
+
+// Batch task table entry (mirrored byte for byte in device memory).
+struct Seg {
+    uint32_t msg;    // message index: key (keys + 8*msg) and digest slot (out + 32*msg)
+    uint32_t first;  // pass 0: first chunk index within the message; pass t: first input CV
+    uint32_t dst;    // index of the resulting CV in the pass's output array (if not final)
+    uint32_t info;   // bits 0..11 lane start, bits 12..23 node count - 1, bit 31 final
+};
+static_assert(sizeof(Seg) == 16, "Seg is a 16-byte table entry");
+
+constexpr uint32_t kSegFinal = 1u << 31;
+inline constexpr uint32_t seg_info(uint32_t lane, uint32_t count, bool final) {
+    return (lane & 0xFFFu) | (((count - 1) & 0xFFFu) << 12) | (final ? kSegFinal : 0u);
+}
+
+// Largest message accepted (bytes): chunk indices of a message fit in 32 bits.
+constexpr uint64_t kMaxMessageBytes = 1ull << 42;
+
+struct PassPlan {
+    uint32_t lanes = 0;                  // lanes (nodes) per workgroup in this pass
+    std::vector<Seg> segs;               // sorted by workgroup, then by lane start
+    std::vector<uint32_t> wg_first_seg;  // W + 1 entries
+    std::vector<uint8_t> wg_levels;      // W entries: ceil(log2(largest segment))
+    uint64_t in_cvs = 0;                 // size of the input CV array (passes > 0)
+    uint64_t out_cvs = 0;                // size of the output CV array
+    uint32_t workgroups() const { return static_cast<uint32_t>(wg_levels.size()); }
+};
+
+struct BatchPlan {
+    std::vector<PassPlan> passes;
+};
+
+uint64_t chunks_of(uint64_t len);       // max(1, ceil(len / 1024))
+uint32_t ceil_log2_host(uint64_t n);     // 0 for n <= 1
+
+// Builds the passes for messages of the given byte lengths. Returns 0 (B3G_OK) or a
+// negative b3g_status (B3G_ETOOBIG when a message or the task table exceeds the limits).
+int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_t level_lanes,
+               BatchPlan *out);
+
+}  // namespace b3g

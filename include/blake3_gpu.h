@@ -1,0 +1,143 @@
+/*
+ * blake3_gpu.h - C ABI of the MI355X (gfx950) BLAKE3 Merkle-tree hashing library.
+ *
+ * The library computes BLAKE3 digests (default or keyed mode, 32-byte output) of byte
+ * buffers that already sit in GPU memory, with every step on the GPU and no host I/O of
+ * the data. The operation is the one the page "BLAKE3 on GPU: 400x faster hashing"
+ * (qfminer.top) describes: sections "BLAKE3" (1 KiB chunks of chained 64-byte block
+ * compressions, keyed mode starting from the key, a binary tree of parent compressions
+ * whose left subtree is complete and at least as large as the right one) and "Our
+ * implementation" / "Kernels 2 and 3" (chunk compression fused with a partial tree
+ * reduction, then level reductions ending in the ROOT-flagged final compression). The
+ * requirements it meets are the introduction's: one GPU computation of a secure hash of
+ * a single large device-resident input, using the whole GPU, without host I/O.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named dev_* are device pointers (HIP device memory, e.g. a torch tensor's
+ *    data_ptr()); host_* and key are host pointers. The caller owns all of them; the
+ *    library never frees or retains them after the call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). All work is
+ *    enqueued on it; no entry point synchronises the host with the device. A digest is
+ *    in dev_out once the stream reaches that point; read it after a stream sync.
+ *  - Scratch (chaining values of intermediate tree levels, the batch task table) is
+ *    allocated and freed in stream order on `stream` from a memory pool the library
+ *    creates once per device and keeps (freed blocks are reused by later calls). Each
+ *    call owns its scratch, so calls on different streams may overlap.
+ *  - Arguments are checked before any HIP call. Errors are returned as negative
+ *    b3g_status values and nothing is enqueued; faults of the device work itself (e.g.
+ *    a dev_in that is not device memory) surface at the caller's next synchronisation.
+ *  - Digests are the 8 output words of the final compression as little-endian bytes.
+ */
+#ifndef BLAKE3_GPU_H
+#define BLAKE3_GPU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    B3G_OK = 0,
+    B3G_EINVAL = -1,  /* a required pointer is NULL, or a batch offset + length overflows */
+    B3G_EALIGN = -2,  /* dev_in / dev_base + offset is not 16-byte aligned */
+    B3G_ENOMEM = -3,  /* stream-ordered scratch allocation failed */
+    B3G_EHIP = -4,    /* a HIP runtime call or a kernel launch failed (incl. no device) */
+    B3G_ETOOBIG = -5, /* the request exceeds what the planner represents (see below) */
+} b3g_status;
+
+#define BLAKE3_GPU_KEY_WORDS 8
+#define BLAKE3_GPU_OUT_LEN 32
+
+/*
+ * Default-mode BLAKE3 of dev_in[0 .. len).
+ *   dev_in     device pointer, 16-byte aligned; may be NULL only when len == 0.
+ *   len        byte count, 0 .. 2^42 (4 TiB; ETOOBIG above, so chunk indices fit 32 bits).
+ *   dev_out32  device pointer to 32 writable bytes; receives the digest.
+ * Errors: EINVAL (dev_out32 NULL, or dev_in NULL with len > 0), EALIGN, ETOOBIG, ENOMEM,
+ * EHIP. The empty input is valid and yields the digest of one zero block of length 0.
+ */
+int blake3_gpu_hash(const void *dev_in, uint64_t len, void *dev_out32, void *stream);
+
+/*
+ * Keyed-mode BLAKE3 of dev_in[0 .. len) (page, section "BLAKE3": the key replaces the
+ * IV as the starting chaining value of every chunk and parent; KEYED_HASH is set on
+ * every compression).
+ *   key        host pointer to 8 uint32 words: the 32-byte key read as little-endian
+ *              words (byte 4*i is the low byte of key[i]). Copied by value into the
+ *              kernel arguments; the buffer may be reused as soon as the call returns.
+ * Other arguments and errors as blake3_gpu_hash; EINVAL also when key is NULL.
+ */
+int blake3_gpu_keyed_hash(const void *dev_in, uint64_t len, const uint32_t key[8], void *dev_out32,
+                          void *stream);
+
+/*
+ * Many independent messages in one call: message i is
+ * dev_base[host_offsets[i] .. host_offsets[i] + host_lengths[i]), hashed with its own key
+ * and its own tree (counters restart at 0, each message gets its own ROOT).
+ *   dev_base      device pointer, 16-byte aligned; may be NULL only if every length is 0.
+ *   host_offsets  host array of n byte offsets, each a multiple of 16. Messages may be
+ *                 in any order and may overlap (they are only read).
+ *   host_lengths  host array of n byte counts (each 0 .. 2^42).
+ *   dev_keys      device array of n*8 uint32 key words (message i's key at 8*i), or NULL
+ *                 for default (unkeyed) mode for every message.
+ *   dev_out       device pointer to n*32 writable bytes; digest i at byte 32*i.
+ *   n             message count, 0 .. 2^32-1 (0 enqueues nothing and returns B3G_OK).
+ * The host arrays are read during the call only (the task table built from them is
+ * copied to device scratch in stream order before the call returns).
+ * Errors: EINVAL (NULL arrays with n > 0, NULL dev_out, NULL dev_base with a non-empty
+ * message, offset + length overflowing 64 bits), EALIGN (misaligned dev_base or offset), ETOOBIG, ENOMEM, EHIP.
+ */
+int blake3_gpu_keyed_hash_batch(const void *dev_base, const uint64_t *host_offsets,
+                                const uint64_t *host_lengths, const uint32_t *dev_keys, void *dev_out,
+                                uint64_t n, void *stream);
+
+/* Chunks per group of blake3_gpu_group_cvs (a power of two). */
+#define BLAKE3_GPU_GROUP_CHUNKS 256
+
+/*
+ * The first tree level above the chunks that one workgroup produces: the chaining value
+ * (CV) of every aligned group of BLAKE3_GPU_GROUP_CHUNKS consecutive 1 KiB chunks of
+ * dev_in[0 .. len) (the last group may be shorter), with chunk counters starting at
+ * chunk_base and no ROOT flag anywhere. This is the page's first kernel on its own
+ * ("Kernel 1": compress every chunk, then a fused partial reduction to one root per
+ * block); each group CV is a node of the BLAKE3 tree of any larger input of which
+ * dev_in is the part starting at chunk chunk_base, provided chunk_base is a multiple of
+ * BLAKE3_GPU_GROUP_CHUNKS. Uses: hashing an input spread over several devices or
+ * produced piece by piece, and timing the chunk kernel alone.
+ *   dev_in     device pointer, 16-byte aligned, len > 0 bytes.
+ *   chunk_base counter of the first chunk of dev_in.
+ *   key        host pointer to 8 key words (keyed mode), or NULL (default mode).
+ *   dev_cvs    device pointer, 16-byte aligned, to ceil(ceil(len/1024)/256) * 32 bytes;
+ *              group g's CV (8 little-endian words) at byte 32*g.
+ * Errors: EINVAL (NULL dev_in or dev_cvs, len == 0, counter overflow), EALIGN, ETOOBIG,
+ * EHIP. Needs no scratch.
+ */
+int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, const uint32_t key[8],
+                         void *dev_cvs, void *stream);
+
+/* Static, human-readable text for a b3g_status value (never NULL). */
+const char *blake3_gpu_strerror(int status);
+
+/* Version of this ABI as major*10000 + minor*100 + patch. */
+int blake3_gpu_version(void);
+
+/*
+ * Inspection of the batch planner, for tests and tools (no GPU work, no HIP call).
+ * Plans the launches blake3_gpu_keyed_hash_batch would make for n messages of the given
+ * byte lengths and serialises the plan into out[0 .. out_words) as uint64 words:
+ *   [passes] then per pass [lanes, workgroups W, segments S, in_cvs, out_cvs,
+ *   W+1 first-segment indices, W level counts, S x (msg, first, dst, info)].
+ * Segment info packs bits 0..11 lane start, 12..23 node count - 1, 31 final.
+ * Returns the number of words the plan needs (nothing is written if out_words is
+ * smaller), or a negative b3g_status (EINVAL for NULL lengths with n > 0, ETOOBIG).
+ */
+int64_t blake3_gpu_debug_plan_batch(const uint64_t *host_lengths, uint64_t n, uint64_t *out,
+                                    uint64_t out_words);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLAKE3_GPU_H */

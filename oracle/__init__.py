@@ -42,6 +42,7 @@ def _load():
     lib.b3o_left_subtree_chunks.argtypes = [ctypes.c_uint64]
     lib.b3o_left_subtree_chunks.restype = ctypes.c_uint64
     lib.b3o_hash_recursive.argtypes = [_u8p, ctypes.c_uint64, _u8p, _u8p]
+    lib.b3o_subtree_cv.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_uint64, _u8p, _u32p]
     lib.b3o_hasher_new.argtypes = [_u8p]
     lib.b3o_hasher_new.restype = ctypes.c_void_p
     lib.b3o_hasher_free.argtypes = [ctypes.c_void_p]
@@ -125,6 +126,15 @@ def hash_recursive(data, key=None):
     out = (ctypes.c_uint8 * 32)()
     _load().b3o_hash_recursive(ptr, arr.size, kp, out)
     return bytes(out)
+
+
+def subtree_cv(data, chunk_base=0, key=None):
+    """8-word CV (no ROOT) of the subtree over all chunks of `data`, first counter chunk_base."""
+    arr, ptr = _as_u8(data)
+    _k, kp = _key(key)
+    out = (ctypes.c_uint32 * 8)()
+    _load().b3o_subtree_cv(ptr, arr.size, chunk_base, kp, out)
+    return list(out)
 
 
 def hash(data, key=None):  # noqa: A001 - mirrors the spec's name

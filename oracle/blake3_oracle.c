@@ -202,20 +202,21 @@ static uint64_t num_chunks(uint64_t len) {
     return len == 0 ? 1 : (len + B3O_CHUNK_LEN - 1) / B3O_CHUNK_LEN;
 }
 
-/* CV of the subtree over chunks [first, first+n) of the input; ROOT only at the top
- * of the whole tree. This is the recursive definition of the tree. */
-static void subtree_cv(const uint32_t kw[8], uint32_t mode, const uint8_t *data, uint64_t len,
+/* CV of the subtree over chunks [first, first+n) of the input, whose chunk 0 has counter
+ * `base`; ROOT only at the top of the whole tree. This is the recursive definition of
+ * the tree. */
+static void subtree_cv(const uint32_t kw[8], uint32_t mode, const uint8_t *data, uint64_t len, uint64_t base,
                        uint64_t first, uint64_t n, int is_root, uint32_t out[8]) {
     if (n == 1) {
         uint64_t off = first * B3O_CHUNK_LEN;
         uint64_t clen = len - off < B3O_CHUNK_LEN ? len - off : B3O_CHUNK_LEN;
-        b3o_chunk_cv(kw, mode, data + off, (size_t)clen, first, is_root, out);
+        b3o_chunk_cv(kw, mode, data + off, (size_t)clen, base + first, is_root, out);
         return;
     }
     uint64_t k = b3o_left_subtree_chunks(n);
     uint32_t l[8], r[8];
-    subtree_cv(kw, mode, data, len, first, k, 0, l);
-    subtree_cv(kw, mode, data, len, first + k, n - k, 0, r);
+    subtree_cv(kw, mode, data, len, base, first, k, 0, l);
+    subtree_cv(kw, mode, data, len, base, first + k, n - k, 0, r);
     b3o_parent_cv(kw, mode, l, r, is_root, out);
 }
 
@@ -227,8 +228,18 @@ static void words_to_bytes(const uint32_t w[8], uint8_t out32[32]) {
 void b3o_hash_recursive(const uint8_t *data, uint64_t len, const uint8_t *key32, uint8_t out32[32]) {
     uint32_t kw[8], mode, root[8];
     mode_setup(key32, kw, &mode);
-    subtree_cv(kw, mode, data, len, 0, num_chunks(len), 1, root);
+    subtree_cv(kw, mode, data, len, 0, 0, num_chunks(len), 1, root);
     words_to_bytes(root, out32);
+}
+
+/* CV (8 words, no ROOT) of the subtree formed by all chunks of data[0 .. len), where
+ * chunk 0 has counter chunk_base: a node of the tree of a larger input when data is an
+ * aligned part of it. key32 == NULL selects default mode. */
+void b3o_subtree_cv(const uint8_t *data, uint64_t len, uint64_t chunk_base, const uint8_t *key32,
+                    uint32_t out[8]) {
+    uint32_t kw[8], mode;
+    mode_setup(key32, kw, &mode);
+    subtree_cv(kw, mode, data, len, chunk_base, 0, num_chunks(len), 0, out);
 }
 
 /* ---- Incremental (stack-merge) form --------------------------------------------- */
@@ -336,7 +347,7 @@ static void *mt_worker(void *arg) {
         if (gidx >= job->n_groups) break;
         uint64_t first = gidx * job->group_chunks;
         uint64_t n = job->n_chunks - first < job->group_chunks ? job->n_chunks - first : job->group_chunks;
-        subtree_cv(job->kw, job->mode, job->data, job->len, first, n, 0, job->group_cv[gidx]);
+        subtree_cv(job->kw, job->mode, job->data, job->len, 0, first, n, 0, job->group_cv[gidx]);
     }
     return NULL;
 }

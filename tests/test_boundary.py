@@ -1,0 +1,99 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments with the documented status codes before it
+makes any HIP call (so these run on a machine with no device)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+import torch
+
+import blake3_merkle_tree_amd as b3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(blake3_gpu_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"blake3_gpu_hash", "blake3_gpu_keyed_hash", "blake3_gpu_keyed_hash_batch",
+            "blake3_gpu_strerror"} <= set(names)
+    lib = ctypes.CDLL(b3.library_path())
+    for n in names:
+        assert hasattr(lib, n), f"{n} is declared in include/ but not exported"
+
+
+def _lib():
+    lib = ctypes.CDLL(b3.library_path())
+    vp, u64 = ctypes.c_void_p, ctypes.c_uint64
+    lib.blake3_gpu_hash.argtypes = [vp, u64, vp, vp]
+    lib.blake3_gpu_keyed_hash.argtypes = [vp, u64, vp, vp, vp]
+    lib.blake3_gpu_keyed_hash_batch.argtypes = [vp, vp, vp, vp, vp, u64, vp]
+    return lib
+
+
+# Fake, never dereferenced addresses: every call below must return before touching them.
+ALIGNED = 0x10000
+MISALIGNED = 0x10004
+
+
+def test_single_argument_checks():
+    lib = _lib()
+    key = (ctypes.c_uint32 * 8)()
+    assert lib.blake3_gpu_hash(None, 5, ALIGNED, None) == b3.EINVAL
+    assert lib.blake3_gpu_hash(ALIGNED, 5, None, None) == b3.EINVAL
+    assert lib.blake3_gpu_hash(MISALIGNED, 5, ALIGNED, None) == b3.EALIGN
+    assert lib.blake3_gpu_hash(ALIGNED, (1 << 42) + 1, ALIGNED, None) == b3.ETOOBIG
+    assert lib.blake3_gpu_keyed_hash(ALIGNED, 5, None, ALIGNED, None) == b3.EINVAL
+    assert lib.blake3_gpu_keyed_hash(MISALIGNED, 5, ctypes.addressof(key), ALIGNED, None) == b3.EALIGN
+    assert lib.blake3_gpu_keyed_hash(ALIGNED, 1 << 43, ctypes.addressof(key), ALIGNED, None) == b3.ETOOBIG
+
+
+def test_batch_argument_checks():
+    lib = _lib()
+    offs = (ctypes.c_uint64 * 2)(0, 32)
+    lens = (ctypes.c_uint64 * 2)(10, 10)
+    o, ln = ctypes.addressof(offs), ctypes.addressof(lens)
+    assert lib.blake3_gpu_keyed_hash_batch(ALIGNED, o, ln, None, ALIGNED, 0, None) == b3.OK  # n == 0
+    assert lib.blake3_gpu_keyed_hash_batch(ALIGNED, None, ln, None, ALIGNED, 2, None) == b3.EINVAL
+    assert lib.blake3_gpu_keyed_hash_batch(ALIGNED, o, None, None, ALIGNED, 2, None) == b3.EINVAL
+    assert lib.blake3_gpu_keyed_hash_batch(ALIGNED, o, ln, None, None, 2, None) == b3.EINVAL
+    assert lib.blake3_gpu_keyed_hash_batch(MISALIGNED, o, ln, None, ALIGNED, 2, None) == b3.EALIGN
+    assert lib.blake3_gpu_keyed_hash_batch(None, o, ln, None, ALIGNED, 2, None) == b3.EINVAL
+    bad_offs = (ctypes.c_uint64 * 2)(0, 40)
+    assert lib.blake3_gpu_keyed_hash_batch(ALIGNED, ctypes.addressof(bad_offs), ln, None, ALIGNED, 2,
+                                           None) == b3.EALIGN
+    big = (ctypes.c_uint64 * 2)(10, (1 << 42) + 1)
+    assert lib.blake3_gpu_keyed_hash_batch(ALIGNED, o, ctypes.addressof(big), None, ALIGNED, 2,
+                                           None) == b3.ETOOBIG
+    wrap_offs = (ctypes.c_uint64 * 2)(0, (1 << 64) - 16)
+    wrap_lens = (ctypes.c_uint64 * 2)(10, 32)  # second message would wrap past 2^64
+    assert lib.blake3_gpu_keyed_hash_batch(ALIGNED, ctypes.addressof(wrap_offs), ctypes.addressof(wrap_lens),
+                                           None, ALIGNED, 2, None) == b3.EINVAL
+
+
+def test_strerror_and_version():
+    for code in (b3.OK, b3.EINVAL, b3.EALIGN, b3.ENOMEM, b3.EHIP, b3.ETOOBIG):
+        assert b3.strerror(code) and b3.strerror(code) != "unknown status"
+    assert b3.strerror(12345) == "unknown status"
+    assert b3.version() >= 10000
+
+
+def test_python_binding_rejects_host_tensors_and_bad_keys():
+    with pytest.raises(ValueError):
+        b3.hash(torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        b3.keyed_hash(torch.zeros(16, dtype=torch.uint8), bytes(32))
+    with pytest.raises(ValueError):
+        b3._key_words(b"short")
+    with pytest.raises(ValueError):
+        b3.keyed_hash_batch(torch.zeros(16, dtype=torch.uint8), [0], [16])

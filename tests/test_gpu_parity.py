@@ -1,0 +1,222 @@
+"""GPU parity: every digest of the HIP path equals the CPU oracle's, bit for bit.
+
+The HIP path is called through the C ABI (via the thin binding); the oracle hashes a host
+copy of the same device bytes. Cases: brute force over chunk counts and tail lengths
+(partial blocks, single-chunk roots, non-power-of-two trees, workgroup and level
+boundaries), the empty input, misaligned views, non-default streams, batches with gap
+bytes of 0xA5 between messages (an over-read changes the digest), and every workload at
+full size in the launch configuration the benchmark times.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TAILS = [1, 63, 64, 65, 1023, 1024]
+NTHREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module")
+def b3():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import blake3_merkle_tree_amd as mod
+    return mod
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+def _host(t):
+    torch.cuda.synchronize()
+    return t.contiguous().view(torch.uint8).reshape(-1).cpu().numpy()
+
+
+def _digests_to_bytes(d):
+    return [bytes(row) for row in d.cpu().numpy().reshape(-1, 32)]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def test_brute_force_lengths_single_call(b3, dev):
+    from blake3_merkle_tree_amd import workloads
+    buf = workloads.random_bytes(400 * 1024, 21, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(22)[0].tolist())
+    lengths = [0] + [(n - 1) * 1024 + t for n in range(1, 301) for t in TAILS] + \
+              [(n - 1) * 1024 + t for n in (384, 399, 400) for t in (1, 1024)]
+    for keyed in (True, False):
+        _say("brute force single-call, keyed =", keyed, "cases", len(lengths))
+        outs = torch.empty((len(lengths), 32), dtype=torch.uint8, device=dev)
+        for i, L in enumerate(lengths):
+            if keyed:
+                b3.keyed_hash(buf[:L], key, out=outs[i])
+            else:
+                b3.hash(buf[:L], out=outs[i])
+        got = _digests_to_bytes(outs)
+        want = oracle.hash_batch(host, [0] * len(lengths), lengths,
+                                 key * len(lengths) if keyed else None, nthreads=NTHREADS)
+        bad = [L for L, g, w in zip(lengths, got, want) if g != w]
+        assert not bad, f"{len(bad)} lengths differ, first {bad[:5]}"
+
+
+def test_level_boundaries(b3, dev):
+    # 256-chunk leaf workgroups and 256-CV level workgroups: counts around 256 and 256^2
+    from blake3_merkle_tree_amd import workloads
+    chunks = [255, 256, 257, 511, 512, 513, 65535, 65536, 65537, 131073]
+    buf = workloads.random_bytes(131073 * 1024, 23, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(24)[0].tolist())
+    lengths = [(n - 1) * 1024 + t for n in chunks for t in (1, 1000, 1024)]
+    _say("level boundaries", len(lengths), "cases")
+    outs = torch.empty((len(lengths), 32), dtype=torch.uint8, device=dev)
+    for i, L in enumerate(lengths):
+        b3.keyed_hash(buf[:L], key, out=outs[i])
+    want = oracle.hash_batch(host, [0] * len(lengths), lengths, key * len(lengths), nthreads=NTHREADS)
+    assert _digests_to_bytes(outs) == want
+
+
+def test_empty_and_dtypes_and_misaligned_views(b3, dev):
+    from blake3_merkle_tree_amd import workloads
+    key = bytes(workloads.key_bytes(25)[0].tolist())
+    empty = torch.empty(0, dtype=torch.uint8, device=dev)
+    assert bytes(b3.hash(empty).cpu().tolist()) == oracle.hash(b"")
+    assert bytes(b3.keyed_hash(empty, key).cpu().tolist()) == oracle.hash(b"", key)
+    buf = workloads.random_bytes(70000, 26, dev)
+    host = _host(buf)
+    for start in (1, 3, 8, 15, 16):  # views not 16-byte aligned are re-allocated by the binding
+        got = bytes(b3.keyed_hash(buf[start:], key).cpu().tolist())
+        assert got == oracle.hash(host[start:].tobytes(), key), start
+    f = torch.randn(3, 1000, 7, dtype=torch.float32, device=dev)
+    assert bytes(b3.keyed_hash(f, key).cpu().tolist()) == oracle.hash(_host(f).tobytes(), key)
+    ft = f.transpose(0, 2)  # non-contiguous: hashed as its contiguous copy
+    assert bytes(b3.hash(ft).cpu().tolist()) == oracle.hash(_host(ft.contiguous()).tobytes())
+
+
+def test_non_default_stream(b3, dev):
+    from blake3_merkle_tree_amd import workloads
+    key = bytes(workloads.key_bytes(27)[0].tolist())
+    s = torch.cuda.Stream(device=dev)
+    buf = workloads.random_bytes(3 * 1024 * 1024 + 7, 28, dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out = b3.keyed_hash(buf, key)
+    s.synchronize()
+    assert bytes(out.cpu().tolist()) == oracle.hash(_host(buf).tobytes(), key)
+
+
+def test_batch_mixed_lengths_with_gaps(b3, dev):
+    from blake3_merkle_tree_amd import workloads
+    rng = np.random.Generator(np.random.PCG64(29))
+    lengths = [0, 1, 63, 64, 65, 1023, 1024, 1025, 5000, 64 * 1024, 256 * 1024, 256 * 1024 + 1,
+               300 * 1024 + 5] + rng.integers(0, 400 * 1024, size=100).tolist() + [1] * 50
+    offs, total = workloads.pack_messages(lengths)
+    base = torch.full((total,), 0xA5, dtype=torch.uint8, device=dev)
+    data = workloads.random_bytes(total, 30, dev)
+    for o, L in zip(offs, lengths):
+        base[o:o + L] = data[o:o + L]
+    host = _host(base)
+    keys = workloads.key_bytes(31, len(lengths))
+    for keyed in (True, False):
+        _say("batch mixed, keyed =", keyed)
+        out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev) if keyed else None)
+        want = oracle.hash_batch(host, offs, lengths, keys.numpy().tobytes() if keyed else None,
+                                 nthreads=NTHREADS)
+        assert _digests_to_bytes(out) == want
+    # the batch equals one call per message
+    singles = [bytes(b3.keyed_hash(base[o:o + L], bytes(keys[i].tolist())).cpu().tolist())
+               for i, (o, L) in enumerate(zip(offs, lengths))]
+    assert singles == _digests_to_bytes(b3.keyed_hash_batch(base, offs, lengths, keys.to(dev)))
+
+
+def test_batch_deep_messages(b3, dev):
+    # messages with more than 256^2 chunks need a second level pass inside the batch
+    from blake3_merkle_tree_amd import workloads
+    lengths = [65537 * 1024 + 3, 12, 256 * 1024 * 3 + 17, 0]
+    offs, total = workloads.pack_messages(lengths)
+    base = workloads.random_bytes(total, 32, dev)
+    keys = workloads.key_bytes(33, len(lengths))
+    out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))
+    want = oracle.hash_batch(_host(base), offs, lengths, keys.numpy().tobytes(), nthreads=NTHREADS)
+    assert _digests_to_bytes(out) == want
+
+
+# ---- workloads at full size -------------------------------------------------------
+
+def _single_workload(b3, dev, name, repeats=1):
+    from blake3_merkle_tree_amd import workloads
+    t, key = workloads.single(name, dev)
+    key = bytes(key.tolist())
+    _say(name, "bytes", t.numel() * t.element_size())
+    digests = set()
+    for _ in range(repeats):
+        digests.add(bytes(b3.keyed_hash(t, key).cpu().tolist()))
+    assert len(digests) == 1, "repeated runs disagree"
+    host = _host(t)
+    del t
+    torch.cuda.empty_cache()
+    want = oracle.hash_mt(host, key, NTHREADS)
+    assert digests.pop() == want
+
+
+def test_workload_mib1(b3, dev):
+    _single_workload(b3, dev, "mib1", repeats=3)
+
+
+def test_workload_fp32_8192(b3, dev):
+    _single_workload(b3, dev, "fp32_8192", repeats=2)
+
+
+def test_workload_gib4(b3, dev):
+    _single_workload(b3, dev, "gib4", repeats=3)
+
+
+def test_workload_gib16(b3, dev):
+    _single_workload(b3, dev, "gib16")
+
+
+def test_workload_ragged256(b3, dev):
+    from blake3_merkle_tree_amd import workloads
+    base, offs, lengths, keys = workloads.ragged_batch(dev)
+    out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))
+    want = oracle.hash_batch(_host(base), offs, lengths, keys.numpy().tobytes(), nthreads=NTHREADS)
+    assert _digests_to_bytes(out) == want
+
+
+def test_workload_batch64k(b3, dev):
+    from blake3_merkle_tree_amd import workloads
+    base, offs, lengths, keys = workloads.uniform_batch(65536, 65536, dev)
+    out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))
+    again = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))
+    assert torch.equal(out, again)
+    host = _host(base)
+    del base
+    want = oracle.hash_batch(host, offs, lengths, keys.numpy().tobytes(), nthreads=NTHREADS)
+    assert _digests_to_bytes(out) == want
+
+
+def test_group_cvs_with_counter_offsets(b3, dev):
+    # the leaf pass alone: one CV per aligned 256-chunk group, no ROOT; chunk_base above
+    # 2^32 exercises the counter's high word
+    from blake3_merkle_tree_amd import workloads
+    buf = workloads.random_bytes(1000 * 1024 + 77, 34, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(35)[0].tolist())
+    G = b3.GROUP_CHUNKS * 1024
+    for base in (0, 256, (1 << 32) + 512, (1 << 40) - 1024):
+        for keyed in (True, False):
+            got = b3.group_cvs(buf, key if keyed else None, chunk_base=base).cpu().numpy().view(np.uint32)
+            assert got.shape == (4, 8)
+            for g in range(4):
+                want = oracle.subtree_cv(host[g * G:(g + 1) * G].tobytes(), base + g * b3.GROUP_CHUNKS,
+                                         key if keyed else None)
+                assert got[g].tolist() == want, (base, keyed, g)

@@ -247,3 +247,18 @@ def test_keyed_differs_from_default_and_flips_propagate():
         assert oracle.hash(bytes(data), bytes(k2)) != base
     # a trailing zero byte is not padding: length is part of the hash
     assert oracle.hash(bytes(data) + b"\0", bytes(key)) != base
+
+
+def test_subtree_cvs_compose_to_the_hash():
+    # a 3-way split 4096 + 2048 + 37 chunks of one input, each hashed as a subtree with its
+    # counter offset, reassembled by the tree rule, gives the whole-input digest
+    key = _rng_bytes(61, 32)
+    kw = _key_words(key)
+    data = _rng_bytes(62, 6181 * 1024 - 5)
+    a = oracle.subtree_cv(data[:4096 * 1024], 0, key)
+    b = oracle.subtree_cv(data[4096 * 1024:6144 * 1024], 4096, key)
+    c = oracle.subtree_cv(data[6144 * 1024:], 6144, key)
+    root = oracle.parent_cv(kw, oracle.KEYED_HASH, a, oracle.parent_cv(kw, oracle.KEYED_HASH, b, c), is_root=True)
+    assert struct.pack("<8I", *root) == oracle.hash(data, key)
+    # the counter offset matters
+    assert oracle.subtree_cv(data[4096 * 1024:6144 * 1024], 0, key) != b
