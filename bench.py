@@ -38,7 +38,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def leaf_compressions(length):
+def leaf_compressions(length, group_chunks):
     """Compressions the leaf pass performs: every block of every chunk, plus the parents
     inside each workgroup (a workgroup of k chunks has k-1)."""
     if length == 0:
@@ -46,7 +46,7 @@ def leaf_compressions(length):
     full, tail = divmod(length, 1024)
     blocks = full * 16 + (0 if tail == 0 else (tail + 63) // 64)
     n = full + (1 if tail else 0)
-    groups = (n + LEAF_LANES - 1) // LEAF_LANES
+    groups = (n + group_chunks - 1) // group_chunks
     return blocks + (n - groups)
 
 
@@ -81,8 +81,9 @@ def measured_traffic(workload):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU's clock settles only after ~100 ms of this load: warm up past that
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="gib4")
     ap.add_argument("--cpu-sample-gib", type=float, default=2.0)
     ap.add_argument("--no-check", action="store_true", help="skip the full-digest oracle check")
@@ -141,19 +142,20 @@ def main():
     # the dominant kernel alone: the leaf pass, launched on the same stream
     roofline = None
     if not batch:
-        cvs = torch.empty(((nbytes + 1023) // 1024 + LEAF_LANES - 1) // LEAF_LANES, 8, dtype=torch.int32, device=dev)
+        group = b3.leaf_group_chunks(nbytes)  # the leaf configuration the chain uses
+        cvs = torch.empty(((nbytes + 1023) // 1024 + group - 1) // group, 8, dtype=torch.int32, device=dev)
         for _ in range(args.warmup):
-            b3.group_cvs(data, key, out=cvs)
+            b3.group_cvs(data, key, group_chunks=group, out=cvs)
         k0 = torch.cuda.Event(enable_timing=True)
         k1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         k0.record(stream)
         for _ in range(args.steps):
-            b3.group_cvs(data, key, out=cvs)
+            b3.group_cvs(data, key, group_chunks=group, out=cvs)
         k1.record(stream)
         torch.cuda.synchronize()
         leaf_ms = k0.elapsed_time(k1) / args.steps
-        ops = leaf_compressions(nbytes) * OPS_PER_COMPRESSION
+        ops = leaf_compressions(nbytes, group) * OPS_PER_COMPRESSION
         achieved = ops / (leaf_ms / 1e3) / 1e12
         roofline = {
             "bound": "alu",
@@ -162,7 +164,7 @@ def main():
             "unit": "Tops/s (int32 VALU lane-ops)",
             "frac": round(achieved / VALU_INT_PEAK_TOPS, 4),
             "traffic": measured_traffic(args.workload),
-            "kernel": "leaf_single_kernel",
+            "kernel": f"leaf_single_kernel<{group // LEAF_LANES}>",
             "kernel_ms": round(leaf_ms, 4),
             "ops_per_launch": ops,
             "hbm_gbs": round(nbytes / 1e9 / (leaf_ms / 1e3), 1),
@@ -209,7 +211,7 @@ def main():
         }[args.workload],
         "bytes": nbytes,
         "chunks": (nbytes + 1023) // 1024,
-        "leaf_workgroup_chunks": LEAF_LANES,
+        "leaf_workgroup_chunks": b3.leaf_group_chunks(nbytes),
         "level_workgroup_cvs": 256,
     }
     rec = {

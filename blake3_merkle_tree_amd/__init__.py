@@ -18,10 +18,8 @@ import struct
 
 import torch
 
-__all__ = ["hash", "keyed_hash", "keyed_hash_batch", "group_cvs", "strerror", "version", "Blake3GpuError",
-           "library_path", "debug_plan_batch", "GROUP_CHUNKS"]
-
-GROUP_CHUNKS = 256
+__all__ = ["hash", "keyed_hash", "keyed_hash_batch", "group_cvs", "leaf_group_chunks", "strerror", "version",
+           "Blake3GpuError", "library_path", "debug_plan_batch"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libblake3_gpu.so")
@@ -52,7 +50,9 @@ def _load():
     lib.blake3_gpu_hash.argtypes = [vp, u64, vp, vp]
     lib.blake3_gpu_keyed_hash.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
     lib.blake3_gpu_keyed_hash_batch.argtypes = [vp, ctypes.POINTER(u64), ctypes.POINTER(u64), vp, vp, u64, vp]
-    lib.blake3_gpu_group_cvs.argtypes = [vp, u64, u64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
+    lib.blake3_gpu_group_cvs.argtypes = [vp, u64, u64, ctypes.POINTER(ctypes.c_uint32), ctypes.c_uint32, vp, vp]
+    lib.blake3_gpu_leaf_group_chunks.argtypes = [u64]
+    lib.blake3_gpu_leaf_group_chunks.restype = ctypes.c_uint32
     lib.blake3_gpu_strerror.argtypes = [ctypes.c_int]
     lib.blake3_gpu_strerror.restype = ctypes.c_char_p
     lib.blake3_gpu_version.argtypes = []
@@ -175,14 +175,21 @@ def keyed_hash_batch(base: torch.Tensor, offsets, lengths, keys=None, out=None, 
     return out
 
 
-def group_cvs(t: torch.Tensor, key=None, chunk_base: int = 0, out=None, stream=None) -> torch.Tensor:
-    """CVs (no ROOT) of the aligned 256-chunk groups of the tensor's bytes, chunk counters
-    starting at chunk_base: a (groups, 8) int32 device tensor of little-endian words."""
+def leaf_group_chunks(nbytes: int) -> int:
+    """Chunks per leaf workgroup the hash calls use for an input of nbytes bytes."""
+    return int(_load().blake3_gpu_leaf_group_chunks(int(nbytes)))
+
+
+def group_cvs(t: torch.Tensor, key=None, chunk_base: int = 0, group_chunks: int = 256, out=None,
+              stream=None) -> torch.Tensor:
+    """CVs (no ROOT) of the aligned groups of group_chunks chunks (256, 512 or 1024) of the
+    tensor's bytes, chunk counters starting at chunk_base: a (groups, 8) int32 device
+    tensor of little-endian words."""
     t = _device_bytes(t)
     nbytes = t.numel() * t.element_size()
     if nbytes == 0:
         raise ValueError("group_cvs needs at least one byte")
-    groups = ((nbytes + 1023) // 1024 + GROUP_CHUNKS - 1) // GROUP_CHUNKS
+    groups = ((nbytes + 1023) // 1024 + group_chunks - 1) // group_chunks
     if out is None:
         out = torch.empty((groups, 8), dtype=torch.int32, device=t.device)
     elif out.device != t.device or out.numel() * out.element_size() != 32 * groups or not out.is_contiguous():
@@ -190,15 +197,17 @@ def group_cvs(t: torch.Tensor, key=None, chunk_base: int = 0, out=None, stream=N
     kw = _key_words(key) if key is not None else None
     with torch.cuda.device(t.device):
         rc = _load().blake3_gpu_group_cvs(ctypes.c_void_p(t.data_ptr()), nbytes, int(chunk_base), kw,
-                                          ctypes.c_void_p(out.data_ptr()), _stream_handle(t.device, stream))
+                                          int(group_chunks), ctypes.c_void_p(out.data_ptr()),
+                                          _stream_handle(t.device, stream))
     _check(rc, "blake3_gpu_group_cvs")
     return out
 
 
 def debug_plan_batch(lengths):
     """The batch planner's launch plan for messages of these byte lengths (no GPU work):
-    a list of passes, each a dict with lanes, in_cvs, out_cvs, wg_first_seg, wg_levels and
-    segs as (msg, first, dst, lane_start, count, final) tuples."""
+    a list of passes, each a dict with lanes, chunks_per_lane, in_cvs, out_cvs,
+    wg_first_seg, wg_levels and segs as (msg, first, dst, lane_start, nodes, final)
+    tuples (pass 0: `first` is a chunk index and a node covers chunks_per_lane chunks)."""
     lib = _load()
     lens = (ctypes.c_uint64 * len(lengths))(*[int(x) for x in lengths])
     need = lib.debug_plan(lens, len(lens), None, 0)
@@ -210,8 +219,8 @@ def debug_plan_batch(lengths):
     pos = 1
     passes = []
     for _ in range(words[0]):
-        lanes, nwg, nseg, in_cvs, out_cvs = words[pos:pos + 5]
-        pos += 5
+        lanes, cpl, nwg, nseg, in_cvs, out_cvs = words[pos:pos + 6]
+        pos += 6
         first = words[pos:pos + nwg + 1]
         pos += nwg + 1
         levels = words[pos:pos + nwg]
@@ -221,6 +230,6 @@ def debug_plan_batch(lengths):
             msg, f, dst, info = words[pos + 4 * i:pos + 4 * i + 4]
             segs.append((msg, f, dst, info & 0xFFF, ((info >> 12) & 0xFFF) + 1, bool(info >> 31)))
         pos += 4 * nseg
-        passes.append(dict(lanes=lanes, in_cvs=in_cvs, out_cvs=out_cvs, wg_first_seg=first,
-                           wg_levels=levels, segs=segs))
+        passes.append(dict(lanes=lanes, chunks_per_lane=cpl, in_cvs=in_cvs, out_cvs=out_cvs,
+                           wg_first_seg=first, wg_levels=levels, segs=segs))
     return passes

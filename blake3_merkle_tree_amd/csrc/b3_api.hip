@@ -12,7 +12,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/blake3_gpu.h"
+#include "blake3_gpu.h"
 #include "b3_device.h"
 #include "b3_kernels.h"
 #include "b3_plan.h"
@@ -99,7 +99,8 @@ int hash_single(const void *in, uint64_t len, const uint32_t key[8], uint32_t mo
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     const uint64_t n = chunks_of(len);
-    const uint64_t w0 = (n + kLeafLanes - 1) / kLeafLanes;
+    const uint32_t k = choose_chunks_per_lane(n);
+    const uint64_t w0 = (n + kLeafLanes * k - 1) / (kLeafLanes * k);
     const uint64_t w1 = (w0 + kLevelLanes - 1) / kLevelLanes;
 
     StreamScratch scratch(s);
@@ -122,7 +123,7 @@ int hash_single(const void *in, uint64_t len, const uint32_t key[8], uint32_t mo
     la.may_root = 1;
     la.cv_out = cv_a;
     la.digest = static_cast<uint8_t *>(out);
-    int rc = launched(launch_single_leaf(la, static_cast<uint32_t>(w0), s));
+    int rc = launched(launch_single_leaf(la, k, use_lds_staging(), static_cast<uint32_t>(w0), s));
     if (rc != B3G_OK) return rc;
 
     uint64_t m = w0;
@@ -147,13 +148,16 @@ int hash_single(const void *in, uint64_t len, const uint32_t key[8], uint32_t mo
     return B3G_OK;
 }
 
-// Leaf pass only: the CV of every aligned group of kLeafLanes chunks, chunk counters
-// starting at chunk_base, no ROOT anywhere.
-int group_cvs(const void *in, uint64_t len, uint64_t chunk_base, const uint32_t *key, void *out, void *stream) {
+// Leaf pass only: the CV of every aligned group of group_chunks (= kLeafLanes * K)
+// chunks, chunk counters starting at chunk_base, no ROOT anywhere.
+int group_cvs(const void *in, uint64_t len, uint64_t chunk_base, const uint32_t *key, uint32_t group_chunks,
+              void *out, void *stream) {
     if (out == nullptr || len == 0 || in == nullptr) return B3G_EINVAL;
-    if (reinterpret_cast<uintptr_t>(in) % 16 != 0) return B3G_EALIGN;
+    if (group_chunks != kLeafLanes && group_chunks != 2 * kLeafLanes && group_chunks != 4 * kLeafLanes)
+        return B3G_EINVAL;
+    if (reinterpret_cast<uintptr_t>(in) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
+        return B3G_EALIGN;
     if (len > kMaxMessageBytes) return B3G_ETOOBIG;
-    if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return B3G_EALIGN;
     const uint64_t n = chunks_of(len);
     if (chunk_base + n < chunk_base) return B3G_EINVAL;
     SingleLeafArgs la{};
@@ -167,7 +171,8 @@ int group_cvs(const void *in, uint64_t len, uint64_t chunk_base, const uint32_t 
     la.may_root = 0;
     la.cv_out = static_cast<uint32_t *>(out);
     la.digest = nullptr;
-    return launched(launch_single_leaf(la, static_cast<uint32_t>((n + kLeafLanes - 1) / kLeafLanes),
+    return launched(launch_single_leaf(la, group_chunks / kLeafLanes, use_lds_staging(),
+                                       static_cast<uint32_t>((n + group_chunks - 1) / group_chunks),
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -187,8 +192,10 @@ int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *length
         if (lengths[i] > 0 && base == nullptr) return B3G_EINVAL;
         if (offsets[i] + lengths[i] < offsets[i]) return B3G_EINVAL;
     }
+    uint64_t total_chunks = 0;
+    for (uint64_t i = 0; i < n; ++i) total_chunks += chunks_of(lengths[i]);
     BatchPlan plan;
-    int rc = plan_batch(lengths, n, kLeafLanes, kLevelLanes, &plan);
+    int rc = plan_batch(lengths, n, kLeafLanes, choose_chunks_per_lane(total_chunks), kLevelLanes, &plan);
     if (rc != B3G_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -246,7 +253,7 @@ int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *length
                             reinterpret_cast<const uint64_t *>(d + msg_off_at),
                             reinterpret_cast<const uint64_t *>(d + msg_len_at),
                             keys, first, levels, segs, cv_out, static_cast<uint8_t *>(out)};
-            rc = launched(launch_batch_leaf(a, pp.workgroups(), s));
+            rc = launched(launch_batch_leaf(a, pp.chunks_per_lane, use_lds_staging(), pp.workgroups(), s));
         } else {
             const auto *cv_in = reinterpret_cast<const uint32_t *>(d + lay[p - 1].cv_out);
             BatchLevelArgs a{cv_in, keys, first, levels, segs, cv_out, static_cast<uint8_t *>(out)};
@@ -279,8 +286,12 @@ int blake3_gpu_keyed_hash_batch(const void *dev_base, const uint64_t *host_offse
 }
 
 int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, const uint32_t key[8],
-                         void *dev_cvs, void *stream) {
-    return b3g::group_cvs(dev_in, len, chunk_base, key, dev_cvs, stream);
+                         uint32_t group_chunks, void *dev_cvs, void *stream) {
+    return b3g::group_cvs(dev_in, len, chunk_base, key, group_chunks, dev_cvs, stream);
+}
+
+uint32_t blake3_gpu_leaf_group_chunks(uint64_t len) {
+    return b3g::kLeafLanes * b3g::choose_chunks_per_lane(b3g::chunks_of(len));
 }
 
 const char *blake3_gpu_strerror(int status) {
@@ -300,13 +311,17 @@ int blake3_gpu_version(void) { return b3g::kAbiVersion; }
 int64_t blake3_gpu_debug_plan_batch(const uint64_t *host_lengths, uint64_t n, uint64_t *out,
                                     uint64_t out_words) {
     if (n > 0 && host_lengths == nullptr) return B3G_EINVAL;
+    uint64_t total_chunks = 0;
+    for (uint64_t i = 0; i < n; ++i) total_chunks += b3g::chunks_of(host_lengths[i]);
     b3g::BatchPlan plan;
-    const int rc = b3g::plan_batch(host_lengths, n, b3g::kLeafLanes, b3g::kLevelLanes, &plan);
+    const int rc = b3g::plan_batch(host_lengths, n, b3g::kLeafLanes, b3g::choose_chunks_per_lane(total_chunks),
+                                   b3g::kLevelLanes, &plan);
     if (rc != B3G_OK) return rc;
     std::vector<uint64_t> w;
     w.push_back(plan.passes.size());
     for (const b3g::PassPlan &p : plan.passes) {
         w.push_back(p.lanes);
+        w.push_back(p.chunks_per_lane);
         w.push_back(p.workgroups());
         w.push_back(p.segs.size());
         w.push_back(p.in_cvs);

@@ -21,7 +21,8 @@
 
 namespace b3g {
 
-// Lanes (= tree nodes) per workgroup. Both kernels use 256 lanes (4 wave64s).
+// Lanes (= tree nodes) per workgroup. Both kernels use 256 lanes (4 wave64s); a leaf lane
+// covers K consecutive chunks (a node of the tree K leaves up).
 constexpr uint32_t kLeafLanes = 256;
 constexpr uint32_t kLevelLanes = 256;
 
@@ -74,9 +75,13 @@ struct BatchLevelArgs {
     uint8_t *digests;
 };
 
-hipError_t launch_single_leaf(const SingleLeafArgs &a, uint32_t grid, hipStream_t s);
+// chunks_per_lane (K) is 1, 2 or 4: each leaf workgroup covers 256*K chunks. `staged`
+// selects the LDS-staged input path for full waves instead of per-lane loads.
+hipError_t launch_single_leaf(const SingleLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
+                              hipStream_t s);
 hipError_t launch_single_level(const SingleLevelArgs &a, uint32_t grid, hipStream_t s);
-hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t grid, hipStream_t s);
+hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
+                             hipStream_t s);
 hipError_t launch_batch_level(const BatchLevelArgs &a, uint32_t grid, hipStream_t s);
 
 }  // namespace b3g

@@ -15,7 +15,10 @@
 //  - "Kernels 2 and 3": further levels reduce the per-workgroup roots; the final
 //    compression of the whole tree carries ROOT.
 //
-// gfx950 design. Lane x of the workgroup owns tree node x; level l+1 node q is computed by
+// gfx950 design. In the leaf kernel each lane hashes K consecutive chunks (K = 1, 2 or 4,
+// chosen by input size) and folds them into one subtree node in registers, so the first
+// log2(K) tree levels cost no cross-lane traffic and the lane-sparse top of the workgroup
+// tree is paid once per 256*K chunks. Lane x of the workgroup owns tree node x; level l+1 node q is computed by
 // lane q from level-l nodes 2q and 2q+1, so the active lanes stay packed at the bottom of
 // the workgroup (dense waves) instead of spreading out. Keeping the node of an odd last
 // position unchanged ("carry") at each level produces exactly the BLAKE3 shape: the left
@@ -43,29 +46,38 @@ __device__ __forceinline__ uint32_t load_word_bounded(const uint8_t *p, uint32_t
     return w;
 }
 
-// Full 1 KiB chunk (16-byte aligned): the next block's four 16-byte loads are issued
-// before the current block is compressed, so their latency hides behind ~680 VALU ops.
+struct Block {
+    uint4 q0, q1, q2, q3;
+};
+
+__device__ __forceinline__ void compress_block(uint32_t (&cv)[8], const Block &k, uint32_t lo, uint32_t hi,
+                                               uint32_t flags) {
+    const uint32_t m[16] = {k.q0.x, k.q0.y, k.q0.z, k.q0.w, k.q1.x, k.q1.y, k.q1.z, k.q1.w,
+                            k.q2.x, k.q2.y, k.q2.z, k.q2.w, k.q3.x, k.q3.y, k.q3.z, k.q3.w};
+    compress(cv, m, lo, hi, kBlockBytes, flags);
+}
+
+__device__ __forceinline__ Block load_block(const uint4 *p) { return Block{p[0], p[1], p[2], p[3]}; }
+
+// Full 1 KiB chunk with per-lane 16-byte loads (16-byte aligned). Blocks are handled in
+// pairs with two register sets, so the loads of a block are issued ahead of its
+// compression and no registers are copied between iterations; the reload of the even set
+// is unconditional (the last iteration re-reads block 14, which is in cache) so that the
+// loop carries no conditional register values.
 __device__ __forceinline__ void hash_full_chunk(uint32_t (&cv)[8], const uint8_t *chunk, uint32_t ctr_lo,
-                                                uint32_t ctr_hi, uint32_t mode, uint32_t end_flags) {
+                                                uint32_t ctr_hi, uint32_t mode) {
     const uint4 *p = reinterpret_cast<const uint4 *>(chunk);
-    uint4 q0 = p[0], q1 = p[1], q2 = p[2], q3 = p[3];
-    for (uint32_t b = 0; b < kBlocksPerChunk; ++b) {
-        const uint32_t m[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
-                                q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
-        if (b + 1 < kBlocksPerChunk) {
-            p += 4;
-            q0 = p[0];
-            q1 = p[1];
-            q2 = p[2];
-            q3 = p[3];
-        }
-        const uint32_t flags =
-            mode | (b == 0 ? kChunkStart : 0u) | (b + 1 == kBlocksPerChunk ? end_flags : 0u);
-        compress(cv, m, ctr_lo, ctr_hi, kBlockBytes, flags);
+    Block even = load_block(p);
+    for (uint32_t b = 0; b < kBlocksPerChunk; b += 2) {
+        const Block odd = load_block(p + 4 * (b + 1));
+        compress_block(cv, even, ctr_lo, ctr_hi, mode | (b == 0 ? kChunkStart : 0u));
+        const uint32_t next = b + 2 < kBlocksPerChunk ? b + 2 : kBlocksPerChunk - 2;
+        even = load_block(p + 4 * next);
+        compress_block(cv, odd, ctr_lo, ctr_hi, mode | (b + 2 == kBlocksPerChunk ? kChunkEnd : 0u));
     }
 }
 
-// Chunk of `len` < 1024 bytes (only the last chunk of a message, or the empty message):
+// Chunk of `len` <= 1024 bytes with per-lane loads that never read past `len`:
 // max(1, ceil(len/64)) blocks, the last one of length len - 64*(blocks-1).
 __device__ void hash_short_chunk(uint32_t (&cv)[8], const uint8_t *chunk, uint32_t len, uint32_t ctr_lo,
                                  uint32_t ctr_hi, uint32_t mode, uint32_t end_flags) {
@@ -83,16 +95,184 @@ __device__ void hash_short_chunk(uint32_t (&cv)[8], const uint8_t *chunk, uint32
     }
 }
 
-// One chunk per lane. Waves whose chunks are all full take the prefetching path; the
-// (at most one per message) wave holding a short chunk takes the bounded path.
-__device__ __forceinline__ void hash_chunk(uint32_t (&cv)[8], bool has_chunk, const uint8_t *chunk,
-                                           uint32_t len, uint64_t counter, uint32_t mode, bool root) {
-    const uint32_t lo = static_cast<uint32_t>(counter), hi = static_cast<uint32_t>(counter >> 32);
-    const uint32_t end_flags = kChunkEnd | (root ? kRoot : 0u);
-    if (__ballot(has_chunk && len != kChunkBytes) == 0) {
-        if (has_chunk) hash_full_chunk(cv, chunk, lo, hi, mode, end_flags);
-    } else {
-        if (has_chunk) hash_short_chunk(cv, chunk, len, lo, hi, mode, end_flags);
+constexpr uint32_t kLanes = kLeafLanes;
+constexpr uint32_t kWaveLanes = 64;
+
+// c <- parent(left, c): the two CVs as one 64-byte block, compressed from the key words
+// with counter 0, block length 64 and PARENT (ROOT when `root`).
+__device__ __forceinline__ void parent_left(uint32_t (&c)[8], const uint32_t (&left)[8], const uint32_t (&key)[8],
+                                            uint32_t mode, bool root) {
+    uint32_t m[16];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        m[w] = left[w];
+        m[w + 8] = c[w];
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) c[w] = key[w];
+    compress(c, m, 0, 0, kBlockBytes, mode | kParent | (root ? kRoot : 0u));
+}
+
+// Folds chunk k's CV `c` into the lane's pending subtrees. After chunk k the lane holds
+// one complete subtree per set bit of k+1; chunk k's CV merges with the pending subtree
+// of each size 2^lv for which bit lv of k is set (its left neighbours of equal size),
+// which keeps every left subtree a complete power of two, at least as large as its
+// right sibling. With K <= 4 a subtree waiting for a right sibling has 1 chunk (slot1c)
+// or 2 chunks (slot2c); the slots are only ever named directly, so they stay in
+// registers. `fin_k` is the index of the lane's last chunk when this node is the whole
+// message (the merge that produces all of it carries ROOT), else K.
+template <uint32_t K>
+__device__ __forceinline__ void fold_chunk(uint32_t (&c)[8], uint32_t k, uint32_t (&slot1c)[8],
+                                           uint32_t (&slot2c)[8], bool store, uint32_t fin_k,
+                                           const uint32_t (&key)[8], uint32_t mode) {
+    if (k & 1u) {
+        parent_left(c, slot1c, key, mode, k == fin_k && k == 1);
+        if (K > 2 && (k & 2u)) parent_left(c, slot2c, key, mode, k == fin_k && k == 3);
+    }
+    // both slots are written every time (value selects): a store to a conditionally chosen
+    // slot would be merged into one store through a selected address, moving the slots
+    // out of registers
+    const bool to1 = store && !(k & 1u);
+    const bool to2 = K > 2 && store && (k & 1u) && !(k & 2u);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        slot1c[w] = to1 ? c[w] : slot1c[w];
+        slot2c[w] = to2 ? c[w] : slot2c[w];
+    }
+}
+
+// Per-lane path (waves holding a short chunk or lanes with fewer than K chunks, i.e.
+// the ends of messages): the lane's nl (1..K) consecutive chunks, starting at `ptr` with
+// counter ctr0, reduced to one node, the BLAKE3 tree over nl leaves. Loads are
+// per-lane and bounded by the byte count. The last chunk has last_len bytes (1024 unless
+// it ends the message). `root`: this node is the whole message, so its final compression
+// carries ROOT.
+template <uint32_t K>
+__device__ __forceinline__ void lane_subtree(uint32_t (&c)[8], const uint8_t *ptr, uint32_t nl,
+                                             uint32_t last_len, uint64_t ctr0, const uint32_t (&key)[8],
+                                             uint32_t mode, bool root) {
+    uint32_t slot1c[8], slot2c[8];
+    const uint32_t fin_k = root ? nl - 1 : K;
+    for (uint32_t k = 0; k < nl; ++k) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) c[w] = key[w];
+        const uint64_t ctr = ctr0 + k;
+        const uint32_t lo = static_cast<uint32_t>(ctr), hi = static_cast<uint32_t>(ctr >> 32);
+        const uint32_t end_flags = kChunkEnd | (root && nl == 1 ? kRoot : 0u);
+        const uint8_t *chunk = ptr + static_cast<uint64_t>(k) * kChunkBytes;
+        hash_short_chunk(c, chunk, k + 1 == nl ? last_len : kChunkBytes, lo, hi, mode, end_flags);
+        if (K > 1) fold_chunk<K>(c, k, slot1c, slot2c, k + 1 < nl, fin_k, key, mode);
+    }
+    // nl not a power of two (only 3 when K <= 4): the 2-chunk subtree on the left remains
+    if (K > 2 && nl == 3) parent_left(c, slot2c, key, mode, root);
+}
+
+// ---- full waves, direct loads (default) ---------------------------------------------
+// Every lane of the wave holds K full chunks. Each lane reads its own chunks with 16-byte
+// loads; a lane starts at chunk (lane mod K) of its run and wraps around, so that at
+// every step the 64 lanes read from K different 1 KiB offsets of their K KiB spans
+// (with equal offsets every lane's line falls in the same cache set and channel and is
+// evicted between the two blocks that share it). The chunk CVs wait in LDS slots, one
+// column per lane (slot j, word w at slots[(j * 8 + w) * kLanes]), and are folded at the
+// end, level by level: node i = parent(node 2i, node 2i+1).
+template <uint32_t K>
+__device__ __forceinline__ void direct_subtree(uint32_t (&c)[8], const uint8_t *ptr, uint64_t ctr0,
+                                               const uint32_t (&key)[8], uint32_t mode, uint32_t *slots) {
+    const uint32_t rot = threadIdx.x % K;
+    for (uint32_t step = 0; step < K; ++step) {
+        const uint32_t k = (step + rot) % K;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) c[w] = key[w];
+        const uint64_t ctr = ctr0 + k;
+        hash_full_chunk(c, ptr + static_cast<uint64_t>(k) * kChunkBytes, static_cast<uint32_t>(ctr),
+                        static_cast<uint32_t>(ctr >> 32), mode);
+        if (K == 1) return;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) slots[(k * 8 + w) * kLanes] = c[w];
+    }
+    for (uint32_t width = K; width > 1; width /= 2) {
+        for (uint32_t i = 0; i < width / 2; ++i) {
+            uint32_t m[16];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                m[w] = slots[(2 * i * 8 + w) * kLanes];
+                m[w + 8] = slots[((2 * i + 1) * 8 + w) * kLanes];
+            }
+#pragma unroll
+            for (int w = 0; w < 8; ++w) c[w] = key[w];
+            compress(c, m, 0, 0, kBlockBytes, mode | kParent);
+            if (width > 2) {
+#pragma unroll
+                for (int w = 0; w < 8; ++w) slots[(i * 8 + w) * kLanes] = c[w];
+            }
+        }
+    }
+}
+
+// ---- full waves, staged loads (BLAKE3_GPU_STAGING=lds) ----------------------------------
+// The same work as direct_subtree with the input staged through LDS. Each step stages 128
+// bytes (two blocks) of every lane's current chunk in the wave's own 8 KiB of LDS:
+// row r holds lane r's bytes, its 16-byte piece p at column p ^ (r & 7). The loads are
+// direct-to-LDS and coalesced: load instruction j fills rows 8j..8j+7, lane i bringing
+// piece (i & 7) ^ (i >> 3) of row 8j + (i >> 3), so every 128-byte line is fetched whole
+// by 8 lanes of one instruction, and the XOR swizzle makes the lanes' row reads cover all
+// LDS banks. The next step's loads are issued as soon as the current row is in
+// registers, so they overlap two compressions.
+constexpr uint32_t kStageBytes = kWaveLanes * 2 * kBlockBytes;  // 8 KiB per wave
+
+// Rows of a wave whose runs of K chunks are evenly spaced (one message): row R starts at
+// base + R * K KiB.
+struct EvenRows {
+    const uint8_t *lane_src;  // this lane's source within load 0
+    uint64_t load_stride;     // 8 rows further per load instruction
+    __device__ const uint8_t *ptr(uint32_t j) const { return lane_src + j * load_stride; }
+};
+
+// Rows at arbitrary addresses (batch): each lane keeps the sources of its 8 loads.
+struct GatherRows {
+    const uint8_t *src[8];
+    __device__ const uint8_t *ptr(uint32_t j) const { return src[j]; }
+};
+
+__device__ __forceinline__ uint32_t stage_piece(uint32_t lw) { return (lw & 7u) ^ (lw >> 3); }
+
+template <class Rows>
+__device__ __forceinline__ void stage_issue(const Rows &rows, uint32_t off, uint32_t *stage) {
+#pragma unroll
+    for (uint32_t j = 0; j < 8; ++j)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(rows.ptr(j) + off),
+                                         (__attribute__((address_space(3))) void *)(stage + j * 256), 16, 0, 0);
+}
+
+template <uint32_t K, class Rows>
+__device__ __forceinline__ void staged_subtree(uint32_t (&c)[8], const Rows &rows, uint32_t *stage, uint64_t ctr0,
+                                               const uint32_t (&key)[8], uint32_t mode) {
+    const uint32_t lw = threadIdx.x % kWaveLanes;
+    const uint4 *row = reinterpret_cast<const uint4 *>(stage) + lw * 8;
+    uint32_t slot1c[8], slot2c[8];
+    stage_issue(rows, 0, stage);
+    for (uint32_t k = 0; k < K; ++k) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) c[w] = key[w];
+        const uint64_t ctr = ctr0 + k;
+        const uint32_t lo = static_cast<uint32_t>(ctr), hi = static_cast<uint32_t>(ctr >> 32);
+        for (uint32_t bp = 0; bp < kBlocksPerChunk / 2; ++bp) {
+            // this step's loads have landed in LDS: even block out of the lane's row
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            uint4 q0 = row[0 ^ (lw & 7u)], q1 = row[1 ^ (lw & 7u)], q2 = row[2 ^ (lw & 7u)], q3 = row[3 ^ (lw & 7u)];
+            compress_block(c, Block{q0, q1, q2, q3}, lo, hi, mode | (bp == 0 ? kChunkStart : 0u));
+            // odd block out, then refill the stage with the next step while it is compressed
+            q0 = row[4 ^ (lw & 7u)];
+            q1 = row[5 ^ (lw & 7u)];
+            q2 = row[6 ^ (lw & 7u)];
+            q3 = row[7 ^ (lw & 7u)];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (bp + 1 < kBlocksPerChunk / 2) stage_issue(rows, k * kChunkBytes + (bp + 1) * 2 * kBlockBytes, stage);
+            else if (k + 1 < K) stage_issue(rows, (k + 1) * kChunkBytes, stage);
+            compress_block(c, Block{q0, q1, q2, q3}, lo, hi,
+                           mode | (bp + 1 == kBlocksPerChunk / 2 ? kChunkEnd : 0u));
+        }
+        if (K > 1) fold_chunk<K>(c, k, slot1c, slot2c, k + 1 < K, K, key, mode);
     }
 }
 
@@ -242,28 +422,56 @@ __device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs 
 
 // ---- kernels ---------------------------------------------------------------------------
 
+// LDS of the leaf kernel: during the chunk phase the waves' stage buffers (staged
+// loads) or the lanes' chunk slots (direct loads); then the tree's two level buffers (a
+// barrier separates the two uses).
+template <uint32_t K, bool Staged>
+constexpr uint32_t leaf_lds_words() {
+    constexpr uint32_t tree = 2 * 8 * kLanes;
+    constexpr uint32_t chunk_phase = Staged ? (kLanes / kWaveLanes) * kStageBytes / 4 : (K > 1 ? K * 8 * kLanes : 0);
+    return tree > chunk_phase ? tree : chunk_phase;
+}
+
+template <uint32_t K, bool Staged>
 __global__ __launch_bounds__(kLeafLanes) void leaf_single_kernel(SingleLeafArgs a) {
-    __shared__ uint32_t buf[2][8][kLeafLanes];
+    __shared__ __attribute__((aligned(16))) uint32_t lds[leaf_lds_words<K, Staged>()];
     const uint32_t lane = threadIdx.x;
-    const uint64_t first = static_cast<uint64_t>(blockIdx.x) * kLeafLanes;
+    constexpr uint64_t kWgChunks = static_cast<uint64_t>(kLanes) * K;
+    const uint64_t first = static_cast<uint64_t>(blockIdx.x) * kWgChunks;
     const uint64_t left = a.n_chunks - first;
-    const uint32_t n_wg = left < kLeafLanes ? static_cast<uint32_t>(left) : kLeafLanes;
-    const bool has_chunk = lane < n_wg;
-    const uint64_t chunk = first + lane;
-    uint32_t len = 0;
-    if (has_chunk) {
-        const uint64_t rem = a.len - chunk * kChunkBytes;  // len == 0 only for the empty message
-        len = a.len == 0 ? 0u : (rem < kChunkBytes ? static_cast<uint32_t>(rem) : kChunkBytes);
+    const uint32_t n_wg = left < kWgChunks ? static_cast<uint32_t>(left) : static_cast<uint32_t>(kWgChunks);
+    const uint32_t nodes = (n_wg + K - 1) / K;
+    const uint64_t c0 = first + static_cast<uint64_t>(lane) * K;
+    uint32_t nl = 0, last_len = kChunkBytes;
+    if (lane < nodes) {
+        nl = n_wg - lane * K < K ? n_wg - lane * K : K;
+        const uint64_t rem = a.len - (c0 + nl - 1) * kChunkBytes;  // bytes from the lane's last chunk on
+        last_len = a.len == 0 ? 0u : (rem < kChunkBytes ? static_cast<uint32_t>(rem) : kChunkBytes);
     }
     const bool whole = a.may_root && gridDim.x == 1;
+    const uint32_t key[8] = {a.key[0], a.key[1], a.key[2], a.key[3], a.key[4], a.key[5], a.key[6], a.key[7]};
     uint32_t cv[8];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) cv[w] = a.key[w];
-    hash_chunk(cv, has_chunk, a.in + chunk * kChunkBytes, len, a.chunk_base + chunk, a.mode,
-               whole && a.n_chunks == 1);
-    SingleSegs sg{n_wg, whole, {a.key[0], a.key[1], a.key[2], a.key[3], a.key[4], a.key[5], a.key[6], a.key[7]},
-                  a.mode, a.cv_out, a.digest};
-    tree_reduce<kLeafLanes>(cv, sg, ceil_log2(n_wg), buf);
+    for (int w = 0; w < 8; ++w) cv[w] = key[w];
+    if (__ballot(nl != K || last_len != kChunkBytes) == 0) {
+        if (Staged) {
+            const uint32_t lw = lane % kWaveLanes;
+            const uint64_t wave_first = first + static_cast<uint64_t>(lane - lw) * K;
+            const EvenRows rows{a.in + (wave_first + (lw >> 3) * K) * kChunkBytes + 16 * stage_piece(lw),
+                                8ull * K * kChunkBytes};
+            staged_subtree<K>(cv, rows, lds + (lane / kWaveLanes) * (kStageBytes / 4), a.chunk_base + c0, key,
+                              a.mode);
+        } else {
+            direct_subtree<K>(cv, a.in + c0 * kChunkBytes, a.chunk_base + c0, key, a.mode, lds + lane);
+        }
+    } else if (nl > 0) {
+        lane_subtree<K>(cv, a.in + c0 * kChunkBytes, nl, last_len, a.chunk_base + c0, key, a.mode,
+                        whole && nodes == 1);
+    }
+    __syncthreads();  // every wave is done with its stage buffer before the tree reuses it
+    SingleSegs sg{nodes, whole, {key[0], key[1], key[2], key[3], key[4], key[5], key[6], key[7]}, a.mode,
+                  a.cv_out, a.digest};
+    tree_reduce<kLanes>(cv, sg, ceil_log2(nodes), reinterpret_cast<uint32_t(*)[8][kLanes]>(lds));
 }
 
 __global__ __launch_bounds__(kLevelLanes) void level_single_kernel(SingleLevelArgs a) {
@@ -280,32 +488,57 @@ __global__ __launch_bounds__(kLevelLanes) void level_single_kernel(SingleLevelAr
     tree_reduce<kLevelLanes>(cv, sg, ceil_log2(n_wg), buf);
 }
 
+template <uint32_t K, bool Staged>
 __global__ __launch_bounds__(kLeafLanes) void leaf_batch_kernel(BatchLeafArgs a) {
-    __shared__ uint32_t buf[2][8][kLeafLanes];
-    __shared__ Seg s_seg[kLeafLanes];
-    __shared__ int s_seg_of[kLeafLanes];
-    stage_segments<kLeafLanes>(a.wg_first_seg, a.segs, s_seg, s_seg_of);
+    __shared__ __attribute__((aligned(16))) uint32_t lds[leaf_lds_words<K, Staged>()];
+    __shared__ Seg s_seg[kLanes];
+    __shared__ int s_seg_of[kLanes];
+    stage_segments<kLanes>(a.wg_first_seg, a.segs, s_seg, s_seg_of);
     const uint32_t lane = threadIdx.x;
     const int s = s_seg_of[lane];
-    const bool has_chunk = s >= 0;
     BatchSegs sg{s_seg, s_seg_of, a.keys, a.cv_out, a.digests};
+    uint32_t key[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const uint8_t *ptr = a.base;
-    uint32_t len = 0;
-    uint64_t chunk = 0;
+    uint32_t nl = 0, last_len = kChunkBytes;
+    uint64_t c0 = 0;
     bool root = false;
-    if (has_chunk) {
+    if (s >= 0) {
         const Seg g = s_seg[s];
-        chunk = g.first + (lane - seg_lane(g.info));
         const uint64_t mlen = a.msg_len[g.msg];
-        const uint64_t rem = mlen - chunk * kChunkBytes;
-        len = mlen == 0 ? 0u : (rem < kChunkBytes ? static_cast<uint32_t>(rem) : kChunkBytes);
-        ptr = a.base + a.msg_off[g.msg] + chunk * kChunkBytes;
+        const uint64_t msg_chunks = mlen == 0 ? 1 : (mlen + kChunkBytes - 1) / kChunkBytes;
+        const uint64_t seg_left = msg_chunks - g.first;  // chunks from the segment start to the message end
+        const uint32_t x = lane - seg_lane(g.info);       // node index within the segment
+        const uint64_t lane_left = seg_left - static_cast<uint64_t>(x) * K;
+        nl = lane_left < K ? static_cast<uint32_t>(lane_left) : K;
+        c0 = g.first + static_cast<uint64_t>(x) * K;
+        const uint64_t rem = mlen - (c0 + nl - 1) * kChunkBytes;
+        last_len = mlen == 0 ? 0u : (rem < kChunkBytes ? static_cast<uint32_t>(rem) : kChunkBytes);
+        ptr = a.base + a.msg_off[g.msg] + c0 * kChunkBytes;
         root = seg_final(g.info) && seg_count(g.info) == 1;
-        sg.key_words(s, cv);
+        sg.key_words(s, key);
+#pragma unroll
+        for (int w = 0; w < 8; ++w) cv[w] = key[w];
     }
-    hash_chunk(cv, has_chunk, ptr, len, chunk, sg.mode(), root);
-    tree_reduce<kLeafLanes>(cv, sg, a.wg_levels[blockIdx.x], buf);
+    if (__ballot(nl != K || last_len != kChunkBytes) == 0) {
+        if (Staged) {
+            // every lane holds K full chunks: gather the 8 rows each lane loads for
+            const uint32_t lw = lane % kWaveLanes;
+            const uint64_t my = reinterpret_cast<uint64_t>(ptr);
+            GatherRows rows;
+#pragma unroll
+            for (uint32_t j = 0; j < 8; ++j)
+                rows.src[j] = reinterpret_cast<const uint8_t *>(__shfl(my, static_cast<int>(8 * j + (lw >> 3)))) +
+                              16 * stage_piece(lw);
+            staged_subtree<K>(cv, rows, lds + (lane / kWaveLanes) * (kStageBytes / 4), c0, key, sg.mode());
+        } else {
+            direct_subtree<K>(cv, ptr, c0, key, sg.mode(), lds + lane);
+        }
+    } else if (nl > 0) {
+        lane_subtree<K>(cv, ptr, nl, last_len, c0, key, sg.mode(), root);
+    }
+    __syncthreads();  // every wave is done with its stage buffer before the tree reuses it
+    tree_reduce<kLanes>(cv, sg, a.wg_levels[blockIdx.x], reinterpret_cast<uint32_t(*)[8][kLanes]>(lds));
 }
 
 __global__ __launch_bounds__(kLevelLanes) void level_batch_kernel(BatchLevelArgs a) {
@@ -326,8 +559,18 @@ __global__ __launch_bounds__(kLevelLanes) void level_batch_kernel(BatchLevelArgs
 
 }  // namespace
 
-hipError_t launch_single_leaf(const SingleLeafArgs &a, uint32_t grid, hipStream_t s) {
-    hipLaunchKernelGGL(leaf_single_kernel, dim3(grid), dim3(kLeafLanes), 0, s, a);
+hipError_t launch_single_leaf(const SingleLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
+                              hipStream_t s) {
+    const dim3 g(grid), b(kLeafLanes);
+    switch (chunks_per_lane * 2 + (staged ? 1 : 0)) {
+        case 2: hipLaunchKernelGGL((leaf_single_kernel<1, false>), g, b, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((leaf_single_kernel<1, true>), g, b, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((leaf_single_kernel<2, false>), g, b, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((leaf_single_kernel<2, true>), g, b, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((leaf_single_kernel<4, false>), g, b, 0, s, a); break;
+        case 9: hipLaunchKernelGGL((leaf_single_kernel<4, true>), g, b, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -336,8 +579,18 @@ hipError_t launch_single_level(const SingleLevelArgs &a, uint32_t grid, hipStrea
     return hipGetLastError();
 }
 
-hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t grid, hipStream_t s) {
-    hipLaunchKernelGGL(leaf_batch_kernel, dim3(grid), dim3(kLeafLanes), 0, s, a);
+hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
+                             hipStream_t s) {
+    const dim3 g(grid), b(kLeafLanes);
+    switch (chunks_per_lane * 2 + (staged ? 1 : 0)) {
+        case 2: hipLaunchKernelGGL((leaf_batch_kernel<1, false>), g, b, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((leaf_batch_kernel<1, true>), g, b, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((leaf_batch_kernel<2, false>), g, b, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((leaf_batch_kernel<2, true>), g, b, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((leaf_batch_kernel<4, false>), g, b, 0, s, a); break;
+        case 9: hipLaunchKernelGGL((leaf_batch_kernel<4, true>), g, b, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

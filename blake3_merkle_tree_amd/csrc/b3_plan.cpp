@@ -14,6 +14,8 @@
 // own R, which keeps the in-workgroup pairing from mixing groups.
 #include "b3_plan.h"
 
+#include <stdlib.h>
+
 #include <algorithm>
 
 namespace b3g {
@@ -35,7 +37,7 @@ struct Group {
 
 // Lays groups out over workgroups of `lanes` lanes.
 int pack(std::vector<Group> &groups, uint32_t lanes, PassPlan *p) {
-    p->lanes = lanes;
+    p->lanes = lanes;  // g.count is in nodes (lanes)
     std::vector<Group> partial;
     for (const Group &g : groups) {
         if (g.count == lanes) {
@@ -69,14 +71,32 @@ int pack(std::vector<Group> &groups, uint32_t lanes, PassPlan *p) {
 
 uint64_t chunks_of(uint64_t len) { return len == 0 ? 1 : (len + 1023) / 1024; }
 
+uint32_t choose_chunks_per_lane(uint64_t total_chunks) {
+    if (const char *e = getenv("BLAKE3_GPU_CHUNKS_PER_LANE")) {
+        const int k = atoi(e);
+        if (k == 1 || k == 2 || k == 4) return static_cast<uint32_t>(k);
+    }
+    // Four chunks per lane once the 1024-chunk workgroups still give every CU at least
+    // two (256 CUs): it cuts the lane-sparse top of each workgroup tree and the fold work
+    // by 4x. Measured on MI355X: 4 GiB and 16 GiB inputs run ~2% faster than at one chunk
+    // per lane, 256 MiB runs equal; smaller inputs need the extra workgroups.
+    if (total_chunks >= (1ull << 19)) return 4;
+    return 1;
+}
+
+bool use_lds_staging() {
+    const char *e = getenv("BLAKE3_GPU_STAGING");
+    return e != nullptr && e[0] == 'l' && e[1] == 'd' && e[2] == 's' && e[3] == 0;
+}
+
 uint32_t ceil_log2_host(uint64_t n) {
     uint32_t r = 0;
     while ((1ull << r) < n) ++r;
     return r;
 }
 
-int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_t level_lanes,
-               BatchPlan *out) {
+int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_t chunks_per_lane,
+               uint32_t level_lanes, BatchPlan *out) {
     out->passes.clear();
     if (n == 0) return kOk;
     if (n >= (1ull << 32)) return kTooBig;
@@ -89,18 +109,22 @@ int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_
     // in_base[i]: where message i's input CVs start in the current pass's input array
     std::vector<uint64_t> in_base(n, 0), out_base(n, 0);
     for (uint32_t pass = 0;; ++pass) {
+        // a pass-0 node is a lane's run of chunks_per_lane chunks; later nodes are CVs
+        const uint64_t per_node = pass == 0 ? chunks_per_lane : 1;
         const uint64_t lanes = pass == 0 ? leaf_lanes : level_lanes;
+        const uint64_t span = lanes * per_node;  // units (chunks or CVs) per full group
         std::vector<Group> groups;
         uint64_t out_cvs = 0;
         for (uint64_t i = 0; i < n; ++i) {
             if (nodes[i] == 0) continue;
-            const uint64_t ngroups = (nodes[i] + lanes - 1) / lanes;
+            const uint64_t ngroups = (nodes[i] + span - 1) / span;
             const bool final = ngroups == 1;
             out_base[i] = out_cvs;
             if (!final) out_cvs += ngroups;
             for (uint64_t k = 0; k < ngroups; ++k) {
-                const uint64_t first = (pass == 0 ? 0 : in_base[i]) + k * lanes;
-                const uint64_t count = std::min<uint64_t>(lanes, nodes[i] - k * lanes);
+                const uint64_t first = (pass == 0 ? 0 : in_base[i]) + k * span;
+                const uint64_t units = std::min<uint64_t>(span, nodes[i] - k * span);
+                const uint64_t count = (units + per_node - 1) / per_node;
                 if (first >= (1ull << 32) || out_base[i] + k >= (1ull << 32)) return kTooBig;
                 groups.push_back(Group{static_cast<uint32_t>(i), static_cast<uint32_t>(first),
                                        static_cast<uint32_t>(count),
@@ -110,6 +134,7 @@ int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_
         }
         if (groups.empty()) break;
         PassPlan p;
+        p.chunks_per_lane = static_cast<uint32_t>(per_node);
         p.in_cvs = pass == 0 ? 0 : out->passes.back().out_cvs;
         p.out_cvs = out_cvs;
         const int rc = pack(groups, static_cast<uint32_t>(lanes), &p);

@@ -32,6 +32,7 @@ constexpr uint64_t kMaxMessageBytes = 1ull << 42;
 
 struct PassPlan {
     uint32_t lanes = 0;                  // lanes (nodes) per workgroup in this pass
+    uint32_t chunks_per_lane = 1;        // pass 0: chunks folded into one node by one lane
     std::vector<Seg> segs;               // sorted by workgroup, then by lane start
     std::vector<uint32_t> wg_first_seg;  // W + 1 entries
     std::vector<uint8_t> wg_levels;      // W entries: ceil(log2(largest segment))
@@ -47,9 +48,21 @@ struct BatchPlan {
 uint64_t chunks_of(uint64_t len);       // max(1, ceil(len / 1024))
 uint32_t ceil_log2_host(uint64_t n);     // 0 for n <= 1
 
-// Builds the passes for messages of the given byte lengths. Returns 0 (B3G_OK) or a
-// negative b3g_status (B3G_ETOOBIG when a message or the task table exceeds the limits).
-int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_t level_lanes,
-               BatchPlan *out);
+// Chunks per leaf lane (1, 2 or 4) for an input of `total_chunks` chunks: 4 once the grid
+// of 1024-chunk workgroups still gives every CU two of them, 1 for smaller inputs so
+// that they keep enough waves in flight. BLAKE3_GPU_CHUNKS_PER_LANE (1, 2 or 4) in the
+// environment overrides the choice (for tests and benchmarks).
+uint32_t choose_chunks_per_lane(uint64_t total_chunks);
+
+// Input path of full leaf waves: per-lane loads (default) or staged through LDS with
+// coalesced direct-to-LDS loads when BLAKE3_GPU_STAGING=lds is set in the environment.
+bool use_lds_staging();
+
+// Builds the passes for messages of the given byte lengths. Pass 0 groups
+// leaf_lanes * chunks_per_lane chunks per workgroup (one node per lane); later passes
+// group level_lanes CVs. Returns 0 (B3G_OK) or a negative b3g_status (B3G_ETOOBIG when a
+// message or the task table exceeds the limits).
+int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_t chunks_per_lane,
+               uint32_t level_lanes, BatchPlan *out);
 
 }  // namespace b3g

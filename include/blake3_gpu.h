@@ -93,29 +93,32 @@ int blake3_gpu_keyed_hash_batch(const void *dev_base, const uint64_t *host_offse
                                 const uint64_t *host_lengths, const uint32_t *dev_keys, void *dev_out,
                                 uint64_t n, void *stream);
 
-/* Chunks per group of blake3_gpu_group_cvs (a power of two). */
-#define BLAKE3_GPU_GROUP_CHUNKS 256
-
 /*
- * The first tree level above the chunks that one workgroup produces: the chaining value
- * (CV) of every aligned group of BLAKE3_GPU_GROUP_CHUNKS consecutive 1 KiB chunks of
- * dev_in[0 .. len) (the last group may be shorter), with chunk counters starting at
- * chunk_base and no ROOT flag anywhere. This is the page's first kernel on its own
- * ("Kernel 1": compress every chunk, then a fused partial reduction to one root per
- * block); each group CV is a node of the BLAKE3 tree of any larger input of which
- * dev_in is the part starting at chunk chunk_base, provided chunk_base is a multiple of
- * BLAKE3_GPU_GROUP_CHUNKS. Uses: hashing an input spread over several devices or
- * produced piece by piece, and timing the chunk kernel alone.
- *   dev_in     device pointer, 16-byte aligned, len > 0 bytes.
- *   chunk_base counter of the first chunk of dev_in.
- *   key        host pointer to 8 key words (keyed mode), or NULL (default mode).
- *   dev_cvs    device pointer, 16-byte aligned, to ceil(ceil(len/1024)/256) * 32 bytes;
- *              group g's CV (8 little-endian words) at byte 32*g.
- * Errors: EINVAL (NULL dev_in or dev_cvs, len == 0, counter overflow), EALIGN, ETOOBIG,
- * EHIP. Needs no scratch.
+ * The first tree level that one workgroup produces: the chaining value (CV) of every
+ * aligned group of group_chunks consecutive 1 KiB chunks of dev_in[0 .. len) (the last
+ * group may be shorter), with chunk counters starting at chunk_base and no ROOT flag
+ * anywhere. This is the page's first kernel on its own ("Kernel 1": compress every chunk,
+ * then a fused partial reduction to one root per block); each group CV is a node of the
+ * BLAKE3 tree of any larger input of which dev_in is the part starting at chunk
+ * chunk_base, provided chunk_base is a multiple of group_chunks. Uses: hashing an input
+ * spread over several devices or produced piece by piece, and timing the chunk kernel
+ * alone.
+ *   dev_in       device pointer, 16-byte aligned, len > 0 bytes.
+ *   chunk_base   counter of the first chunk of dev_in.
+ *   key          host pointer to 8 key words (keyed mode), or NULL (default mode).
+ *   group_chunks 256, 512 or 1024 (blake3_gpu_leaf_group_chunks(len) is what the hash
+ *                entry points use for an input of len bytes).
+ *   dev_cvs      device pointer, 16-byte aligned, to ceil(ceil(len/1024)/group_chunks) * 32
+ *                bytes; group g's CV (8 little-endian words) at byte 32*g.
+ * Errors: EINVAL (NULL dev_in or dev_cvs, len == 0, other group_chunks, counter
+ * overflow), EALIGN, ETOOBIG, EHIP. Needs no scratch.
  */
 int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, const uint32_t key[8],
-                         void *dev_cvs, void *stream);
+                         uint32_t group_chunks, void *dev_cvs, void *stream);
+
+/* Chunks per leaf workgroup (256, 512 or 1024) that the hash entry points use for an
+ * input of len bytes: larger inputs fold more chunks per lane before the workgroup tree. */
+uint32_t blake3_gpu_leaf_group_chunks(uint64_t len);
 
 /* Static, human-readable text for a b3g_status value (never NULL). */
 const char *blake3_gpu_strerror(int status);
@@ -127,9 +130,10 @@ int blake3_gpu_version(void);
  * Inspection of the batch planner, for tests and tools (no GPU work, no HIP call).
  * Plans the launches blake3_gpu_keyed_hash_batch would make for n messages of the given
  * byte lengths and serialises the plan into out[0 .. out_words) as uint64 words:
- *   [passes] then per pass [lanes, workgroups W, segments S, in_cvs, out_cvs,
- *   W+1 first-segment indices, W level counts, S x (msg, first, dst, info)].
- * Segment info packs bits 0..11 lane start, 12..23 node count - 1, 31 final.
+ *   [passes] then per pass [lanes, chunks per lane K, workgroups W, segments S, in_cvs,
+ *   out_cvs, W+1 first-segment indices, W level counts, S x (msg, first, dst, info)].
+ * Segment info packs bits 0..11 lane start, 12..23 node count - 1, 31 final. In pass 0 a
+ * node is a lane's run of K chunks and `first` a chunk index; later nodes are CVs.
  * Returns the number of words the plan needs (nothing is written if out_words is
  * smaller), or a negative b3g_status (EINVAL for NULL lengths with n > 0, ETOOBIG).
  */

@@ -204,19 +204,57 @@ def test_workload_batch64k(b3, dev):
     assert _digests_to_bytes(out) == want
 
 
-def test_group_cvs_with_counter_offsets(b3, dev):
-    # the leaf pass alone: one CV per aligned 256-chunk group, no ROOT; chunk_base above
-    # 2^32 exercises the counter's high word
+@pytest.mark.parametrize("staging", ["direct", "lds"])
+@pytest.mark.parametrize("group_chunks", [256, 512, 1024])
+def test_group_cvs_with_counter_offsets(b3, dev, monkeypatch, group_chunks, staging):
+    monkeypatch.setenv("BLAKE3_GPU_STAGING", staging)
+    # the leaf pass alone: one CV per aligned group, no ROOT; chunk_base above 2^32
+    # exercises the counter's high word
     from blake3_merkle_tree_amd import workloads
-    buf = workloads.random_bytes(1000 * 1024 + 77, 34, dev)
+    n_groups = 4
+    buf = workloads.random_bytes((n_groups - 1) * group_chunks * 1024 + 100 * 1024 + 77, 34, dev)
     host = _host(buf)
     key = bytes(workloads.key_bytes(35)[0].tolist())
-    G = b3.GROUP_CHUNKS * 1024
-    for base in (0, 256, (1 << 32) + 512, (1 << 40) - 1024):
+    G = group_chunks * 1024
+    for base in (0, group_chunks, (1 << 32) + 2 * group_chunks, (1 << 40) - 4 * group_chunks):
         for keyed in (True, False):
-            got = b3.group_cvs(buf, key if keyed else None, chunk_base=base).cpu().numpy().view(np.uint32)
-            assert got.shape == (4, 8)
-            for g in range(4):
-                want = oracle.subtree_cv(host[g * G:(g + 1) * G].tobytes(), base + g * b3.GROUP_CHUNKS,
+            got = b3.group_cvs(buf, key if keyed else None, chunk_base=base, group_chunks=group_chunks)
+            got = got.cpu().numpy().view(np.uint32)
+            assert got.shape == (n_groups, 8)
+            for g in range(n_groups):
+                want = oracle.subtree_cv(host[g * G:(g + 1) * G].tobytes(), base + g * group_chunks,
                                          key if keyed else None)
                 assert got[g].tolist() == want, (base, keyed, g)
+
+
+@pytest.mark.parametrize("staging", ["direct", "lds"])
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_chunks_per_lane_paths(b3, dev, monkeypatch, k, staging):
+    # each leaf lane folds k chunks; waves whose 64 lanes all hold k full chunks take the
+    # fast input path (per-lane loads, or staged through LDS), the rest the bounded
+    # per-lane loads: sizes cover both, partial waves, partial workgroups and tails
+    monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", str(k))
+    monkeypatch.setenv("BLAKE3_GPU_STAGING", staging)
+    from blake3_merkle_tree_amd import workloads
+    KiB = 1024
+    lengths = [0, 1, 1024, 1025, 4 * KiB, 4 * KiB + 1, 255 * KiB, 256 * KiB, 256 * KiB + 1, 1024 * KiB - 7,
+               1024 * KiB, 1024 * KiB + 1000, 2 * 1024 * KiB + 3 * KiB + 5, 3 * 1024 * KiB, 5 * 1024 * KiB + 17]
+    buf = workloads.random_bytes(max(lengths), 40 + k, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(41)[0].tolist())
+    outs = torch.empty((len(lengths), 32), dtype=torch.uint8, device=dev)
+    for i, L in enumerate(lengths):
+        b3.keyed_hash(buf[:L], key, out=outs[i])
+    want = oracle.hash_batch(host, [0] * len(lengths), lengths, key * len(lengths), nthreads=NTHREADS)
+    assert _digests_to_bytes(outs) == want
+    # batch: whole staged waves (64 KiB messages), ragged ends, tiny messages, gap bytes
+    blens = [64 * KiB] * 40 + [0, 1, 1000, 5000, 63 * KiB + 5, 65 * KiB, 300 * KiB + 9, 1024 * KiB + 3] + [1] * 20
+    offs, total = workloads.pack_messages(blens)
+    base = torch.full((total,), 0xA5, dtype=torch.uint8, device=dev)
+    data = workloads.random_bytes(total, 42, dev)
+    for o, L in zip(offs, blens):
+        base[o:o + L] = data[o:o + L]
+    keys = workloads.key_bytes(43, len(blens))
+    out = b3.keyed_hash_batch(base, offs, blens, keys.to(dev))
+    want = oracle.hash_batch(_host(base), offs, blens, keys.numpy().tobytes(), nthreads=NTHREADS)
+    assert _digests_to_bytes(out) == want

@@ -45,15 +45,23 @@ LENGTH_SETS = [
 ]
 
 
+@pytest.fixture(params=[1, 2, 4])
+def chunks_per_lane(request, monkeypatch):
+    monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", str(request.param))
+    return request.param
+
+
 @pytest.mark.parametrize("lengths", LENGTH_SETS)
-def test_plan_invariants(lengths):
+def test_plan_invariants(lengths, chunks_per_lane):
     plan = b3.debug_plan_batch(lengths)
     n = len(lengths)
     finals = [0] * n
-    nodes = {i: _chunks(L) for i, L in enumerate(lengths)}  # nodes entering the pass
+    units = {i: _chunks(L) for i, L in enumerate(lengths)}  # chunks (pass 0) or CVs entering the pass
     for pi, p in enumerate(plan):
         lanes = p["lanes"]
-        assert lanes == 256
+        per_node = chunks_per_lane if pi == 0 else 1
+        assert lanes == 256 and p["chunks_per_lane"] == per_node
+        span = lanes * per_node
         covered = {}
         out_seen = set()
         first_idx = p["wg_first_seg"]
@@ -67,6 +75,9 @@ def test_plan_invariants(lengths):
                 assert lane >= used and lane + count <= lanes, "segments overlap or overflow"
                 used = lane + count
                 covered.setdefault(msg, []).append((first, count))
+                if pi == 0:
+                    seg_units = min(span, units[msg] - first)
+                    assert count == (seg_units + per_node - 1) // per_node
                 if final:
                     finals[msg] += 1
                 else:
@@ -74,17 +85,17 @@ def test_plan_invariants(lengths):
                     out_seen.add(dst)
             assert p["wg_levels"][w] == max(_ceil_log2(s[4]) for s in segs)
         assert len(out_seen) == p["out_cvs"]
-        # each message still open is covered exactly once, in aligned groups of `lanes`
+        # each message still open is covered exactly once, in aligned groups of `span` units
         for msg, spans in covered.items():
             spans.sort()
-            total = sum(c for _, c in spans)
-            assert total == nodes[msg]
             base = spans[0][0]
             for k, (first, count) in enumerate(spans):
-                assert first == base + k * lanes
+                assert first == base + k * span
+            last_first, last_count = spans[-1]
+            assert (len(spans) - 1) * span + min(span, units[msg] - (last_first - base)) == units[msg]
             if pi == 0:
                 assert base == 0
-        nodes = {msg: len(spans) for msg, spans in covered.items() if len(spans) > 1}
+        units = {msg: len(spans) for msg, spans in covered.items() if len(spans) > 1}
     assert finals == [1] * n, "every message is finished exactly once"
 
 
@@ -106,15 +117,23 @@ def _execute_plan(data, offsets, lengths, keys):
     cvs_in = []
     for pi, p in enumerate(plan):
         cvs_out = [None] * p["out_cvs"]
+        K = p["chunks_per_lane"]
         for (msg, first, dst, lane, count, final) in p["segs"]:
             kw = list(struct.unpack("<8I", keys[msg])) if keys else oracle.iv()
             mode = oracle.KEYED_HASH if keys else 0
             if pi == 0:
+                # each lane folds its run of K chunks into one node, then the nodes pair up
                 o, L = offsets[msg], lengths[msg]
                 msg_bytes = data[o:o + L]
-                nodes = [oracle.chunk_cv(kw, mode, msg_bytes[1024 * j:1024 * (j + 1)], j,
-                                         is_root=final and count == 1)
-                         for j in range(first, first + count)]
+                n_msg = _chunks(L)
+                nodes = []
+                for x in range(count):
+                    c0 = first + x * K
+                    run = range(c0, min(c0 + K, n_msg))
+                    lone = final and count == 1
+                    cvs = [oracle.chunk_cv(kw, mode, msg_bytes[1024 * j:1024 * (j + 1)], j,
+                                           is_root=lone and len(run) == 1) for j in run]
+                    nodes.append(_pair_reduce(cvs, kw, mode, lone))
             else:
                 nodes = cvs_in[first:first + count]
             top = _pair_reduce(nodes, kw, mode, final)
@@ -127,7 +146,7 @@ def _execute_plan(data, offsets, lengths, keys):
 
 
 @pytest.mark.parametrize("keyed", [False, True])
-def test_executed_plan_matches_oracle(keyed):
+def test_executed_plan_matches_oracle(keyed, chunks_per_lane):
     rng = np.random.Generator(np.random.PCG64(11))
     lengths = [0, 1, 63, 64, 65, 1023, 1024, 1025, 13 * 1024 + 17, 3 * 1024 + 1000, 65 * 1024 + 5,
                256 * 1024, 256 * 1024 + 1, 511 * 1024 + 9] + rng.integers(0, 300 * 1024, size=12).tolist()
@@ -142,8 +161,10 @@ def test_executed_plan_matches_oracle(keyed):
         assert got[i] == oracle.hash(data[o:o + L], keys[i] if keys else None), (i, L)
 
 
-def test_executed_plan_deep_tree():
-    # 70,000 chunks of one message: pass 0 (274 groups) -> pass 1 (2 groups) -> pass 2
+def test_executed_plan_deep_tree(monkeypatch):
+    # 70,000 chunks of one message at one chunk per lane: pass 0 (274 groups) ->
+    # pass 1 (2 groups) -> pass 2
+    monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", "1")
     rng = np.random.Generator(np.random.PCG64(12))
     L = 70000 * 1024 - 100
     data = rng.bytes(L)
@@ -151,3 +172,13 @@ def test_executed_plan_deep_tree():
     plan = b3.debug_plan_batch([L])
     assert len(plan) == 3
     assert _execute_plan(data, [0], [L], [key])[0] == oracle.hash(data, key)
+
+
+def test_chunks_per_lane_choice(monkeypatch):
+    monkeypatch.delenv("BLAKE3_GPU_CHUNKS_PER_LANE", raising=False)
+    ks = [b3.debug_plan_batch([size])[0]["chunks_per_lane"] for size in
+          (1 << 20, 256 << 20, 1 << 30, 2 << 30, 4 << 30, 16 << 30)]
+    assert ks[0] == 1 and ks[-1] == 4 and ks == sorted(ks), ks
+    assert all(k in (1, 2, 4) for k in ks)
+    monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", "2")
+    assert b3.debug_plan_batch([1 << 20])[0]["chunks_per_lane"] == 2
