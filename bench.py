@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--cpu-sample-gib", type=float, default=2.0)
     ap.add_argument("--no-check", action="store_true", help="skip the full-digest oracle check")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--calibrate-copy", type=float, default=None, metavar="GIB",
+                    help="only run an elementwise copy kernel over GIB GiB (reads and writes that many "
+                         "bytes) --steps times: the reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the hash of one buffer "
@@ -102,6 +105,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.calibrate_copy is not None:
+        n = int(args.calibrate_copy * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
+                          "launches": args.steps}), flush=True)
+        return
     batch = args.workload == "batch64k"
     if batch:
         base, offs, lengths, keys_cpu = workloads.uniform_batch(65536, 65536, dev)
