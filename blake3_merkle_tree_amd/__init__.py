@@ -16,6 +16,7 @@ import ctypes
 import os
 import struct
 
+import numpy as np
 import torch
 
 __all__ = ["hash", "keyed_hash", "keyed_hash_batch", "group_cvs", "leaf_group_chunks", "strerror", "version",
@@ -49,7 +50,7 @@ def _load():
     vp, u64 = ctypes.c_void_p, ctypes.c_uint64
     lib.blake3_gpu_hash.argtypes = [vp, u64, vp, vp]
     lib.blake3_gpu_keyed_hash.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
-    lib.blake3_gpu_keyed_hash_batch.argtypes = [vp, ctypes.POINTER(u64), ctypes.POINTER(u64), vp, vp, u64, vp]
+    lib.blake3_gpu_keyed_hash_batch.argtypes = [vp, vp, vp, vp, vp, u64, vp]
     lib.blake3_gpu_group_cvs.argtypes = [vp, u64, u64, ctypes.POINTER(ctypes.c_uint32), ctypes.c_uint32, vp, vp]
     lib.blake3_gpu_leaf_group_chunks.argtypes = [u64]
     lib.blake3_gpu_leaf_group_chunks.restype = ctypes.c_uint32
@@ -108,6 +109,23 @@ def _key_words(key):
     return (ctypes.c_uint32 * 8)(*struct.unpack("<8I", key))
 
 
+def _u64_array(v, what):
+    """A sequence of non-negative integers as a contiguous uint64 host array (no copy for
+    a uint64 numpy array or CPU tensor)."""
+    if isinstance(v, torch.Tensor):
+        v = v.detach().cpu().numpy()
+    if isinstance(v, np.ndarray):
+        if v.dtype.kind not in "iu":
+            raise TypeError(f"{what} must hold integers")
+        if v.dtype.kind == "i" and v.size and int(v.min()) < 0:
+            raise ValueError(f"{what} must be non-negative")
+        return np.ascontiguousarray(v.reshape(-1), dtype=np.uint64)
+    try:
+        return np.asarray(v, dtype=np.uint64).reshape(-1)
+    except OverflowError:
+        raise ValueError(f"{what} must be non-negative 64-bit integers") from None
+
+
 def _out(out, device, n):
     if out is None:
         return torch.empty(n, dtype=torch.uint8, device=device)
@@ -143,21 +161,22 @@ def keyed_hash(t: torch.Tensor, key, out=None, stream=None) -> torch.Tensor:
 
 def keyed_hash_batch(base: torch.Tensor, offsets, lengths, keys=None, out=None, stream=None) -> torch.Tensor:
     """Hash messages base[offsets[i] : offsets[i] + lengths[i]] (byte offsets into the
-    tensor's bytes, multiples of 16). keys: None (default mode) or a device tensor with 32
-    bytes per message, shape (n, 32) uint8 or (n, 8) int32. Returns (n, 32) uint8."""
+    tensor's bytes, multiples of 16; offsets and lengths are sequences, numpy arrays or
+    CPU tensors). keys: None (default mode) or a device tensor with 32 bytes per message,
+    shape (n, 32) uint8 or (n, 8) int32. Returns (n, 32) uint8. Equal lengths at evenly
+    spaced offsets take a faster path that needs no launch table."""
     if not isinstance(base, torch.Tensor) or base.device.type != "cuda":
         raise ValueError("base must be a tensor on a HIP device")
     if not base.is_contiguous():
         raise ValueError("base must be contiguous (offsets address its bytes)")
-    offs = (ctypes.c_uint64 * len(offsets))(*[int(x) for x in offsets])
-    lens = (ctypes.c_uint64 * len(lengths))(*[int(x) for x in lengths])
+    offs = _u64_array(offsets, "offsets")
+    lens = _u64_array(lengths, "lengths")
     n = len(offs)
     if len(lens) != n:
         raise ValueError("offsets and lengths differ in size")
     nbytes = base.numel() * base.element_size()
-    for o, l in zip(offs, lens):
-        if o + l > nbytes:
-            raise ValueError("a message runs past the end of base")
+    if n and bool(np.any((offs > nbytes) | (lens > nbytes - np.minimum(offs, nbytes)))):
+        raise ValueError("a message runs past the end of base")
     kp = ctypes.c_void_p(0)
     if keys is not None:
         if not isinstance(keys, torch.Tensor) or keys.device != base.device or not keys.is_contiguous():
@@ -168,7 +187,8 @@ def keyed_hash_batch(base: torch.Tensor, offsets, lengths, keys=None, out=None, 
     out = _out(out, base.device, 32 * n).view(n, 32) if n else torch.empty((0, 32), dtype=torch.uint8,
                                                                            device=base.device)
     with torch.cuda.device(base.device):
-        rc = _load().blake3_gpu_keyed_hash_batch(ctypes.c_void_p(base.data_ptr() if nbytes else 0), offs, lens,
+        rc = _load().blake3_gpu_keyed_hash_batch(ctypes.c_void_p(base.data_ptr() if nbytes else 0),
+                                                 offs.ctypes.data, lens.ctypes.data,
                                                  kp, ctypes.c_void_p(out.data_ptr()),
                                                  n, _stream_handle(base.device, stream))
     _check(rc, "blake3_gpu_keyed_hash_batch")

@@ -26,26 +26,44 @@ namespace b3g {
 constexpr uint32_t kLeafLanes = 256;
 constexpr uint32_t kLevelLanes = 256;
 
-// Single message: segment geometry follows from blockIdx; the key is a kernel argument.
-struct SingleLeafArgs {
-    const uint8_t *in;     // message bytes (16-byte aligned)
-    uint64_t len;          // message length in bytes
-    uint64_t n_chunks;     // max(1, ceil(len / 1024))
-    uint64_t chunk_base;   // counter of chunk 0 (0 for a whole message)
-    uint32_t key[8];       // starting chaining value (key words, or the IV)
-    uint32_t mode;         // kKeyedHash or 0
-    uint32_t may_root;     // 1: a single workgroup is the whole message and emits the digest
-    uint32_t *cv_out;      // one 8-word CV per workgroup (subtree roots, never ROOT-flagged)
-    uint8_t *digest;       // 32-byte digest (when may_root and gridDim.x == 1)
+// Uniform batch: n messages of `len` bytes each, message m at base + m * stride (one
+// message is n = 1). Geometry follows from blockIdx, so no task table is needed.
+//   Case A (lanes_per_msg != 0): a message's nodes fit one workgroup; each message takes
+//     lanes_per_msg = R lanes (a power of two), a workgroup holds 256 / R messages and
+//     finishes them (digests).
+//   Case B (lanes_per_msg == 0): a message spans `groups` workgroups; workgroup w reduces
+//     group (w mod groups) of message (w / groups) to one CV at cv_out + 8*w.
+struct UniformLeafArgs {
+    const uint8_t *base;     // message 0 (16-byte aligned)
+    uint64_t stride;         // bytes from one message to the next (multiple of 16)
+    uint64_t len;            // bytes per message
+    uint64_t n_chunks;       // chunks per message: max(1, ceil(len / 1024))
+    uint64_t chunk_base;     // counter of chunk 0 of every message (0 for whole messages)
+    uint32_t n_msgs;
+    uint32_t lanes_per_msg;  // R in case A, 0 in case B
+    uint32_t groups;         // workgroups per message in case B
+    uint32_t may_root;       // 1: a workgroup holding a whole message emits its digest
+    const uint32_t *keys;    // 8 key words per message, or nullptr: every message uses `key`
+    uint32_t key[8];         // key words (or the IV) when keys == nullptr
+    uint32_t mode;           // kKeyedHash or 0
+    uint32_t *cv_out;
+    uint8_t *digests;        // message m's digest at digests + 32*m
 };
 
-struct SingleLevelArgs {
-    const uint32_t *cv_in; // m CVs, 8 words each
-    uint64_t m;
+// Uniform level pass: every message has g_in CVs, contiguous in cv_in (message m's at
+// cv_in + 8 * m * g_in). Case A (g_in <= 256): R = next power of two of g_in lanes per
+// message, digests out. Case B: g_out = ceil(g_in / 256) workgroups per message, CVs out.
+struct UniformLevelArgs {
+    const uint32_t *cv_in;
+    uint64_t g_in;
+    uint32_t n_msgs;
+    uint32_t lanes_per_msg;  // R in case A, 0 in case B
+    uint32_t g_out;          // case B
+    const uint32_t *keys;
     uint32_t key[8];
     uint32_t mode;
-    uint32_t *cv_out;      // one CV per workgroup (when gridDim.x > 1)
-    uint8_t *digest;       // when gridDim.x == 1
+    uint32_t *cv_out;
+    uint8_t *digests;
 };
 
 // Batch mode: workgroups read their segments (struct Seg, b3_plan.h) from a task table.
@@ -77,9 +95,9 @@ struct BatchLevelArgs {
 
 // chunks_per_lane (K) is 1, 2 or 4: each leaf workgroup covers 256*K chunks. `staged`
 // selects the LDS-staged input path for full waves instead of per-lane loads.
-hipError_t launch_single_leaf(const SingleLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
-                              hipStream_t s);
-hipError_t launch_single_level(const SingleLevelArgs &a, uint32_t grid, hipStream_t s);
+hipError_t launch_uniform_leaf(const UniformLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
+                               hipStream_t s);
+hipError_t launch_uniform_level(const UniformLevelArgs &a, uint32_t grid, hipStream_t s);
 hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
                              hipStream_t s);
 hipError_t launch_batch_level(const BatchLevelArgs &a, uint32_t grid, hipStream_t s);

@@ -63,9 +63,10 @@ __device__ __forceinline__ Block load_block(const uint4 *p) { return Block{p[0],
 // pairs with two register sets, so the loads of a block are issued ahead of its
 // compression and no registers are copied between iterations; the reload of the even set
 // is unconditional (the last iteration re-reads block 14, which is in cache) so that the
-// loop carries no conditional register values.
+// loop carries no conditional register values. `end_flags` go on the last block
+// (CHUNK_END, plus ROOT when the chunk is the whole message).
 __device__ __forceinline__ void hash_full_chunk(uint32_t (&cv)[8], const uint8_t *chunk, uint32_t ctr_lo,
-                                                uint32_t ctr_hi, uint32_t mode) {
+                                                uint32_t ctr_hi, uint32_t mode, uint32_t end_flags) {
     const uint4 *p = reinterpret_cast<const uint4 *>(chunk);
     Block even = load_block(p);
     for (uint32_t b = 0; b < kBlocksPerChunk; b += 2) {
@@ -73,7 +74,7 @@ __device__ __forceinline__ void hash_full_chunk(uint32_t (&cv)[8], const uint8_t
         compress_block(cv, even, ctr_lo, ctr_hi, mode | (b == 0 ? kChunkStart : 0u));
         const uint32_t next = b + 2 < kBlocksPerChunk ? b + 2 : kBlocksPerChunk - 2;
         even = load_block(p + 4 * next);
-        compress_block(cv, odd, ctr_lo, ctr_hi, mode | (b + 2 == kBlocksPerChunk ? kChunkEnd : 0u));
+        compress_block(cv, odd, ctr_lo, ctr_hi, mode | (b + 2 == kBlocksPerChunk ? end_flags : 0u));
     }
 }
 
@@ -174,10 +175,12 @@ __device__ __forceinline__ void lane_subtree(uint32_t (&c)[8], const uint8_t *pt
 // (with equal offsets every lane's line falls in the same cache set and channel and is
 // evicted between the two blocks that share it). The chunk CVs wait in LDS slots, one
 // column per lane (slot j, word w at slots[(j * 8 + w) * kLanes]), and are folded at the
-// end, level by level: node i = parent(node 2i, node 2i+1).
+// end, level by level: node i = parent(node 2i, node 2i+1). `root_flag` (ROOT or 0)
+// marks the lane's node as the whole message: its last compression carries it.
 template <uint32_t K>
 __device__ __forceinline__ void direct_subtree(uint32_t (&c)[8], const uint8_t *ptr, uint64_t ctr0,
-                                               const uint32_t (&key)[8], uint32_t mode, uint32_t *slots) {
+                                               const uint32_t (&key)[8], uint32_t mode, uint32_t root_flag,
+                                               uint32_t *slots) {
     const uint32_t rot = threadIdx.x % K;
     for (uint32_t step = 0; step < K; ++step) {
         const uint32_t k = (step + rot) % K;
@@ -185,7 +188,7 @@ __device__ __forceinline__ void direct_subtree(uint32_t (&c)[8], const uint8_t *
         for (int w = 0; w < 8; ++w) c[w] = key[w];
         const uint64_t ctr = ctr0 + k;
         hash_full_chunk(c, ptr + static_cast<uint64_t>(k) * kChunkBytes, static_cast<uint32_t>(ctr),
-                        static_cast<uint32_t>(ctr >> 32), mode);
+                        static_cast<uint32_t>(ctr >> 32), mode, kChunkEnd | (K == 1 ? root_flag : 0u));
         if (K == 1) return;
 #pragma unroll
         for (int w = 0; w < 8; ++w) slots[(k * 8 + w) * kLanes] = c[w];
@@ -200,7 +203,7 @@ __device__ __forceinline__ void direct_subtree(uint32_t (&c)[8], const uint8_t *
             }
 #pragma unroll
             for (int w = 0; w < 8; ++w) c[w] = key[w];
-            compress(c, m, 0, 0, kBlockBytes, mode | kParent);
+            compress(c, m, 0, 0, kBlockBytes, mode | kParent | (width == 2 ? root_flag : 0u));
             if (width > 2) {
 #pragma unroll
                 for (int w = 0; w < 8; ++w) slots[(i * 8 + w) * kLanes] = c[w];
@@ -246,7 +249,7 @@ __device__ __forceinline__ void stage_issue(const Rows &rows, uint32_t off, uint
 
 template <uint32_t K, class Rows>
 __device__ __forceinline__ void staged_subtree(uint32_t (&c)[8], const Rows &rows, uint32_t *stage, uint64_t ctr0,
-                                               const uint32_t (&key)[8], uint32_t mode) {
+                                               const uint32_t (&key)[8], uint32_t mode, uint32_t root_flag) {
     const uint32_t lw = threadIdx.x % kWaveLanes;
     const uint4 *row = reinterpret_cast<const uint4 *>(stage) + lw * 8;
     uint32_t slot1c[8], slot2c[8];
@@ -270,9 +273,9 @@ __device__ __forceinline__ void staged_subtree(uint32_t (&c)[8], const Rows &row
             if (bp + 1 < kBlocksPerChunk / 2) stage_issue(rows, k * kChunkBytes + (bp + 1) * 2 * kBlockBytes, stage);
             else if (k + 1 < K) stage_issue(rows, (k + 1) * kChunkBytes, stage);
             compress_block(c, Block{q0, q1, q2, q3}, lo, hi,
-                           mode | (bp + 1 == kBlocksPerChunk / 2 ? kChunkEnd : 0u));
+                           mode | (bp + 1 == kBlocksPerChunk / 2 ? kChunkEnd | (K == 1 ? root_flag : 0u) : 0u));
         }
-        if (K > 1) fold_chunk<K>(c, k, slot1c, slot2c, k + 1 < K, K, key, mode);
+        if (K > 1) fold_chunk<K>(c, k, slot1c, slot2c, k + 1 < K, root_flag ? K - 1 : K, key, mode);
     }
 }
 
@@ -298,26 +301,39 @@ __device__ __forceinline__ void load_cv(uint32_t (&cv)[8], const uint32_t *src) 
 
 // ---- segment descriptions ------------------------------------------------------------
 
-// Single message: the workgroup holds one segment of `n` nodes at lane 0.
-struct SingleSegs {
-    uint32_t n;
-    bool whole;  // the segment is the whole message: its top compression carries ROOT
+// Uniform batch: `segs` segments of `nodes` nodes each, segment s at lanes
+// [s << lanes_log2, (s << lanes_log2) + nodes), all of one kind (whole messages, or one
+// group of a message).
+struct UniformSegs {
+    uint32_t lanes_log2;
+    uint32_t nodes;
+    uint32_t segs;
+    uint32_t first_msg;  // message of segment 0
+    bool whole;          // segments are whole messages: their top compression carries ROOT
+    const uint32_t *keys;
     uint32_t key[8];
     uint32_t mode_flag;
     uint32_t *cv_out;
-    uint8_t *digest;
+    uint8_t *digests;
 
-    __device__ int seg_of(uint32_t pos) const { return pos < n ? 0 : -1; }
-    __device__ uint32_t start(int) const { return 0; }
-    __device__ uint32_t count(int) const { return n; }
+    __device__ int seg_of(uint32_t pos) const {
+        const uint32_t s = pos >> lanes_log2;
+        return s < segs && pos - (s << lanes_log2) < nodes ? static_cast<int>(s) : -1;
+    }
+    __device__ uint32_t start(int s) const { return static_cast<uint32_t>(s) << lanes_log2; }
+    __device__ uint32_t count(int) const { return nodes; }
     __device__ bool final(int) const { return whole; }
     __device__ uint32_t mode() const { return mode_flag; }
-    __device__ void key_words(int, uint32_t (&kw)[8]) const {
+    __device__ void key_words(int s, uint32_t (&kw)[8]) const {
+        if (keys) {
+            load_cv(kw, keys + 8ull * (first_msg + static_cast<uint32_t>(s)));
+        } else {
 #pragma unroll
-        for (int w = 0; w < 8; ++w) kw[w] = key[w];
+            for (int w = 0; w < 8; ++w) kw[w] = key[w];
+        }
     }
-    __device__ void emit(int, const uint32_t (&cv)[8]) const {
-        if (whole) store_digest(digest, cv);
+    __device__ void emit(int s, const uint32_t (&cv)[8]) const {
+        if (whole) store_digest(digests + 32ull * (first_msg + static_cast<uint32_t>(s)), cv);
         else store_cv(cv_out + 8ull * blockIdx.x, cv);
     }
 };
@@ -432,60 +448,119 @@ constexpr uint32_t leaf_lds_words() {
     return tree > chunk_phase ? tree : chunk_phase;
 }
 
+// Sets the fields of a UniformSegs that do not depend on the pass.
+template <typename Args>
+__device__ __forceinline__ void uniform_common(UniformSegs &sg, const Args &a) {
+    sg.keys = a.keys;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sg.key[w] = a.key[w];
+    sg.mode_flag = a.mode;
+    sg.cv_out = a.cv_out;
+    sg.digests = a.digests;
+}
+
+// Case A groups: `per_wg` messages per workgroup, R = 1 << lanes_log2 lanes each.
+__device__ __forceinline__ void uniform_case_a(UniformSegs &sg, uint32_t lanes_per_msg, uint32_t n_msgs,
+                                               uint32_t wg_lanes) {
+    sg.lanes_log2 = static_cast<uint32_t>(__builtin_ctz(lanes_per_msg));
+    const uint32_t per_wg = wg_lanes >> sg.lanes_log2;
+    sg.first_msg = blockIdx.x * per_wg;
+    sg.segs = n_msgs - sg.first_msg < per_wg ? n_msgs - sg.first_msg : per_wg;
+}
+
 template <uint32_t K, bool Staged>
-__global__ __launch_bounds__(kLeafLanes) void leaf_single_kernel(SingleLeafArgs a) {
+__global__ __launch_bounds__(kLeafLanes) void leaf_uniform_kernel(UniformLeafArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t lds[leaf_lds_words<K, Staged>()];
     const uint32_t lane = threadIdx.x;
     constexpr uint64_t kWgChunks = static_cast<uint64_t>(kLanes) * K;
-    const uint64_t first = static_cast<uint64_t>(blockIdx.x) * kWgChunks;
-    const uint64_t left = a.n_chunks - first;
-    const uint32_t n_wg = left < kWgChunks ? static_cast<uint32_t>(left) : static_cast<uint32_t>(kWgChunks);
-    const uint32_t nodes = (n_wg + K - 1) / K;
-    const uint64_t c0 = first + static_cast<uint64_t>(lane) * K;
+    UniformSegs sg{};
+    uint64_t first_chunk = 0;
+    if (a.lanes_per_msg != 0) {  // case A: whole messages, several per workgroup
+        uniform_case_a(sg, a.lanes_per_msg, a.n_msgs, kLanes);
+        sg.nodes = static_cast<uint32_t>((a.n_chunks + K - 1) / K);
+        sg.whole = a.may_root != 0;
+    } else {  // case B: one group of one message
+        sg.lanes_log2 = 8;
+        sg.first_msg = blockIdx.x / a.groups;
+        sg.segs = 1;
+        first_chunk = static_cast<uint64_t>(blockIdx.x - sg.first_msg * a.groups) * kWgChunks;
+        const uint64_t left = a.n_chunks - first_chunk;
+        sg.nodes = left >= kWgChunks ? kLanes : static_cast<uint32_t>((left + K - 1) / K);
+        sg.whole = a.may_root != 0 && a.groups == 1;
+    }
+    uniform_common(sg, a);
+
+    const uint32_t s = lane >> sg.lanes_log2, x = lane - (s << sg.lanes_log2);
     uint32_t nl = 0, last_len = kChunkBytes;
-    if (lane < nodes) {
-        nl = n_wg - lane * K < K ? n_wg - lane * K : K;
+    uint64_t c0 = 0;
+    const uint8_t *ptr = a.base;
+    uint32_t key[8];
+    sg.key_words(s < sg.segs ? static_cast<int>(s) : 0, key);
+    if (s < sg.segs && x < sg.nodes) {
+        c0 = first_chunk + static_cast<uint64_t>(x) * K;
+        nl = a.n_chunks - c0 < K ? static_cast<uint32_t>(a.n_chunks - c0) : K;
         const uint64_t rem = a.len - (c0 + nl - 1) * kChunkBytes;  // bytes from the lane's last chunk on
         last_len = a.len == 0 ? 0u : (rem < kChunkBytes ? static_cast<uint32_t>(rem) : kChunkBytes);
+        ptr = a.base + static_cast<uint64_t>(sg.first_msg + s) * a.stride + c0 * kChunkBytes;
     }
-    const bool whole = a.may_root && gridDim.x == 1;
-    const uint32_t key[8] = {a.key[0], a.key[1], a.key[2], a.key[3], a.key[4], a.key[5], a.key[6], a.key[7]};
+    // a message of one node: the lane's own subtree is the whole tree
+    const uint32_t root_flag = sg.whole && sg.nodes == 1 ? kRoot : 0u;
     uint32_t cv[8];
 #pragma unroll
     for (int w = 0; w < 8; ++w) cv[w] = key[w];
     if (__ballot(nl != K || last_len != kChunkBytes) == 0) {
         if (Staged) {
             const uint32_t lw = lane % kWaveLanes;
-            const uint64_t wave_first = first + static_cast<uint64_t>(lane - lw) * K;
-            const EvenRows rows{a.in + (wave_first + (lw >> 3) * K) * kChunkBytes + 16 * stage_piece(lw),
-                                8ull * K * kChunkBytes};
-            staged_subtree<K>(cv, rows, lds + (lane / kWaveLanes) * (kStageBytes / 4), a.chunk_base + c0, key,
-                              a.mode);
+            uint32_t *stage = lds + (lane / kWaveLanes) * (kStageBytes / 4);
+            if (a.lanes_per_msg == 0) {  // the wave's runs of K chunks are evenly spaced
+                // lane lw reads from ptr - (lw - (lw >> 3)) * K chunks: row lw >> 3 of load 0
+                const EvenRows rows{ptr - static_cast<uint64_t>(lw - (lw >> 3)) * K * kChunkBytes +
+                                        16 * stage_piece(lw),
+                                    8ull * K * kChunkBytes};
+                staged_subtree<K>(cv, rows, stage, a.chunk_base + c0, key, a.mode, root_flag);
+            } else {  // gather the 8 rows each lane loads for
+                const uint64_t my = reinterpret_cast<uint64_t>(ptr);
+                GatherRows rows;
+#pragma unroll
+                for (uint32_t j = 0; j < 8; ++j)
+                    rows.src[j] = reinterpret_cast<const uint8_t *>(__shfl(my, static_cast<int>(8 * j + (lw >> 3)))) +
+                                  16 * stage_piece(lw);
+                staged_subtree<K>(cv, rows, stage, a.chunk_base + c0, key, a.mode, root_flag);
+            }
         } else {
-            direct_subtree<K>(cv, a.in + c0 * kChunkBytes, a.chunk_base + c0, key, a.mode, lds + lane);
+            direct_subtree<K>(cv, ptr, a.chunk_base + c0, key, a.mode, root_flag, lds + lane);
         }
     } else if (nl > 0) {
-        lane_subtree<K>(cv, a.in + c0 * kChunkBytes, nl, last_len, a.chunk_base + c0, key, a.mode,
-                        whole && nodes == 1);
+        lane_subtree<K>(cv, ptr, nl, last_len, a.chunk_base + c0, key, a.mode, root_flag != 0);
     }
-    __syncthreads();  // every wave is done with its stage buffer before the tree reuses it
-    SingleSegs sg{nodes, whole, {key[0], key[1], key[2], key[3], key[4], key[5], key[6], key[7]}, a.mode,
-                  a.cv_out, a.digest};
-    tree_reduce<kLanes>(cv, sg, ceil_log2(nodes), reinterpret_cast<uint32_t(*)[8][kLanes]>(lds));
+    __syncthreads();  // every wave is done with its stage buffer or slots before the tree reuses them
+    tree_reduce<kLanes>(cv, sg, ceil_log2(sg.nodes), reinterpret_cast<uint32_t(*)[8][kLanes]>(lds));
 }
 
-__global__ __launch_bounds__(kLevelLanes) void level_single_kernel(SingleLevelArgs a) {
+__global__ __launch_bounds__(kLevelLanes) void level_uniform_kernel(UniformLevelArgs a) {
     __shared__ uint32_t buf[2][8][kLevelLanes];
     const uint32_t lane = threadIdx.x;
-    const uint64_t first = static_cast<uint64_t>(blockIdx.x) * kLevelLanes;
-    const uint64_t left = a.m - first;
-    const uint32_t n_wg = left < kLevelLanes ? static_cast<uint32_t>(left) : kLevelLanes;
+    UniformSegs sg{};
+    uint64_t first_cv = 0;
+    if (a.lanes_per_msg != 0) {  // case A: the last g_in CVs of several messages, finished here
+        uniform_case_a(sg, a.lanes_per_msg, a.n_msgs, kLevelLanes);
+        sg.nodes = static_cast<uint32_t>(a.g_in);
+        sg.whole = true;
+    } else {  // case B: 256 CVs (or the rest) of one message
+        sg.lanes_log2 = 8;
+        sg.first_msg = blockIdx.x / a.g_out;
+        sg.segs = 1;
+        first_cv = static_cast<uint64_t>(blockIdx.x - sg.first_msg * a.g_out) * kLevelLanes;
+        const uint64_t left = a.g_in - first_cv;
+        sg.nodes = left < kLevelLanes ? static_cast<uint32_t>(left) : kLevelLanes;
+        sg.whole = false;
+    }
+    uniform_common(sg, a);
+    const uint32_t s = lane >> sg.lanes_log2, x = lane - (s << sg.lanes_log2);
     uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (lane < n_wg) load_cv(cv, a.cv_in + 8 * (first + lane));
-    SingleSegs sg{n_wg, gridDim.x == 1,
-                  {a.key[0], a.key[1], a.key[2], a.key[3], a.key[4], a.key[5], a.key[6], a.key[7]},
-                  a.mode, a.cv_out, a.digest};
-    tree_reduce<kLevelLanes>(cv, sg, ceil_log2(n_wg), buf);
+    if (s < sg.segs && x < sg.nodes)
+        load_cv(cv, a.cv_in + 8 * (static_cast<uint64_t>(sg.first_msg + s) * a.g_in + first_cv + x));
+    tree_reduce<kLevelLanes>(cv, sg, ceil_log2(sg.nodes), buf);
 }
 
 template <uint32_t K, bool Staged>
@@ -530,9 +605,10 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_batch_kernel(BatchLeafArgs a)
             for (uint32_t j = 0; j < 8; ++j)
                 rows.src[j] = reinterpret_cast<const uint8_t *>(__shfl(my, static_cast<int>(8 * j + (lw >> 3)))) +
                               16 * stage_piece(lw);
-            staged_subtree<K>(cv, rows, lds + (lane / kWaveLanes) * (kStageBytes / 4), c0, key, sg.mode());
+            staged_subtree<K>(cv, rows, lds + (lane / kWaveLanes) * (kStageBytes / 4), c0, key, sg.mode(),
+                              root ? kRoot : 0u);
         } else {
-            direct_subtree<K>(cv, ptr, c0, key, sg.mode(), lds + lane);
+            direct_subtree<K>(cv, ptr, c0, key, sg.mode(), root ? kRoot : 0u, lds + lane);
         }
     } else if (nl > 0) {
         lane_subtree<K>(cv, ptr, nl, last_len, c0, key, sg.mode(), root);
@@ -559,23 +635,23 @@ __global__ __launch_bounds__(kLevelLanes) void level_batch_kernel(BatchLevelArgs
 
 }  // namespace
 
-hipError_t launch_single_leaf(const SingleLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
-                              hipStream_t s) {
+hipError_t launch_uniform_leaf(const UniformLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
+                               hipStream_t s) {
     const dim3 g(grid), b(kLeafLanes);
     switch (chunks_per_lane * 2 + (staged ? 1 : 0)) {
-        case 2: hipLaunchKernelGGL((leaf_single_kernel<1, false>), g, b, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((leaf_single_kernel<1, true>), g, b, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((leaf_single_kernel<2, false>), g, b, 0, s, a); break;
-        case 5: hipLaunchKernelGGL((leaf_single_kernel<2, true>), g, b, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((leaf_single_kernel<4, false>), g, b, 0, s, a); break;
-        case 9: hipLaunchKernelGGL((leaf_single_kernel<4, true>), g, b, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((leaf_uniform_kernel<1, false>), g, b, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((leaf_uniform_kernel<1, true>), g, b, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((leaf_uniform_kernel<2, false>), g, b, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((leaf_uniform_kernel<2, true>), g, b, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((leaf_uniform_kernel<4, false>), g, b, 0, s, a); break;
+        case 9: hipLaunchKernelGGL((leaf_uniform_kernel<4, true>), g, b, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_single_level(const SingleLevelArgs &a, uint32_t grid, hipStream_t s) {
-    hipLaunchKernelGGL(level_single_kernel, dim3(grid), dim3(kLevelLanes), 0, s, a);
+hipError_t launch_uniform_level(const UniformLevelArgs &a, uint32_t grid, hipStream_t s) {
+    hipLaunchKernelGGL(level_uniform_kernel, dim3(grid), dim3(kLevelLanes), 0, s, a);
     return hipGetLastError();
 }
 

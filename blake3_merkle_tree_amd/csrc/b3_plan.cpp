@@ -8,10 +8,10 @@
 // subtree is complete and at least as large as the right), the tree over the group
 // roots is the BLAKE3 tree of the message, one level up.
 //
-// Packing. A full group fills a workgroup alone. Smaller groups are sorted by the next
-// power of two R of their size (largest first) and laid out back to back; because the
-// sizes are non-increasing powers of two, every group then starts at a multiple of its
-// own R, which keeps the in-workgroup pairing from mixing groups.
+// Packing. A full group fills a workgroup alone. Smaller groups are bucketed by the next
+// power of two R of their size (largest first, in one linear pass) and laid out back to
+// back; because the sizes are non-increasing powers of two, every group then starts at a
+// multiple of its own R, which keeps the in-workgroup pairing from mixing groups.
 #include "b3_plan.h"
 
 #include <stdlib.h>
@@ -35,23 +35,40 @@ struct Group {
     bool final;
 };
 
-// Lays groups out over workgroups of `lanes` lanes.
-int pack(std::vector<Group> &groups, uint32_t lanes, PassPlan *p) {
+// Lays groups out over workgroups of `lanes` lanes (a power of two).
+int pack(const std::vector<Group> &groups, uint32_t lanes, PassPlan *p) {
     p->lanes = lanes;  // g.count is in nodes (lanes)
-    std::vector<Group> partial;
+    // bucket the partial groups by log2 of their power of two (stable within a bucket)
+    const uint32_t top = ceil_log2_host(lanes);
+    std::vector<uint64_t> bucket_size(top + 2, 0);
+    uint64_t full = 0;
     for (const Group &g : groups) {
+        if (g.count == lanes) ++full;
+        else ++bucket_size[ceil_log2_host(g.count)];
+    }
+    std::vector<uint64_t> bucket_at(top + 2, 0);  // largest power first
+    uint64_t pos = 0;
+    for (int b = static_cast<int>(top); b >= 0; --b) {
+        bucket_at[b] = pos;
+        pos += bucket_size[b];
+    }
+    std::vector<uint32_t> order(pos);
+    p->segs.reserve(groups.size());
+    p->wg_first_seg.reserve(full + pos / 2 + 2);
+    p->wg_levels.reserve(full + pos / 2 + 1);
+    for (size_t i = 0; i < groups.size(); ++i) {
+        const Group &g = groups[i];
         if (g.count == lanes) {
             p->wg_first_seg.push_back(static_cast<uint32_t>(p->segs.size()));
             p->wg_levels.push_back(static_cast<uint8_t>(ceil_log2_host(g.count)));
             p->segs.push_back(Seg{g.msg, g.first, g.dst, seg_info(0, g.count, g.final)});
         } else {
-            partial.push_back(g);
+            order[bucket_at[ceil_log2_host(g.count)]++] = static_cast<uint32_t>(i);
         }
     }
-    std::stable_sort(partial.begin(), partial.end(),
-                     [](const Group &a, const Group &b) { return next_pow2(a.count) > next_pow2(b.count); });
     uint32_t offset = lanes;  // forces a new workgroup for the first partial group
-    for (const Group &g : partial) {
+    for (uint32_t i : order) {
+        const Group &g = groups[i];
         const uint32_t r = next_pow2(g.count);
         if (offset + r > lanes) {
             p->wg_first_seg.push_back(static_cast<uint32_t>(p->segs.size()));
@@ -84,6 +101,11 @@ uint32_t choose_chunks_per_lane(uint64_t total_chunks) {
     return 1;
 }
 
+bool uniform_batch_disabled() {
+    const char *e = getenv("BLAKE3_GPU_BATCH_TABLE");
+    return e != nullptr && e[0] == '1' && e[1] == 0;
+}
+
 bool use_lds_staging() {
     const char *e = getenv("BLAKE3_GPU_STAGING");
     return e != nullptr && e[0] == 'l' && e[1] == 'd' && e[2] == 's' && e[3] == 0;
@@ -114,6 +136,7 @@ int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_
         const uint64_t lanes = pass == 0 ? leaf_lanes : level_lanes;
         const uint64_t span = lanes * per_node;  // units (chunks or CVs) per full group
         std::vector<Group> groups;
+        groups.reserve(pass == 0 ? n : n / 4 + 16);
         uint64_t out_cvs = 0;
         for (uint64_t i = 0; i < n; ++i) {
             if (nodes[i] == 0) continue;

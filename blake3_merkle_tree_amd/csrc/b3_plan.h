@@ -58,6 +58,11 @@ uint32_t choose_chunks_per_lane(uint64_t total_chunks);
 // coalesced direct-to-LDS loads when BLAKE3_GPU_STAGING=lds is set in the environment.
 bool use_lds_staging();
 
+// Batches of equal lengths at evenly spaced offsets skip the planner (their geometry is
+// implied); BLAKE3_GPU_BATCH_TABLE=1 in the environment routes them through the task
+// table like any other batch (for tests).
+bool uniform_batch_disabled();
+
 // Builds the passes for messages of the given byte lengths. Pass 0 groups
 // leaf_lanes * chunks_per_lane chunks per workgroup (one node per lane); later passes
 // group level_lanes CVs. Returns 0 (B3G_OK) or a negative b3g_status (B3G_ETOOBIG when a

@@ -83,9 +83,13 @@ int blake3_gpu_keyed_hash(const void *dev_in, uint64_t len, const uint32_t key[8
  *   dev_keys      device array of n*8 uint32 key words (message i's key at 8*i), or NULL
  *                 for default (unkeyed) mode for every message.
  *   dev_out       device pointer to n*32 writable bytes; digest i at byte 32*i.
- *   n             message count, 0 .. 2^32-1 (0 enqueues nothing and returns B3G_OK).
- * The host arrays are read during the call only (the task table built from them is
- * copied to device scratch in stream order before the call returns).
+ *   n             message count (0 enqueues nothing and returns B3G_OK); at most 2^32-1
+ *                 unless the batch is uniform (below).
+ * The host arrays are read during the call only. A uniform batch (every length equal, and
+ * offsets evenly spaced: offset i = offset 0 + i*d for one d, a multiple of 16, possibly
+ * 0) needs no table: its launch geometry follows from (offset 0, d, length, n). Any other
+ * batch is planned on the host into a task table that is copied to device scratch in
+ * stream order before the call returns. Both give the same digests.
  * Errors: EINVAL (NULL arrays with n > 0, NULL dev_out, NULL dev_base with a non-empty
  * message, offset + length overflowing 64 bits), EALIGN (misaligned dev_base or offset), ETOOBIG, ENOMEM, EHIP.
  */
@@ -128,8 +132,9 @@ int blake3_gpu_version(void);
 
 /*
  * Inspection of the batch planner, for tests and tools (no GPU work, no HIP call).
- * Plans the launches blake3_gpu_keyed_hash_batch would make for n messages of the given
- * byte lengths and serialises the plan into out[0 .. out_words) as uint64 words:
+ * Plans the launches blake3_gpu_keyed_hash_batch makes for n messages of the given byte
+ * lengths when the batch is not uniform, and serialises the plan into out[0 .. out_words)
+ * as uint64 words:
  *   [passes] then per pass [lanes, chunks per lane K, workgroups W, segments S, in_cvs,
  *   out_cvs, W+1 first-segment indices, W level counts, S x (msg, first, dst, info)].
  * Segment info packs bits 0..11 lane start, 12..23 node count - 1, 31 final. In pass 0 a

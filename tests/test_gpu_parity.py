@@ -192,12 +192,16 @@ def test_workload_ragged256(b3, dev):
     assert _digests_to_bytes(out) == want
 
 
-def test_workload_batch64k(b3, dev):
+def test_workload_batch64k(b3, dev, monkeypatch):
     from blake3_merkle_tree_amd import workloads
     base, offs, lengths, keys = workloads.uniform_batch(65536, 65536, dev)
     out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))
     again = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))
     assert torch.equal(out, again)
+    # the same batch through the launch table agrees
+    monkeypatch.setenv("BLAKE3_GPU_BATCH_TABLE", "1")
+    assert torch.equal(b3.keyed_hash_batch(base, offs, lengths, keys.to(dev)), out)
+    monkeypatch.delenv("BLAKE3_GPU_BATCH_TABLE")
     host = _host(base)
     del base
     want = oracle.hash_batch(host, offs, lengths, keys.numpy().tobytes(), nthreads=NTHREADS)
@@ -258,3 +262,49 @@ def test_chunks_per_lane_paths(b3, dev, monkeypatch, k, staging):
     out = b3.keyed_hash_batch(base, offs, blens, keys.to(dev))
     want = oracle.hash_batch(_host(base), offs, blens, keys.numpy().tobytes(), nthreads=NTHREADS)
     assert _digests_to_bytes(out) == want
+
+
+# (count, length, stride): equal lengths at evenly spaced offsets take the table-free path
+UNIFORM_CASES = [
+    (1000, 0, 16),
+    (513, 1, 16),
+    (300, 1024, 1024),  # one full chunk per message: the chunk carries ROOT
+    (100, 2048, 2048),
+    (200, 4096, 4096),  # at four chunks per lane: one node per message, ROOT on its last parent
+    (300, 3 * 1024 + 5, 4096),
+    (129, 64 * 1024, 64 * 1024 + 32),
+    (77, 200 * 1024 + 1, 256 * 1024),
+    (50, 5000, 0),  # every message is the same bytes; the keys differ
+    (9, 1024 * 1024 + 1000, 1024 * 1024 + 1024),
+    (3, 4 * 1024 * 1024, 4 * 1024 * 1024),
+    (2, 65537 * 1024 + 3, 65537 * 1024 + 16),  # at one chunk per lane: two level passes
+]
+
+
+@pytest.mark.parametrize("staging", ["direct", "lds"])
+@pytest.mark.parametrize("k", [None, 1, 4])
+def test_uniform_batches(b3, dev, monkeypatch, k, staging):
+    if k is not None:
+        monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", str(k))
+    monkeypatch.setenv("BLAKE3_GPU_STAGING", staging)
+    from blake3_merkle_tree_amd import workloads
+    for ci, (count, L, stride) in enumerate(UNIFORM_CASES):
+        offs = np.arange(count, dtype=np.uint64) * stride
+        lengths = np.full(count, L, dtype=np.uint64)
+        total = (count - 1) * stride + L + 16
+        base = workloads.random_bytes(total, 50 + ci, dev)
+        host = _host(base)
+        keys = workloads.key_bytes(60 + ci, count)
+        for keyed in (True, False):
+            _say("uniform batch", count, "x", L, "stride", stride, "k", k, "keyed", keyed)
+            out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev) if keyed else None)
+            want = oracle.hash_batch(host, offs.tolist(), lengths.tolist(),
+                                     keys.numpy().tobytes() if keyed else None, nthreads=NTHREADS)
+            assert _digests_to_bytes(out) == want, (count, L, stride, keyed)
+        # the same batch through the launch table
+        monkeypatch.setenv("BLAKE3_GPU_BATCH_TABLE", "1")
+        assert torch.equal(b3.keyed_hash_batch(base, offs, lengths, keys.to(dev)),
+                           b3.keyed_hash_batch(base, offs, lengths, keys.to(dev)))
+        assert _digests_to_bytes(b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))) == \
+            oracle.hash_batch(host, offs.tolist(), lengths.tolist(), keys.numpy().tobytes(), nthreads=NTHREADS)
+        monkeypatch.delenv("BLAKE3_GPU_BATCH_TABLE")
