@@ -286,6 +286,20 @@ __device__ __forceinline__ void store_digest(uint8_t *out, const uint32_t (&cv)[
         for (int k = 0; k < 4; ++k) out[4 * w + k] = static_cast<uint8_t>(cv[w] >> (8 * k));
 }
 
+// Words j and 4 + j of a digest or CV (one lane of a quad's share of a node).
+__device__ __forceinline__ void store_digest_pair(uint8_t *out, uint32_t j, uint32_t lo, uint32_t hi) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        out[4 * j + k] = static_cast<uint8_t>(lo >> (8 * k));
+        out[16 + 4 * j + k] = static_cast<uint8_t>(hi >> (8 * k));
+    }
+}
+
+__device__ __forceinline__ void store_cv_pair(uint32_t *dst, uint32_t j, uint32_t lo, uint32_t hi) {
+    dst[j] = lo;
+    dst[4 + j] = hi;
+}
+
 __device__ __forceinline__ void store_cv(uint32_t *dst, const uint32_t (&cv)[8]) {
     uint4 *d = reinterpret_cast<uint4 *>(dst);
     d[0] = make_uint4(cv[0], cv[1], cv[2], cv[3]);
@@ -336,6 +350,10 @@ struct UniformSegs {
         if (whole) store_digest(digests + 32ull * (first_msg + static_cast<uint32_t>(s)), cv);
         else store_cv(cv_out + 8ull * blockIdx.x, cv);
     }
+    __device__ void emit_pair(int s, uint32_t j, uint32_t lo, uint32_t hi) const {
+        if (whole) store_digest_pair(digests + 32ull * (first_msg + static_cast<uint32_t>(s)), j, lo, hi);
+        else store_cv_pair(cv_out + 8ull * blockIdx.x, j, lo, hi);
+    }
 };
 
 // Batch: segments of this workgroup staged in LDS, plus the lane -> segment map.
@@ -362,6 +380,10 @@ struct BatchSegs {
     __device__ void emit(int s, const uint32_t (&cv)[8]) const {
         if (final(s)) store_digest(digests + 32ull * seg[s].msg, cv);
         else store_cv(cv_out + 8ull * seg[s].dst, cv);
+    }
+    __device__ void emit_pair(int s, uint32_t j, uint32_t lo, uint32_t hi) const {
+        if (final(s)) store_digest_pair(digests + 32ull * seg[s].msg, j, lo, hi);
+        else store_cv_pair(cv_out + 8ull * seg[s].dst, j, lo, hi);
     }
 };
 
@@ -391,9 +413,44 @@ __device__ __forceinline__ void stage_segments(const uint32_t *wg_first_seg, con
     __syncthreads();
 }
 
+// compress_quad with this lane's message words read from LDS (src[moff[4r + t]] is its
+// t-th word of round r). The next round's 4 words are loaded while the current round
+// runs; the compiler barrier keeps later loads from being hoisted, so that only 8 words
+// are held at a time.
+__device__ __forceinline__ void compress_quad_lds(uint32_t &a, uint32_t &b, uint32_t &c, uint32_t &d,
+                                                  const uint32_t *src, const uint32_t (&moff)[28]) {
+    uint32_t cur[4], nxt[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) cur[t] = src[moff[t]];
+#pragma unroll
+    for (int r = 0; r < 7; ++r) {
+        if (r + 1 < 7) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) nxt[t] = src[moff[4 * (r + 1) + t]];
+        }
+        asm volatile("" ::: "memory");
+        quarter(a, b, c, d, cur[0], cur[1]);
+        b = quad_take<1>(b);
+        c = quad_take<2>(c);
+        d = quad_take<3>(d);
+        quarter(a, b, c, d, cur[2], cur[3]);
+        b = quad_take<3>(b);
+        c = quad_take<2>(c);
+        d = quad_take<1>(d);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cur[t] = nxt[t];
+    }
+}
+
+// Output nodes per level up to which a level runs on quads (four lanes per node): at
+// most 32 nodes would fill half a wave or less at one lane per node.
+constexpr uint32_t kQuadLevelNodes = 32;
+
 // The fused partial Merkle reduction. On entry lane x holds the level-0 node x in `cv`
-// (if it belongs to a segment). Each segment's result is emitted by the lane that
-// computes it, at the level where the segment reaches a single node.
+// (if it belongs to a segment). Each segment's result is emitted by the lane (or quad)
+// that computes it, at the level where the segment reaches a single node. Levels with
+// more than kQuadLevelNodes output positions run one lane per node; the sparse top of
+// the tree runs one quad per node, output node p on lanes 4p..4p+3.
 template <uint32_t C, class Segs>
 __device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs &sg, uint32_t levels,
                                             uint32_t (*buf)[8][C]) {
@@ -404,7 +461,10 @@ __device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs 
         for (int w = 0; w < 8; ++w) buf[0][w][lane] = cv[w];
         if (sg.count(s0) == 1) sg.emit(s0, cv);
     }
-    for (uint32_t l = 0; l < levels; ++l) {
+    // levels l with C >> (l + 1) > kQuadLevelNodes output positions
+    constexpr uint32_t kLaneLevels = C > kQuadLevelNodes ? 31 - __builtin_clz(C / kQuadLevelNodes) : 0;
+    uint32_t l = 0;
+    for (; l < levels && l < kLaneLevels; ++l) {
         __syncthreads();
         const uint32_t pos = lane << (l + 1);  // first leaf position under output node `lane`
         if (pos >= C) continue;
@@ -433,6 +493,51 @@ __device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs 
 #pragma unroll
         for (int w = 0; w < 8; ++w) buf[(l + 1) & 1][w][lane] = node[w];
         if (l + 1 == r) sg.emit(s, node);
+    }
+    if (l >= levels) return;
+
+    // Quad levels. Output node p is the parent of nodes 2p and 2p+1, whose 16 words are
+    // the message (left node's words 0..7, then the right node's); moff holds the word
+    // offsets, within a level buffer, of the 28 words this lane reads.
+    const uint32_t p = lane >> 2, j = lane & 3u;
+    uint32_t moff[28];
+#pragma unroll
+    for (int r = 0; r < 7; ++r)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t idx = (static_cast<uint32_t>(kQuadWord.at[r][t]) >> (4 * j)) & 15u;
+            moff[4 * r + t] = (idx & 7u) * C + 2 * p + (idx >> 3);
+        }
+    for (; l < levels; ++l) {
+        __syncthreads();
+        const uint32_t pos = p << (l + 1);
+        if (pos >= C) continue;
+        const int s = sg.seg_of(pos);
+        if (s < 0) continue;
+        const uint32_t start = sg.start(s), n = sg.count(s), r = ceil_log2(n);
+        if (l >= r) continue;  // segment already reduced to one node
+        // every condition above depends on p only: the quad's four lanes stay together
+        const uint32_t *src = &buf[l & 1][0][0];
+        uint32_t lo, hi;
+        if ((((2 * p + 1) << l) - start) < n) {  // a right child exists
+            uint32_t kw[8];
+            sg.key_words(s, kw);
+            uint32_t a = pick4(kw[0], kw[1], kw[2], kw[3], j);
+            uint32_t b = pick4(kw[4], kw[5], kw[6], kw[7], j);
+            uint32_t c = pick4(kIV[0], kIV[1], kIV[2], kIV[3], j);
+            const uint32_t flags = sg.mode() | kParent | (sg.final(s) && l + 1 == r ? kRoot : 0u);
+            uint32_t d = j == 3u ? flags : (j == 2u ? kBlockBytes : 0u);  // counter 0, length 64
+            compress_quad_lds(a, b, c, d, src, moff);
+            lo = a ^ c;
+            hi = b ^ d;
+        } else {  // carry node 2p up unchanged
+            lo = src[j * C + 2 * p];
+            hi = src[(4 + j) * C + 2 * p];
+        }
+        uint32_t *dst = &buf[(l + 1) & 1][0][0];
+        dst[j * C + p] = lo;
+        dst[(4 + j) * C + p] = hi;
+        if (l + 1 == r) sg.emit_pair(s, j, lo, hi);
     }
 }
 
