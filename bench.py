@@ -88,7 +88,8 @@ def main():
     # the GPU's clock settles only after ~100 ms of this load: warm up past that
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="gib4")
-    ap.add_argument("--cpu-sample-gib", type=float, default=2.0)
+    ap.add_argument("--cpu-sample-gib", type=float, default=None,
+                    help="time the CPU oracle on the first GIB GiB only (default: the whole input)")
     ap.add_argument("--no-check", action="store_true", help="skip the full-digest oracle check")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--calibrate-copy", type=float, default=None, metavar="GIB",
@@ -220,26 +221,36 @@ def main():
         import oracle
         cores = min(CPU_SHARE, os.cpu_count() or 1)
         host = data.contiguous().view(torch.uint8).reshape(-1).cpu().numpy()
+        want = None
         if not args.no_cpu:
-            sample = min(len(host), int(args.cpu_sample_gib * (1 << 30)))
+            # the oracle over the whole input (or the first --cpu-sample-gib GiB of it)
+            sample = len(host) if args.cpu_sample_gib is None else min(len(host), int(args.cpu_sample_gib * (1 << 30)))
             c0 = time.perf_counter()
             if batch:
                 per = BATCH_LEN
-                oracle.hash_batch(host[:sample], [i * per for i in range(sample // per)], [per] * (sample // per),
-                                  keys_cpu.numpy().tobytes()[:32 * (sample // per)], nthreads=cores)
+                got = oracle.hash_batch(host[:sample], [i * per for i in range(sample // per)],
+                                        [per] * (sample // per), keys_cpu.numpy().tobytes()[:32 * (sample // per)],
+                                        nthreads=cores)
+                sample = per * (sample // per)
             else:
-                oracle.hash_mt(host[:sample], key, cores)
+                got = oracle.hash_mt(host[:sample], key, cores)
             c_s = time.perf_counter() - c0
+            if sample == len(host):
+                want = got
+            what = "all" if sample == len(host) else f"the first {sample}"
             cpu = {"value": round(sample / 1e9 / c_s, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-                   "sample": f"first {sample} bytes of the same {args.workload} input, plain scalar C oracle "
-                             f"(multi-threaded aligned-subtree form), {c_s:.2f} s wall"}
+                   "sample": f"{what} bytes of the same {args.workload} input ({sample} B), plain scalar C oracle "
+                             f"(multi-threaded aligned-subtree form), {c_s:.2f} s wall, {cores} threads"}
             log(f"cpu oracle: {cpu['value']} GB/s on {cores} threads ({sample} bytes)")
         if not args.no_check:
             if batch:
-                want = oracle.hash_batch(host, offs, lengths, keys_cpu.numpy().tobytes(), nthreads=cores)
+                if want is None:
+                    want = oracle.hash_batch(host, offs, lengths, keys_cpu.numpy().tobytes(), nthreads=cores)
                 digest_match = [bytes(r) for r in out.cpu().numpy()] == want
             else:
-                digest_match = bytes(out.cpu().tolist()) == oracle.hash_mt(host, key, cores)
+                if want is None:
+                    want = oracle.hash_mt(host, key, cores)
+                digest_match = bytes(out.cpu().tolist()) == want
             log(f"digest matches the oracle: {digest_match}")
 
     cfg = {
