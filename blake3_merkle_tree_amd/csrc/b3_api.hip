@@ -100,19 +100,28 @@ uint32_t next_pow2_u32(uint64_t x) {
 constexpr uint64_t kMaxGrid = 0xFFFFFFFFull / kLeafLanes;
 
 // n_msgs messages of len bytes each, message m at base + m * stride (wrapping 64-bit
-// arithmetic), keyed by keys + 8*m (device) or all by `key` (host words). A message of
-// at most 256*K chunks is finished by the leaf pass, 256/R messages per workgroup. A
-// longer one spans G leaf workgroups, whose CVs the level passes reduce 256 to one
+// arithmetic), keyed by keys + 8*m (device) or all by `key` (host words). A leaf
+// workgroup covers `span` chunks (256*K, or 64 with the quad leaf for small inputs). A
+// message of at most `span` chunks is finished by the leaf pass, span/R messages per
+// workgroup. A longer one spans G leaf workgroups, whose CVs the level passes reduce 256 to one
 // workgroup until at most 256 remain, which one last pass finishes. Pass outputs
 // ping-pong between two CV arrays.
 int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_msgs, const uint32_t *keys,
                  const uint32_t key[8], uint32_t mode, uint8_t *out, hipStream_t s) {
     if (n_msgs == 0) return B3G_OK;
     const uint64_t c = chunks_of(len);
-    uint32_t k = choose_chunks_per_lane(c * n_msgs);
+    const uint64_t total = c > UINT64_MAX / n_msgs ? UINT64_MAX : c * n_msgs;  // chunks, saturated
+    // small inputs: a quad per chunk, kQuadLeafChunks chunk slots per workgroup
+    const bool quad = total <= quad_leaf_max_chunks();
+    uint32_t k = choose_chunks_per_lane(total);
     while (k > 1 && k > c) k >>= 1;  // a lane's run of chunks does not outgrow the message
-    const uint64_t span = static_cast<uint64_t>(kLeafLanes) * k;
+    if (quad) k = 1;
+    const uint64_t span = quad ? kQuadLeafChunks : static_cast<uint64_t>(kLeafLanes) * k;
+    const uint32_t wg_slots = quad ? kQuadLeafChunks : kLeafLanes;  // nodes per leaf workgroup
     const bool staged = use_lds_staging();
+    auto leaf = [&](const UniformLeafArgs &args, uint32_t grid) {
+        return quad ? launch_quad_leaf(args, grid, s) : launch_uniform_leaf(args, k, staged, grid, s);
+    };
 
     UniformLeafArgs la{};
     la.stride = stride;
@@ -126,7 +135,7 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
 
     if (c <= span) {  // case A: every message is finished by its leaf workgroup
         const uint32_t r = next_pow2_u32((c + k - 1) / k);
-        const uint64_t per_wg = kLeafLanes / r;
+        const uint64_t per_wg = wg_slots / r;
         for (uint64_t m0 = 0; m0 < n_msgs; m0 += kMaxGrid * per_wg) {
             const uint64_t nm = n_msgs - m0 < kMaxGrid * per_wg ? n_msgs - m0 : kMaxGrid * per_wg;
             la.base = base + m0 * stride;
@@ -135,7 +144,7 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
             la.groups = 1;
             la.keys = keys ? keys + 8 * m0 : nullptr;
             la.digests = out + 32 * m0;
-            const int rc = launched(launch_uniform_leaf(la, k, staged, static_cast<uint32_t>((nm + per_wg - 1) / per_wg), s));
+            const int rc = launched(leaf(la, static_cast<uint32_t>((nm + per_wg - 1) / per_wg)));
             if (rc != B3G_OK) return rc;
         }
         return B3G_OK;
@@ -163,7 +172,7 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
         la.keys = mkeys;
         la.cv_out = cv_a;
         la.digests = nullptr;
-        rc = launched(launch_uniform_leaf(la, k, staged, static_cast<uint32_t>(nm * g), s));
+        rc = launched(leaf(la, static_cast<uint32_t>(nm * g)));
         if (rc != B3G_OK) return rc;
 
         uint64_t m = g;

@@ -98,6 +98,11 @@ struct BatchLevelArgs {
 hipError_t launch_uniform_leaf(const UniformLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
                                hipStream_t s);
 hipError_t launch_uniform_level(const UniformLevelArgs &a, uint32_t grid, hipStream_t s);
+
+// Small inputs: one quad of lanes per chunk, kQuadLeafChunks chunks per workgroup, one
+// chunk per node (lanes_per_msg and groups count chunk slots of that workgroup).
+constexpr uint32_t kQuadLeafChunks = 64;
+hipError_t launch_quad_leaf(const UniformLeafArgs &a, uint32_t grid, hipStream_t s);
 hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
                              hipStream_t s);
 hipError_t launch_batch_level(const BatchLevelArgs &a, uint32_t grid, hipStream_t s);

@@ -330,6 +330,8 @@ struct UniformSegs {
     uint32_t *cv_out;
     uint8_t *digests;
 
+    // node positions in use: the tree's levels fit the quad layout by this bound
+    __device__ uint32_t used_positions() const { return segs << lanes_log2; }
     __device__ int seg_of(uint32_t pos) const {
         const uint32_t s = pos >> lanes_log2;
         return s < segs && pos - (s << lanes_log2) < nodes ? static_cast<int>(s) : -1;
@@ -364,6 +366,7 @@ struct BatchSegs {
     uint32_t *cv_out;
     uint8_t *digests;
 
+    __device__ uint32_t used_positions() const { return kLanes; }
     __device__ int seg_of(uint32_t pos) const { return seg_of_pos[pos]; }
     __device__ uint32_t start(int s) const { return seg_lane(seg[s].info); }
     __device__ uint32_t count(int s) const { return seg_count(seg[s].info); }
@@ -446,59 +449,23 @@ __device__ __forceinline__ void compress_quad_lds(uint32_t &a, uint32_t &b, uint
 // most 32 nodes would fill half a wave or less at one lane per node.
 constexpr uint32_t kQuadLevelNodes = 32;
 
-// The fused partial Merkle reduction. On entry lane x holds the level-0 node x in `cv`
-// (if it belongs to a segment). Each segment's result is emitted by the lane (or quad)
-// that computes it, at the level where the segment reaches a single node. Levels with
-// more than kQuadLevelNodes output positions run one lane per node; the sparse top of
-// the tree runs one quad per node, output node p on lanes 4p..4p+3.
-template <uint32_t C, class Segs>
-__device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs &sg, uint32_t levels,
-                                            uint32_t (*buf)[8][C]) {
-    const uint32_t lane = threadIdx.x;
-    const int s0 = sg.seg_of(lane);
-    if (s0 >= 0) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) buf[0][w][lane] = cv[w];
-        if (sg.count(s0) == 1) sg.emit(s0, cv);
-    }
-    // levels l with C >> (l + 1) > kQuadLevelNodes output positions
-    constexpr uint32_t kLaneLevels = C > kQuadLevelNodes ? 31 - __builtin_clz(C / kQuadLevelNodes) : 0;
+// Levels l of a tree over `used` node positions with more than kQuadLevelNodes output
+// positions (these run one lane per node).
+__device__ __forceinline__ uint32_t lane_levels(uint32_t used) {
     uint32_t l = 0;
-    for (; l < levels && l < kLaneLevels; ++l) {
-        __syncthreads();
-        const uint32_t pos = lane << (l + 1);  // first leaf position under output node `lane`
-        if (pos >= C) continue;
-        const int s = sg.seg_of(pos);
-        if (s < 0) continue;
-        const uint32_t start = sg.start(s), n = sg.count(s), r = ceil_log2(n);
-        if (l >= r) continue;  // segment already reduced to one node
-        const uint32_t(*src)[C] = buf[l & 1];
-        uint32_t node[8];
-        const bool has_right = (((2 * lane + 1) << l) - start) < n;
-        if (has_right) {
-            uint32_t m[16];
-#pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                const uint2 pr = *reinterpret_cast<const uint2 *>(&src[w][2 * lane]);
-                m[w] = pr.x;
-                m[w + 8] = pr.y;
-            }
-            sg.key_words(s, node);
-            const uint32_t flags = sg.mode() | kParent | (sg.final(s) && l + 1 == r ? kRoot : 0u);
-            compress(node, m, 0, 0, kBlockBytes, flags);
-        } else {
-#pragma unroll
-            for (int w = 0; w < 8; ++w) node[w] = src[w][2 * lane];
-        }
-#pragma unroll
-        for (int w = 0; w < 8; ++w) buf[(l + 1) & 1][w][lane] = node[w];
-        if (l + 1 == r) sg.emit(s, node);
-    }
-    if (l >= levels) return;
+    while (((used - 1) >> (l + 1)) + 1 > kQuadLevelNodes) ++l;
+    return l;
+}
 
-    // Quad levels. Output node p is the parent of nodes 2p and 2p+1, whose 16 words are
-    // the message (left node's words 0..7, then the right node's); moff holds the word
-    // offsets, within a level buffer, of the 28 words this lane reads.
+// Levels l .. levels-1 of the tree on quads, the level-l nodes being in buf[l & 1]
+// (word w of node x at buf[.][w][x]). Output node p is the parent of nodes 2p and 2p+1,
+// whose 16 words are the message (left node's words 0..7, then the right node's), and
+// runs on lanes 4p..4p+3; moff holds the word offsets, within a level buffer, of the 28
+// words this lane reads. The workgroup needs 2C lanes for the first of these levels.
+template <uint32_t C, class Segs>
+__device__ __forceinline__ void tree_levels_quad(const Segs &sg, uint32_t l, uint32_t levels,
+                                                 uint32_t (*buf)[8][C]) {
+    const uint32_t lane = threadIdx.x;
     const uint32_t p = lane >> 2, j = lane & 3u;
     uint32_t moff[28];
 #pragma unroll
@@ -539,6 +506,56 @@ __device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs 
         dst[(4 + j) * C + p] = hi;
         if (l + 1 == r) sg.emit_pair(s, j, lo, hi);
     }
+}
+
+// The fused partial Merkle reduction. On entry lane x holds the level-0 node x in `cv`
+// (if it belongs to a segment). Each segment's result is emitted by the lane (or quad)
+// that computes it, at the level where the segment reaches a single node. Levels with
+// more than kQuadLevelNodes output positions run one lane per node; the sparse top of
+// the tree runs one quad per node, output node p on lanes 4p..4p+3.
+template <uint32_t C, class Segs>
+__device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs &sg, uint32_t levels,
+                                            uint32_t (*buf)[8][C]) {
+    const uint32_t lane = threadIdx.x;
+    const int s0 = sg.seg_of(lane);
+    if (s0 >= 0) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) buf[0][w][lane] = cv[w];
+        if (sg.count(s0) == 1) sg.emit(s0, cv);
+    }
+    const uint32_t lane_lv = lane_levels(sg.used_positions());
+    uint32_t l = 0;
+    for (; l < levels && l < lane_lv; ++l) {
+        __syncthreads();
+        const uint32_t pos = lane << (l + 1);  // first leaf position under output node `lane`
+        if (pos >= C) continue;
+        const int s = sg.seg_of(pos);
+        if (s < 0) continue;
+        const uint32_t start = sg.start(s), n = sg.count(s), r = ceil_log2(n);
+        if (l >= r) continue;  // segment already reduced to one node
+        const uint32_t(*src)[C] = buf[l & 1];
+        uint32_t node[8];
+        const bool has_right = (((2 * lane + 1) << l) - start) < n;
+        if (has_right) {
+            uint32_t m[16];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const uint2 pr = *reinterpret_cast<const uint2 *>(&src[w][2 * lane]);
+                m[w] = pr.x;
+                m[w + 8] = pr.y;
+            }
+            sg.key_words(s, node);
+            const uint32_t flags = sg.mode() | kParent | (sg.final(s) && l + 1 == r ? kRoot : 0u);
+            compress(node, m, 0, 0, kBlockBytes, flags);
+        } else {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) node[w] = src[w][2 * lane];
+        }
+#pragma unroll
+        for (int w = 0; w < 8; ++w) buf[(l + 1) & 1][w][lane] = node[w];
+        if (l + 1 == r) sg.emit(s, node);
+    }
+    if (l < levels) tree_levels_quad<C>(sg, l, levels, buf);
 }
 
 // ---- kernels ---------------------------------------------------------------------------
@@ -668,6 +685,99 @@ __global__ __launch_bounds__(kLevelLanes) void level_uniform_kernel(UniformLevel
     tree_reduce<kLevelLanes>(cv, sg, ceil_log2(sg.nodes), buf);
 }
 
+// ---- small inputs: one quad per chunk -------------------------------------------------
+// With a few thousand chunks the lane-per-chunk leaf cannot fill the chip, and its time
+// is the latency of 16 sequential compressions on one lane plus the tree. Here a quad
+// hashes each chunk (compress_quad, a third of the latency): a workgroup of 256 lanes
+// takes kQuadLeafChunks = 64 chunks, stages them whole in LDS (16-byte loads, zero past
+// the end of a short chunk), runs their blocks, and reduces the chunk CVs on quads.
+
+// Bytes [off, off + 16) of a chunk holding len valid bytes; bytes at or past len read as
+// zero and are not loaded.
+__device__ __forceinline__ uint4 load_piece_bounded(const uint8_t *chunk, uint32_t off, uint32_t len) {
+    if (off + 16 <= len) return *reinterpret_cast<const uint4 *>(chunk + off);
+    return make_uint4(load_word_bounded(chunk, off, len), load_word_bounded(chunk, off + 4, len),
+                      load_word_bounded(chunk, off + 8, len), load_word_bounded(chunk, off + 12, len));
+}
+
+__global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a) {
+    // the staged chunks (64 KiB); afterwards the tree's level buffers
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kQuadLeafChunks * kChunkBytes / 4];
+    const uint32_t lane = threadIdx.x, q = lane >> 2, j = lane & 3u;
+    UniformSegs sg{};
+    uint64_t first_chunk = 0;
+    if (a.lanes_per_msg != 0) {  // case A: whole messages, R chunk slots each
+        uniform_case_a(sg, a.lanes_per_msg, a.n_msgs, kQuadLeafChunks);
+        sg.nodes = static_cast<uint32_t>(a.n_chunks);
+        sg.whole = a.may_root != 0;
+    } else {  // case B: 64 chunks (or the rest) of one message
+        sg.lanes_log2 = 6;
+        sg.first_msg = blockIdx.x / a.groups;
+        sg.segs = 1;
+        first_chunk = static_cast<uint64_t>(blockIdx.x - sg.first_msg * a.groups) * kQuadLeafChunks;
+        const uint64_t left = a.n_chunks - first_chunk;
+        sg.nodes = left >= kQuadLeafChunks ? kQuadLeafChunks : static_cast<uint32_t>(left);
+        sg.whole = a.may_root != 0 && a.groups == 1;
+    }
+    uniform_common(sg, a);
+
+    // chunk slot q of the workgroup: chunk x of segment s
+    const uint32_t s = q >> sg.lanes_log2, x = q - (s << sg.lanes_log2);
+    const bool active = s < sg.segs && x < sg.nodes;  // the same for the quad's 4 lanes
+    uint32_t *mine = lds + q * (kChunkBytes / 4);
+    uint32_t lo = 0, hi = 0;  // this lane's CV words j and 4 + j
+    uint32_t clen = 0;
+    if (active) {
+        const uint64_t ci = first_chunk + x;
+        const uint8_t *chunk = a.base + static_cast<uint64_t>(sg.first_msg + s) * a.stride + ci * kChunkBytes;
+        const uint64_t rem = a.len - ci * kChunkBytes;
+        clen = a.len == 0 ? 0u : (rem < kChunkBytes ? static_cast<uint32_t>(rem) : kChunkBytes);
+        // lane j stages the 16-byte pieces j, j + 4, ... of the quad's chunk
+#pragma unroll
+        for (uint32_t i = 0; i < 16; ++i) {
+            const uint32_t off = 64 * i + 16 * j;
+            reinterpret_cast<uint4 *>(mine)[4 * i + j] = load_piece_bounded(chunk, off, clen);
+        }
+    }
+    // the quad reads what its own lanes wrote (same wave, LDS in order): keep the
+    // compiler from moving the reads above the writes
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    if (active) {
+        uint32_t moff[28];  // block word offsets of this lane's 28 message words
+#pragma unroll
+        for (int r = 0; r < 7; ++r)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) moff[4 * r + t] = (static_cast<uint32_t>(kQuadWord.at[r][t]) >> (4 * j)) & 15u;
+        uint32_t kw[8];
+        sg.key_words(static_cast<int>(s), kw);
+        lo = pick4(kw[0], kw[1], kw[2], kw[3], j);
+        hi = pick4(kw[4], kw[5], kw[6], kw[7], j);
+        const uint64_t ctr = a.chunk_base + first_chunk + x;
+        const uint32_t nb = clen == 0 ? 1u : (clen + kBlockBytes - 1) / kBlockBytes;
+        const uint32_t end_flags = kChunkEnd | (sg.whole && sg.nodes == 1 ? kRoot : 0u);
+        const uint32_t iv_j = pick4(kIV[0], kIV[1], kIV[2], kIV[3], j);
+        for (uint32_t b = 0; b < nb; ++b) {
+            const uint32_t last = b + 1 == nb;
+            const uint32_t flags = sg.mode() | (b == 0 ? kChunkStart : 0u) | (last ? end_flags : 0u);
+            const uint32_t blen = last ? clen - kBlockBytes * b : kBlockBytes;
+            uint32_t va = lo, vb = hi, vc = iv_j;
+            uint32_t vd = pick4(static_cast<uint32_t>(ctr), static_cast<uint32_t>(ctr >> 32), blen, flags, j);
+            compress_quad_lds(va, vb, vc, vd, mine + 16 * b, moff);
+            lo = va ^ vc;
+            hi = vb ^ vd;
+        }
+    }
+    __syncthreads();  // every quad is done with its staged chunk: the tree reuses the LDS
+    auto buf = reinterpret_cast<uint32_t(*)[8][kQuadLeafChunks]>(lds);
+    if (active) {
+        buf[0][j][q] = lo;
+        buf[0][4 + j][q] = hi;
+        if (sg.nodes == 1) sg.emit_pair(static_cast<int>(s), j, lo, hi);
+    }
+    tree_levels_quad<kQuadLeafChunks>(sg, 0, ceil_log2(sg.nodes), buf);
+}
+
 template <uint32_t K, bool Staged>
 __global__ __launch_bounds__(kLeafLanes) void leaf_batch_kernel(BatchLeafArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t lds[leaf_lds_words<K, Staged>()];
@@ -752,6 +862,11 @@ hipError_t launch_uniform_leaf(const UniformLeafArgs &a, uint32_t chunks_per_lan
         case 9: hipLaunchKernelGGL((leaf_uniform_kernel<4, true>), g, b, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quad_leaf(const UniformLeafArgs &a, uint32_t grid, hipStream_t s) {
+    hipLaunchKernelGGL(leaf_quad_kernel, dim3(grid), dim3(kLeafLanes), 0, s, a);
     return hipGetLastError();
 }
 

@@ -101,6 +101,11 @@ uint32_t choose_chunks_per_lane(uint64_t total_chunks) {
     return 1;
 }
 
+uint64_t quad_leaf_max_chunks() {
+    if (const char *e = getenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS")) return strtoull(e, nullptr, 10);
+    return kQuadLeafMaxChunksDefault;
+}
+
 bool uniform_batch_disabled() {
     const char *e = getenv("BLAKE3_GPU_BATCH_TABLE");
     return e != nullptr && e[0] == '1' && e[1] == 0;

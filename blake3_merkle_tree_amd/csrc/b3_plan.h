@@ -58,6 +58,13 @@ uint32_t choose_chunks_per_lane(uint64_t total_chunks);
 // coalesced direct-to-LDS loads when BLAKE3_GPU_STAGING=lds is set in the environment.
 bool use_lds_staging();
 
+// Inputs (single messages and uniform batches) of at most this many chunks in total take
+// the quad leaf (four lanes per chunk): below it the lane-per-chunk leaf is bound by the
+// latency of one lane's 16 sequential compressions, not by the chip's VALU rate.
+// BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS in the environment overrides it (0 turns it off).
+constexpr uint64_t kQuadLeafMaxChunksDefault = 16384;
+uint64_t quad_leaf_max_chunks();
+
 // Batches of equal lengths at evenly spaced offsets skip the planner (their geometry is
 // implied); BLAKE3_GPU_BATCH_TABLE=1 in the environment routes them through the task
 // table like any other batch (for tests).

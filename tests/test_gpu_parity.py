@@ -47,7 +47,15 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def test_brute_force_lengths_single_call(b3, dev):
+# BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS: inputs up to this many chunks take the quad leaf
+# (four lanes per chunk); "0" sends every input to the lane-per-chunk leaf
+QUAD_OFF, QUAD_ALL = "0", str(1 << 62)
+
+
+@pytest.mark.parametrize("quad", ["default", QUAD_OFF])
+def test_brute_force_lengths_single_call(b3, dev, monkeypatch, quad):
+    if quad != "default":
+        monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", quad)
     from blake3_merkle_tree_amd import workloads
     buf = workloads.random_bytes(400 * 1024, 21, dev)
     host = _host(buf)
@@ -69,10 +77,14 @@ def test_brute_force_lengths_single_call(b3, dev):
         assert not bad, f"{len(bad)} lengths differ, first {bad[:5]}"
 
 
-def test_level_boundaries(b3, dev):
-    # 256-chunk leaf workgroups and 256-CV level workgroups: counts around 256 and 256^2
+@pytest.mark.parametrize("quad", ["default", QUAD_ALL])
+def test_level_boundaries(b3, dev, monkeypatch, quad):
+    # 256-chunk leaf workgroups and 256-CV level workgroups: counts around 256 and 256^2;
+    # with the quad leaf, 64-chunk workgroups: counts around 64, 64*256 and 64*256^2
+    if quad != "default":
+        monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", quad)
     from blake3_merkle_tree_amd import workloads
-    chunks = [255, 256, 257, 511, 512, 513, 65535, 65536, 65537, 131073]
+    chunks = [63, 64, 65, 255, 256, 257, 511, 512, 513, 16383, 16384, 16385, 65535, 65536, 65537, 131073]
     buf = workloads.random_bytes(131073 * 1024, 23, dev)
     host = _host(buf)
     key = bytes(workloads.key_bytes(24)[0].tolist())
@@ -239,6 +251,7 @@ def test_chunks_per_lane_paths(b3, dev, monkeypatch, k, staging):
     # per-lane loads: sizes cover both, partial waves, partial workgroups and tails
     monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", str(k))
     monkeypatch.setenv("BLAKE3_GPU_STAGING", staging)
+    monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", QUAD_OFF)
     from blake3_merkle_tree_amd import workloads
     KiB = 1024
     lengths = [0, 1, 1024, 1025, 4 * KiB, 4 * KiB + 1, 255 * KiB, 256 * KiB, 256 * KiB + 1, 1024 * KiB - 7,
@@ -277,15 +290,21 @@ UNIFORM_CASES = [
     (50, 5000, 0),  # every message is the same bytes; the keys differ
     (9, 1024 * 1024 + 1000, 1024 * 1024 + 1024),
     (3, 4 * 1024 * 1024, 4 * 1024 * 1024),
+    (40, 64 * 1024 + 1, 65 * 1024),  # 65 chunks: just past one quad-leaf workgroup
     (2, 65537 * 1024 + 3, 65537 * 1024 + 16),  # at one chunk per lane: two level passes
 ]
 
 
 @pytest.mark.parametrize("staging", ["direct", "lds"])
-@pytest.mark.parametrize("k", [None, 1, 4])
+@pytest.mark.parametrize("k", [None, 1, 4, "quad"])
 def test_uniform_batches(b3, dev, monkeypatch, k, staging):
-    if k is not None:
+    # k: chunks per lane of the lane-per-chunk leaf (None: the default choice, which
+    # sends small batches to the quad leaf), or "quad": the quad leaf for every batch
+    if k == "quad":
+        monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", QUAD_ALL)
+    elif k is not None:
         monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", str(k))
+        monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", QUAD_OFF)
     monkeypatch.setenv("BLAKE3_GPU_STAGING", staging)
     from blake3_merkle_tree_amd import workloads
     for ci, (count, L, stride) in enumerate(UNIFORM_CASES):
