@@ -43,6 +43,7 @@ def _load():
     lib.b3o_left_subtree_chunks.restype = ctypes.c_uint64
     lib.b3o_hash_recursive.argtypes = [_u8p, ctypes.c_uint64, _u8p, _u8p]
     lib.b3o_subtree_cv.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_uint64, _u8p, _u32p]
+    lib.b3o_hash_xof.argtypes = [_u8p, ctypes.c_uint64, _u8p, _u8p, ctypes.c_uint64]
     lib.b3o_hasher_new.argtypes = [_u8p]
     lib.b3o_hasher_new.restype = ctypes.c_void_p
     lib.b3o_hasher_free.argtypes = [ctypes.c_void_p]
@@ -135,6 +136,16 @@ def subtree_cv(data, chunk_base=0, key=None):
     out = (ctypes.c_uint32 * 8)()
     _load().b3o_subtree_cv(ptr, arr.size, chunk_base, kp, out)
     return list(out)
+
+
+def hash_xof(data, key=None, out_len=32):
+    """Extended output: out_len bytes of the root node's output stream (blocks of 64
+    bytes, counter 0, 1, ...); the first 32 bytes are the hash."""
+    arr, ptr = _as_u8(data)
+    _k, kp = _key(key)
+    out = (ctypes.c_uint8 * max(int(out_len), 1))()
+    _load().b3o_hash_xof(ptr, arr.size, kp, out, int(out_len))
+    return bytes(out)[:int(out_len)]
 
 
 def hash(data, key=None):  # noqa: A001 - mirrors the spec's name

@@ -242,6 +242,46 @@ void b3o_subtree_cv(const uint8_t *data, uint64_t len, uint64_t chunk_base, cons
     subtree_cv(kw, mode, data, len, chunk_base, 0, num_chunks(len), 0, out);
 }
 
+/* ---- Extended output (XOF) ---------------------------------------------------------
+ * The root node is the tree's final compression: for a one-chunk input, the chunk's
+ * last block, with the CV chained through the earlier blocks; otherwise the parent of
+ * the two top subtrees (left: the largest power of two of chunks below n). Output block
+ * t (64 bytes) is that compression run again with counter t and ROOT, all sixteen output
+ * words (specification, "Extendable output"); its first 32 bytes for t = 0 are the hash.
+ * The page leaves extendable output out ("Future work"). key32 == NULL: default mode. */
+void b3o_hash_xof(const uint8_t *data, uint64_t len, const uint8_t *key32, uint8_t *out, uint64_t out_len) {
+    uint32_t kw[8], mode, cv[8], m[16], o[16], blen, flags;
+    mode_setup(key32, kw, &mode);
+    uint64_t n = num_chunks(len);
+    if (n == 1) {
+        size_t nblocks = len == 0 ? 1 : (size_t)((len + B3O_BLOCK_LEN - 1) / B3O_BLOCK_LEN);
+        memcpy(cv, kw, sizeof(cv));
+        for (size_t b = 0; b + 1 < nblocks; b++) {
+            words_from_block(data + b * B3O_BLOCK_LEN, B3O_BLOCK_LEN, m);
+            b3o_compress(cv, m, 0, B3O_BLOCK_LEN, mode | (b == 0 ? B3O_CHUNK_START : 0), o);
+            memcpy(cv, o, sizeof(cv));
+        }
+        size_t off = (nblocks - 1) * B3O_BLOCK_LEN;
+        blen = (uint32_t)(len - off);
+        words_from_block(data + off, blen, m);
+        flags = mode | B3O_CHUNK_END | (nblocks == 1 ? B3O_CHUNK_START : 0);
+    } else {
+        uint64_t k = b3o_left_subtree_chunks(n);
+        subtree_cv(kw, mode, data, len, 0, 0, k, 0, m);
+        subtree_cv(kw, mode, data, len, 0, k, n - k, 0, m + 8);
+        memcpy(cv, kw, sizeof(cv));
+        blen = B3O_BLOCK_LEN;
+        flags = mode | B3O_PARENT;
+    }
+    for (uint64_t t = 0; t * B3O_BLOCK_LEN < out_len; t++) {
+        uint8_t block[B3O_BLOCK_LEN];
+        b3o_compress(cv, m, t, blen, flags | B3O_ROOT, o);
+        for (int i = 0; i < 16; i++) store_le32(block + 4 * i, o[i]);
+        uint64_t take = out_len - t * B3O_BLOCK_LEN < B3O_BLOCK_LEN ? out_len - t * B3O_BLOCK_LEN : B3O_BLOCK_LEN;
+        memcpy(out + t * B3O_BLOCK_LEN, block, (size_t)take);
+    }
+}
+
 /* ---- Incremental (stack-merge) form --------------------------------------------- */
 
 typedef struct {
