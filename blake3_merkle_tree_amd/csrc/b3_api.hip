@@ -107,7 +107,8 @@ constexpr uint64_t kMaxGrid = 0xFFFFFFFFull / kLeafLanes;
 // workgroup until at most 256 remain, which one last pass finishes. Pass outputs
 // ping-pong between two CV arrays.
 int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_msgs, const uint32_t *keys,
-                 const uint32_t key[8], uint32_t mode, uint8_t *out, hipStream_t s) {
+                 const uint32_t key[8], uint32_t mode, uint64_t chunk_base, uint32_t root_flag, uint8_t *out,
+                 hipStream_t s) {
     if (n_msgs == 0) return B3G_OK;
     const uint64_t c = chunks_of(len);
     const uint64_t total = c > UINT64_MAX / n_msgs ? UINT64_MAX : c * n_msgs;  // chunks, saturated
@@ -127,8 +128,9 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
     la.stride = stride;
     la.len = len;
     la.n_chunks = c;
-    la.chunk_base = 0;
+    la.chunk_base = chunk_base;
     la.may_root = 1;
+    la.root_flag = root_flag;
     la.keys = keys;
     memcpy(la.key, key, sizeof(la.key));
     la.mode = mode;
@@ -186,6 +188,7 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
             lv.keys = mkeys;
             memcpy(lv.key, key, sizeof(lv.key));
             lv.mode = mode;
+            lv.root_flag = root_flag;
             if (m <= kLevelLanes) {  // last pass: 256/R messages per workgroup, digests out
                 const uint32_t r = next_pow2_u32(m);
                 const uint64_t per_wg = kLevelLanes / r;
@@ -214,8 +217,80 @@ int hash_single(const void *in, uint64_t len, const uint32_t key[8], uint32_t mo
     if (out == nullptr || (in == nullptr && len > 0)) return B3G_EINVAL;
     if (reinterpret_cast<uintptr_t>(in) % 16 != 0) return B3G_EALIGN;
     if (len > kMaxMessageBytes) return B3G_ETOOBIG;
-    return hash_uniform(static_cast<const uint8_t *>(in), 0, len, 1, nullptr, key, mode, static_cast<uint8_t *>(out),
+    return hash_uniform(static_cast<const uint8_t *>(in), 0, len, 1, nullptr, key, mode, 0, kRoot,
+                        static_cast<uint8_t *>(out), static_cast<hipStream_t>(stream));
+}
+
+// The CV (no ROOT) of the subtree over all chunks of in[0 .. len), chunk counters from
+// chunk_base: the whole-message path with the top flag left out.
+int subtree_cv(const void *in, uint64_t len, uint64_t chunk_base, const uint32_t *key, void *out, void *stream) {
+    if (out == nullptr || (in == nullptr && len > 0)) return B3G_EINVAL;
+    if (reinterpret_cast<uintptr_t>(in) % 16 != 0) return B3G_EALIGN;
+    if (len > kMaxMessageBytes) return B3G_ETOOBIG;
+    if (chunk_base + chunks_of(len) < chunk_base) return B3G_EINVAL;
+    return hash_uniform(static_cast<const uint8_t *>(in), 0, len, 1, nullptr, key ? key : kIV,
+                        key ? kKeyedHash : 0u, chunk_base, 0u, static_cast<uint8_t *>(out),
                         static_cast<hipStream_t>(stream));
+}
+
+// Extended output. The root node's inputs are gathered first: for one chunk, a small
+// kernel chains the chunk's blocks up to the last one and copies the last block; for
+// more, the two top subtrees (left: the largest power of two of chunks below n) are
+// hashed without ROOT into one 64-byte block. Then every output block t is the root
+// compression with counter t, one lane each.
+int hash_xof(const void *in, uint64_t len, const uint32_t *key, void *out, uint64_t out_len, void *stream) {
+    if ((out == nullptr && out_len > 0) || (in == nullptr && len > 0)) return B3G_EINVAL;
+    if (reinterpret_cast<uintptr_t>(in) % 16 != 0) return B3G_EALIGN;
+    if (len > kMaxMessageBytes || out_len > kMaxXofBytes) return B3G_ETOOBIG;
+    if (out_len == 0) return B3G_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint32_t *kw = key ? key : kIV;
+    const uint32_t mode = key ? kKeyedHash : 0u;
+
+    StreamScratch scratch(s);
+    int rc = scratch.alloc(256);
+    if (rc != B3G_OK) return rc;
+    auto *rec_m = reinterpret_cast<uint32_t *>(scratch.get());       // 16 message words
+    auto *rec_cv = reinterpret_cast<uint32_t *>(scratch.get() + 64);  // 8 CV words (one chunk)
+
+    XofArgs x{};
+    memcpy(x.key, kw, sizeof(x.key));
+    x.m = rec_m;
+    x.out = static_cast<uint8_t *>(out);
+    x.out_len = out_len;
+    const uint64_t n = chunks_of(len);
+    if (n == 1) {
+        const uint64_t nb = len == 0 ? 1 : (len + kBlockBytes - 1) / kBlockBytes;
+        ChunkRootArgs c{static_cast<const uint8_t *>(in), static_cast<uint32_t>(len), {}, mode, rec_cv, rec_m};
+        memcpy(c.key, kw, sizeof(c.key));
+        rc = launched(launch_xof_chunk_root(c, s));
+        if (rc != B3G_OK) return rc;
+        x.cv = rec_cv;
+        x.block_len = static_cast<uint32_t>(len - kBlockBytes * (nb - 1));
+        x.flags = mode | kChunkEnd | (nb == 1 ? kChunkStart : 0u) | kRoot;
+    } else {
+        uint64_t k = 1;
+        while (k * 2 < n) k *= 2;
+        const uint8_t *bytes = static_cast<const uint8_t *>(in);
+        rc = hash_uniform(bytes, 0, k * kChunkBytes, 1, nullptr, kw, mode, 0, 0u,
+                          reinterpret_cast<uint8_t *>(rec_m), s);
+        if (rc != B3G_OK) return rc;
+        rc = hash_uniform(bytes + k * kChunkBytes, 0, len - k * kChunkBytes, 1, nullptr, kw, mode, k, 0u,
+                          reinterpret_cast<uint8_t *>(rec_m + 8), s);
+        if (rc != B3G_OK) return rc;
+        x.cv = nullptr;  // the key words
+        x.block_len = kBlockBytes;
+        x.flags = mode | kParent | kRoot;
+    }
+    const uint64_t blocks = (out_len + kBlockBytes - 1) / kBlockBytes;
+    constexpr uint64_t kPerLaunch = kMaxGrid * kXofLanes;
+    for (uint64_t b0 = 0; b0 < blocks; b0 += kPerLaunch) {
+        x.first_block = b0;
+        x.n_blocks = blocks - b0 < kPerLaunch ? blocks - b0 : kPerLaunch;
+        rc = launched(launch_xof_expand(x, static_cast<uint32_t>((x.n_blocks + kXofLanes - 1) / kXofLanes), s));
+        if (rc != B3G_OK) return rc;
+    }
+    return B3G_OK;
 }
 
 // Leaf pass only: the CV of every aligned group of group_chunks (= kLeafLanes * K)
@@ -274,7 +349,7 @@ int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *length
         uniform = lengths[i] == lengths[0] && offsets[i] - offsets[i - 1] == stride;
     if (uniform)
         return hash_uniform(static_cast<const uint8_t *>(base) + offsets[0], stride, lengths[0], n, keys,
-                            kIV, keys ? kKeyedHash : 0u, static_cast<uint8_t *>(out), s);
+                            kIV, keys ? kKeyedHash : 0u, 0, kRoot, static_cast<uint8_t *>(out), s);
 
     uint64_t total_chunks = 0;
     for (uint64_t i = 0; i < n; ++i) total_chunks += chunks_of(lengths[i]);
@@ -366,6 +441,16 @@ int blake3_gpu_keyed_hash_batch(const void *dev_base, const uint64_t *host_offse
                                 const uint64_t *host_lengths, const uint32_t *dev_keys, void *dev_out,
                                 uint64_t n, void *stream) {
     return b3g::hash_batch(dev_base, host_offsets, host_lengths, dev_keys, dev_out, n, stream);
+}
+
+int blake3_gpu_subtree_cv(const void *dev_in, uint64_t len, uint64_t chunk_base, const uint32_t key[8],
+                          void *dev_out32, void *stream) {
+    return b3g::subtree_cv(dev_in, len, chunk_base, key, dev_out32, stream);
+}
+
+int blake3_gpu_hash_xof(const void *dev_in, uint64_t len, const uint32_t key[8], void *dev_out, uint64_t out_len,
+                        void *stream) {
+    return b3g::hash_xof(dev_in, len, key, dev_out, out_len, stream);
 }
 
 int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, const uint32_t key[8],

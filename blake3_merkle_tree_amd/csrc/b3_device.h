@@ -108,6 +108,27 @@ __device__ __forceinline__ void compress(uint32_t (&cv)[8], const uint32_t (&m)[
     for (int i = 0; i < 8; ++i) cv[i] = v[i] ^ v[i + 8];
 }
 
+// All sixteen output words of the compression (extended output): words 0..7 as in
+// compress, words 8..15 = v[i+8] ^ cv[i].
+__device__ __forceinline__ void compress_xof(const uint32_t (&cv)[8], const uint32_t (&m)[16], uint32_t counter_lo,
+                                             uint32_t counter_hi, uint32_t block_len, uint32_t flags,
+                                             uint32_t (&out)[16]) {
+    uint32_t v[16] = {cv[0],  cv[1],  cv[2],  cv[3],      cv[4],      cv[5],     cv[6],     cv[7],
+                      kIV[0], kIV[1], kIV[2], kIV[3], counter_lo, counter_hi, block_len, flags};
+    round_r<0>(v, m);
+    round_r<1>(v, m);
+    round_r<2>(v, m);
+    round_r<3>(v, m);
+    round_r<4>(v, m);
+    round_r<5>(v, m);
+    round_r<6>(v, m);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        out[i] = v[i] ^ v[i + 8];
+        out[i + 8] = v[i + 8] ^ cv[i];
+    }
+}
+
 // ---- one compression on four lanes ---------------------------------------------------
 // Lane j (0..3) of a quad (four consecutive lanes, all active) holds column j of the
 // state: a = v[j], b = v[4+j], c = v[8+j], d = v[12+j]. In a round each lane runs the

@@ -42,7 +42,8 @@ struct UniformLeafArgs {
     uint32_t n_msgs;
     uint32_t lanes_per_msg;  // R in case A, 0 in case B
     uint32_t groups;         // workgroups per message in case B
-    uint32_t may_root;       // 1: a workgroup holding a whole message emits its digest
+    uint32_t may_root;       // 1: a workgroup holding a whole message finishes it (writes `digests`)
+    uint32_t root_flag;      // flag of a finished message's top compression: ROOT, or 0 (subtree CV)
     const uint32_t *keys;    // 8 key words per message, or nullptr: every message uses `key`
     uint32_t key[8];         // key words (or the IV) when keys == nullptr
     uint32_t mode;           // kKeyedHash or 0
@@ -62,6 +63,7 @@ struct UniformLevelArgs {
     const uint32_t *keys;
     uint32_t key[8];
     uint32_t mode;
+    uint32_t root_flag;      // flag of the finishing pass's top compressions: ROOT, or 0 (subtree CVs)
     uint32_t *cv_out;
     uint8_t *digests;
 };
@@ -103,6 +105,34 @@ hipError_t launch_uniform_level(const UniformLevelArgs &a, uint32_t grid, hipStr
 // chunk per node (lanes_per_msg and groups count chunk slots of that workgroup).
 constexpr uint32_t kQuadLeafChunks = 64;
 hipError_t launch_quad_leaf(const UniformLeafArgs &a, uint32_t grid, hipStream_t s);
+// Extended output: output block t (64 bytes at out + 64*(t - first_block)) is the root
+// compression (cv, m, block_len, flags with ROOT) run with counter t; all 16 output words.
+constexpr uint32_t kXofLanes = 256;
+struct XofArgs {
+    const uint32_t *cv;   // device CV words of the root compression, or nullptr: `key`
+    uint32_t key[8];
+    const uint32_t *m;    // device: the root compression's 16 message words
+    uint32_t block_len;
+    uint32_t flags;       // includes ROOT
+    uint64_t first_block; // counter of the first block of this launch
+    uint64_t n_blocks;    // blocks of this launch
+    uint8_t *out;         // stream byte 64*first_block goes to out[64*first_block]
+    uint64_t out_len;     // total bytes wanted
+};
+hipError_t launch_xof_expand(const XofArgs &a, uint32_t grid, hipStream_t s);
+
+// Root compression inputs of a one-chunk message (len <= 1024): the CV after all blocks
+// but the last (cv_out, 8 words) and the last block, zero-padded (m_out, 16 words).
+struct ChunkRootArgs {
+    const uint8_t *in;
+    uint32_t len;
+    uint32_t key[8];
+    uint32_t mode;
+    uint32_t *cv_out;
+    uint32_t *m_out;
+};
+hipError_t launch_xof_chunk_root(const ChunkRootArgs &a, hipStream_t s);
+
 hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
                              hipStream_t s);
 hipError_t launch_batch_level(const BatchLevelArgs &a, uint32_t grid, hipStream_t s);

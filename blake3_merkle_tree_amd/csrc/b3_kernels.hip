@@ -323,12 +323,15 @@ struct UniformSegs {
     uint32_t nodes;
     uint32_t segs;
     uint32_t first_msg;  // message of segment 0
-    bool whole;          // segments are whole messages: their top compression carries ROOT
+    bool whole;          // segments are whole messages: their result goes to `digests`
+    uint32_t top_flag;   // flag of a whole message's top compression: ROOT, or 0 for a subtree CV
     const uint32_t *keys;
     uint32_t key[8];
     uint32_t mode_flag;
     uint32_t *cv_out;
     uint8_t *digests;
+
+    __device__ uint32_t root_bit() const { return top_flag; }
 
     // node positions in use: the tree's levels fit the quad layout by this bound
     __device__ uint32_t used_positions() const { return segs << lanes_log2; }
@@ -367,6 +370,7 @@ struct BatchSegs {
     uint8_t *digests;
 
     __device__ uint32_t used_positions() const { return kLanes; }
+    __device__ uint32_t root_bit() const { return kRoot; }
     __device__ int seg_of(uint32_t pos) const { return seg_of_pos[pos]; }
     __device__ uint32_t start(int s) const { return seg_lane(seg[s].info); }
     __device__ uint32_t count(int s) const { return seg_count(seg[s].info); }
@@ -492,7 +496,7 @@ __device__ __forceinline__ void tree_levels_quad(const Segs &sg, uint32_t l, uin
             uint32_t a = pick4(kw[0], kw[1], kw[2], kw[3], j);
             uint32_t b = pick4(kw[4], kw[5], kw[6], kw[7], j);
             uint32_t c = pick4(kIV[0], kIV[1], kIV[2], kIV[3], j);
-            const uint32_t flags = sg.mode() | kParent | (sg.final(s) && l + 1 == r ? kRoot : 0u);
+            const uint32_t flags = sg.mode() | kParent | (sg.final(s) && l + 1 == r ? sg.root_bit() : 0u);
             uint32_t d = j == 3u ? flags : (j == 2u ? kBlockBytes : 0u);  // counter 0, length 64
             compress_quad_lds(a, b, c, d, src, moff);
             lo = a ^ c;
@@ -545,7 +549,7 @@ __device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs 
                 m[w + 8] = pr.y;
             }
             sg.key_words(s, node);
-            const uint32_t flags = sg.mode() | kParent | (sg.final(s) && l + 1 == r ? kRoot : 0u);
+            const uint32_t flags = sg.mode() | kParent | (sg.final(s) && l + 1 == r ? sg.root_bit() : 0u);
             compress(node, m, 0, 0, kBlockBytes, flags);
         } else {
 #pragma unroll
@@ -573,6 +577,7 @@ constexpr uint32_t leaf_lds_words() {
 // Sets the fields of a UniformSegs that do not depend on the pass.
 template <typename Args>
 __device__ __forceinline__ void uniform_common(UniformSegs &sg, const Args &a) {
+    sg.top_flag = a.root_flag;
     sg.keys = a.keys;
 #pragma unroll
     for (int w = 0; w < 8; ++w) sg.key[w] = a.key[w];
@@ -626,7 +631,7 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_uniform_kernel(UniformLeafArg
         ptr = a.base + static_cast<uint64_t>(sg.first_msg + s) * a.stride + c0 * kChunkBytes;
     }
     // a message of one node: the lane's own subtree is the whole tree
-    const uint32_t root_flag = sg.whole && sg.nodes == 1 ? kRoot : 0u;
+    const uint32_t root_flag = sg.whole && sg.nodes == 1 ? sg.top_flag : 0u;
     uint32_t cv[8];
 #pragma unroll
     for (int w = 0; w < 8; ++w) cv[w] = key[w];
@@ -755,7 +760,7 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a
         hi = pick4(kw[4], kw[5], kw[6], kw[7], j);
         const uint64_t ctr = a.chunk_base + first_chunk + x;
         const uint32_t nb = clen == 0 ? 1u : (clen + kBlockBytes - 1) / kBlockBytes;
-        const uint32_t end_flags = kChunkEnd | (sg.whole && sg.nodes == 1 ? kRoot : 0u);
+        const uint32_t end_flags = kChunkEnd | (sg.whole && sg.nodes == 1 ? sg.top_flag : 0u);
         const uint32_t iv_j = pick4(kIV[0], kIV[1], kIV[2], kIV[3], j);
         for (uint32_t b = 0; b < nb; ++b) {
             const uint32_t last = b + 1 == nb;
@@ -848,7 +853,69 @@ __global__ __launch_bounds__(kLevelLanes) void level_batch_kernel(BatchLevelArgs
     tree_reduce<kLevelLanes>(cv, sg, a.wg_levels[blockIdx.x], buf);
 }
 
+// ---- extended output ------------------------------------------------------------------
+
+// Root node of a one-chunk message: chain its blocks up to the last (one lane; at most
+// 15 compressions) and copy the last block zero-padded.
+__global__ __launch_bounds__(64) void xof_chunk_root_kernel(ChunkRootArgs a) {
+    if (threadIdx.x != 0) return;
+    const uint32_t nb = a.len == 0 ? 1u : (a.len + kBlockBytes - 1) / kBlockBytes;
+    uint32_t cv[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) cv[w] = a.key[w];
+    for (uint32_t b = 0; b + 1 < nb; ++b) {
+        uint32_t m[16];
+#pragma unroll
+        for (int w = 0; w < 16; ++w) m[w] = load_word_bounded(a.in, b * kBlockBytes + 4 * w, a.len);
+        compress(cv, m, 0, 0, kBlockBytes, a.mode | (b == 0 ? kChunkStart : 0u));
+    }
+    const uint32_t off = (nb - 1) * kBlockBytes;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) a.m_out[w] = load_word_bounded(a.in, off + 4 * w, a.len);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) a.cv_out[w] = cv[w];
+}
+
+// One 64-byte output block per lane; the last block of the request is cut to out_len.
+__global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * kXofLanes + threadIdx.x;
+    if (i >= a.n_blocks) return;
+    const uint64_t t = a.first_block + i;
+    uint32_t cv[8], m[16], o[16];
+    if (a.cv) {
+        load_cv(cv, a.cv);
+    } else {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) cv[w] = a.key[w];
+    }
+#pragma unroll
+    for (int w = 0; w < 16; ++w) m[w] = a.m[w];
+    compress_xof(cv, m, static_cast<uint32_t>(t), static_cast<uint32_t>(t >> 32), a.block_len, a.flags, o);
+    uint8_t *dst = a.out + kBlockBytes * t;
+    const uint64_t left = a.out_len - kBlockBytes * t;
+    if (left >= kBlockBytes && reinterpret_cast<uintptr_t>(dst) % 16 == 0) {
+        uint4 *d = reinterpret_cast<uint4 *>(dst);
+        d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        d[2] = make_uint4(o[8], o[9], o[10], o[11]);
+        d[3] = make_uint4(o[12], o[13], o[14], o[15]);
+    } else {
+        const uint32_t n = left < kBlockBytes ? static_cast<uint32_t>(left) : kBlockBytes;
+        for (uint32_t k = 0; k < n; ++k) dst[k] = static_cast<uint8_t>(o[k / 4] >> (8 * (k % 4)));
+    }
+}
+
 }  // namespace
+
+hipError_t launch_xof_expand(const XofArgs &a, uint32_t grid, hipStream_t s) {
+    hipLaunchKernelGGL(xof_expand_kernel, dim3(grid), dim3(kXofLanes), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_xof_chunk_root(const ChunkRootArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(xof_chunk_root_kernel, dim3(1), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_uniform_leaf(const UniformLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
                                hipStream_t s) {

@@ -29,6 +29,8 @@ inline constexpr uint32_t seg_info(uint32_t lane, uint32_t count, bool final) {
 
 // Largest message accepted (bytes): chunk indices of a message fit in 32 bits.
 constexpr uint64_t kMaxMessageBytes = 1ull << 42;
+// Longest extended output accepted (bytes).
+constexpr uint64_t kMaxXofBytes = 1ull << 42;
 
 struct PassPlan {
     uint32_t lanes = 0;                  // lanes (nodes) per workgroup in this pass

@@ -98,6 +98,40 @@ int blake3_gpu_keyed_hash_batch(const void *dev_base, const uint64_t *host_offse
                                 uint64_t n, void *stream);
 
 /*
+ * Chaining value of a subtree: the BLAKE3 tree over all chunks of dev_in[0 .. len) with
+ * chunk counters starting at chunk_base, reduced to one 8-word CV with no ROOT flag
+ * (page "BLAKE3 on GPU: 400x faster hashing", sections "BLAKE3" and "Merkle tree
+ * reduction": every node of the tree is such a CV). When dev_in is the part of a larger
+ * input that starts at chunk chunk_base and chunk_base is a multiple of the subtree's
+ * size rounded up to a power of two, the result is that node of the larger input's
+ * tree: shares of one input hashed on several devices combine through parent
+ * compressions, and the two top subtrees are the root's message block.
+ *   dev_in      device pointer, 16-byte aligned (may be NULL only if len == 0; len == 0 is
+ *               the CV of one empty chunk).
+ *   chunk_base  counter of the first chunk.
+ *   key         host pointer to 8 key words (keyed mode), or NULL (default mode).
+ *   dev_out32   device pointer to 32 writable bytes: the 8 CV words, little-endian.
+ * Errors: EINVAL (NULL dev_out32, NULL dev_in with len > 0, chunk counter overflow),
+ * EALIGN, ETOOBIG, ENOMEM, EHIP.
+ */
+int blake3_gpu_subtree_cv(const void *dev_in, uint64_t len, uint64_t chunk_base, const uint32_t key[8],
+                          void *dev_out32, void *stream);
+
+/*
+ * Extendable output of dev_in[0 .. len): out_len bytes of the output stream of the
+ * tree's root node, written to dev_out. Stream block t (64 bytes) is the root
+ * compression run with counter t and ROOT, all sixteen output words (BLAKE3
+ * specification, extendable output; the page lists it as future work, "Future work").
+ * The first 32 bytes are the 32-byte hash; a longer request extends a shorter one.
+ *   key         host pointer to 8 key words (keyed mode), or NULL (default mode).
+ *   dev_out     device pointer to out_len writable bytes (any alignment).
+ *   out_len     0 .. 2^42 bytes (0 enqueues nothing).
+ * Other arguments and errors as blake3_gpu_hash (ETOOBIG also for out_len > 2^42).
+ */
+int blake3_gpu_hash_xof(const void *dev_in, uint64_t len, const uint32_t key[8], void *dev_out, uint64_t out_len,
+                        void *stream);
+
+/*
  * The first tree level that one workgroup produces: the chaining value (CV) of every
  * aligned group of group_chunks consecutive 1 KiB chunks of dev_in[0 .. len) (the last
  * group may be shorter), with chunk counters starting at chunk_base and no ROOT flag

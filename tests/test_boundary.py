@@ -38,6 +38,8 @@ def _lib():
     lib.blake3_gpu_hash.argtypes = [vp, u64, vp, vp]
     lib.blake3_gpu_keyed_hash.argtypes = [vp, u64, vp, vp, vp]
     lib.blake3_gpu_keyed_hash_batch.argtypes = [vp, vp, vp, vp, vp, u64, vp]
+    lib.blake3_gpu_subtree_cv.argtypes = [vp, u64, u64, vp, vp, vp]
+    lib.blake3_gpu_hash_xof.argtypes = [vp, u64, vp, vp, u64, vp]
     return lib
 
 
@@ -56,6 +58,20 @@ def test_single_argument_checks():
     assert lib.blake3_gpu_keyed_hash(ALIGNED, 5, None, ALIGNED, None) == b3.EINVAL
     assert lib.blake3_gpu_keyed_hash(MISALIGNED, 5, ctypes.addressof(key), ALIGNED, None) == b3.EALIGN
     assert lib.blake3_gpu_keyed_hash(ALIGNED, 1 << 43, ctypes.addressof(key), ALIGNED, None) == b3.ETOOBIG
+
+
+def test_subtree_and_xof_argument_checks():
+    lib = _lib()
+    assert lib.blake3_gpu_subtree_cv(ALIGNED, 5, 0, None, None, None) == b3.EINVAL
+    assert lib.blake3_gpu_subtree_cv(None, 5, 0, None, ALIGNED, None) == b3.EINVAL
+    assert lib.blake3_gpu_subtree_cv(MISALIGNED, 5, 0, None, ALIGNED, None) == b3.EALIGN
+    assert lib.blake3_gpu_subtree_cv(ALIGNED, (1 << 42) + 1, 0, None, ALIGNED, None) == b3.ETOOBIG
+    assert lib.blake3_gpu_subtree_cv(ALIGNED, 2048, (1 << 64) - 1, None, ALIGNED, None) == b3.EINVAL
+    assert lib.blake3_gpu_hash_xof(ALIGNED, 5, None, None, 10, None) == b3.EINVAL
+    assert lib.blake3_gpu_hash_xof(None, 5, None, ALIGNED, 10, None) == b3.EINVAL
+    assert lib.blake3_gpu_hash_xof(MISALIGNED, 5, None, ALIGNED, 10, None) == b3.EALIGN
+    assert lib.blake3_gpu_hash_xof(ALIGNED, 5, None, ALIGNED, (1 << 42) + 1, None) == b3.ETOOBIG
+    assert lib.blake3_gpu_hash_xof(ALIGNED, 5, None, None, 0, None) == b3.OK  # nothing to write
 
 
 def test_batch_argument_checks():

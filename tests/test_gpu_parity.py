@@ -327,3 +327,46 @@ def test_uniform_batches(b3, dev, monkeypatch, k, staging):
         assert _digests_to_bytes(b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))) == \
             oracle.hash_batch(host, offs.tolist(), lengths.tolist(), keys.numpy().tobytes(), nthreads=NTHREADS)
         monkeypatch.delenv("BLAKE3_GPU_BATCH_TABLE")
+
+
+# ---- extendable output and subtree CVs ----------------------------------------------------
+
+XOF_LENGTHS = [0, 1, 63, 64, 65, 1023, 1024, 1025, 2048, 2049, 5 * 1024 + 7, 64 * 1024, 300 * 1024 + 9,
+               16384 * 1024 + 1, 20000 * 1024 + 3]
+XOF_OUT = [0, 1, 31, 32, 33, 64, 65, 200, 4096 + 17]
+
+
+@pytest.mark.parametrize("keyed", [True, False])
+def test_xof_matches_oracle(b3, dev, keyed):
+    from blake3_merkle_tree_amd import workloads
+    buf = workloads.random_bytes(max(XOF_LENGTHS), 70, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(71)[0].tolist()) if keyed else None
+    for L in XOF_LENGTHS:
+        want = oracle.hash_xof(host[:L].tobytes(), key, max(XOF_OUT))
+        for n in XOF_OUT:
+            _say("xof", L, "bytes ->", n, "keyed", keyed)
+            got = bytes(b3.hash_xof(buf[:L], key, n).cpu().tolist())
+            assert got == want[:n], (L, n)
+    # a long output: many lanes, the last block cut short, a misaligned destination
+    L = 3000
+    want = oracle.hash_xof(host[:L].tobytes(), key, (1 << 20) + 5)
+    assert bytes(b3.hash_xof(buf[:L], key, (1 << 20) + 5).cpu().numpy().tobytes()) == want
+    dst = torch.zeros(1000 + 3, dtype=torch.uint8, device=dev)
+    b3.hash_xof(buf[:L], key, 1000, out=dst[3:])
+    assert bytes(dst[3:].cpu().numpy().tobytes()) == want[:1000]
+    assert dst[:3].sum().item() == 0
+
+
+@pytest.mark.parametrize("keyed", [True, False])
+def test_subtree_cv_matches_oracle(b3, dev, keyed):
+    from blake3_merkle_tree_amd import workloads
+    buf = workloads.random_bytes(70000 * 1024, 72, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(73)[0].tolist()) if keyed else None
+    cases = [(0, 0), (1, 0), (1024, 5), (1025, 2), (64 * 1024, 64), (300 * 1024 + 9, 512),
+             (16384 * 1024 + 1, 1 << 15), (70000 * 1024, 1 << 17), (5000, (1 << 40) + 8)]
+    for L, base in cases:
+        _say("subtree cv", L, "bytes, chunk base", base, "keyed", keyed)
+        got = b3.subtree_cv(buf[:L], key, chunk_base=base).cpu().numpy().view(np.uint32).tolist()
+        assert got == oracle.subtree_cv(host[:L].tobytes(), base, key), (L, base)
