@@ -1,6 +1,6 @@
 """Benchmark: keyed BLAKE3 of one device-resident buffer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload gib4|gib16|fp32_8192|mib1|batch64k]
+    python bench.py [--steps K] [--warmup W] [--workload gib4|gib16|fp32_8192|mib1|batch64k|xof_gib8]
 
 A step is one full hash (leaf pass + level passes, ROOT) of the workload's bytes, which
 are already in HBM when the timed region starts. Prints ONE JSON line on stdout:
@@ -81,6 +81,73 @@ def measured_traffic(workload):
         return None
 
 
+XOF_WORKLOAD = "xof_gib8"
+# An output block keeps all 16 words: the 8 xors of the fold plus 8 more for v[i+8] ^ cv[i].
+XOF_OPS_PER_BLOCK = 7 * 8 * 12 + 16
+XOF_OUT_BYTES = 8 << 30
+XOF_CHECK_BYTES = 64 << 20
+
+
+def bench_xof(args, torch, b3, workloads, dev, stream):
+    """Extendable output: 8 GiB of keyed XOF output from the 1 MiB input. The step is the
+    whole call (the input's two top subtrees, then the expansion kernel, one lane per
+    64-byte block); the expansion is the dominant kernel, and its roofline is taken over
+    the step's time (the input hash, ~30 us, is included in the time, not in the ops)."""
+    data, key_t = workloads.single("mib1", dev)
+    key = bytes(key_t.tolist())
+    out = torch.empty(XOF_OUT_BYTES, dtype=torch.uint8, device=dev)
+
+    def step():
+        b3.hash_xof(data, key, XOF_OUT_BYTES, out=out)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    value = XOF_OUT_BYTES / 1e9 / (ms / 1e3)
+    ops = (XOF_OUT_BYTES // 64) * XOF_OPS_PER_BLOCK
+    achieved = ops / (ms / 1e3) / 1e12
+    log(f"xof: {ms:.4f} ms/step ({value:.1f} GB/s of output), {achieved:.2f} Tops/s = "
+        f"{achieved / VALU_INT_PEAK_TOPS:.1%} of the int-VALU peak")
+    cpu = None
+    digest_match = None
+    if not args.no_check or not args.no_cpu:
+        import oracle
+        host = data.contiguous().view(torch.uint8).reshape(-1).cpu().numpy()
+        c0 = time.perf_counter()
+        want = oracle.hash_xof(host, key, XOF_CHECK_BYTES)
+        c_s = time.perf_counter() - c0
+        if not args.no_cpu:
+            cpu = {"value": round(XOF_CHECK_BYTES / 1e9 / c_s, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                   "sample": f"the first {XOF_CHECK_BYTES} bytes of the same output stream, plain scalar C "
+                             f"oracle on one thread, {c_s:.2f} s wall"}
+        if not args.no_check:
+            digest_match = bytes(out[:XOF_CHECK_BYTES].cpu().numpy().tobytes()) == want
+            log(f"first {XOF_CHECK_BYTES} output bytes match the oracle: {digest_match}")
+    rec = {
+        "metric": "GB/s of extended output, keyed BLAKE3 XOF",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u32", "data": "synthetic",
+        "config": {"workload": "8 GiB of keyed BLAKE3 extendable output of 1 MiB uniform random bytes "
+                               "(seed 0, key seed 1)", "input_bytes": data.numel(), "output_bytes": XOF_OUT_BYTES},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_INT_PEAK_TOPS, 3),
+                     "unit": "Tops/s (int32 VALU lane-ops)", "frac": round(achieved / VALU_INT_PEAK_TOPS, 4),
+                     "traffic": None, "kernel": "xof_expand_kernel (step time, input hash included)",
+                     "kernel_ms": round(ms, 4), "ops_per_launch": ops,
+                     "hbm_write_gbs": round(value, 1), "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": cpu,
+        "digest_match": digest_match,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +186,8 @@ def main():
         print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
                           "launches": args.steps}), flush=True)
         return
+    if args.workload == XOF_WORKLOAD:
+        return bench_xof(args, torch, b3, workloads, dev, stream)
     batch = args.workload == "batch64k"
     if batch:
         base, offs, lengths, keys_cpu = workloads.uniform_batch(BATCH_COUNT, BATCH_LEN, dev)

@@ -881,15 +881,19 @@ __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
     const uint64_t i = static_cast<uint64_t>(blockIdx.x) * kXofLanes + threadIdx.x;
     if (i >= a.n_blocks) return;
     const uint64_t t = a.first_block + i;
+    // the root's inputs are the same for every lane and nothing here writes them: scalar loads
+    const uint32_t *__restrict__ src_m = a.m;
     uint32_t cv[8], m[16], o[16];
     if (a.cv) {
-        load_cv(cv, a.cv);
+        const uint32_t *__restrict__ src_cv = a.cv;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) cv[w] = src_cv[w];
     } else {
 #pragma unroll
         for (int w = 0; w < 8; ++w) cv[w] = a.key[w];
     }
 #pragma unroll
-    for (int w = 0; w < 16; ++w) m[w] = a.m[w];
+    for (int w = 0; w < 16; ++w) m[w] = src_m[w];
     compress_xof(cv, m, static_cast<uint32_t>(t), static_cast<uint32_t>(t >> 32), a.block_len, a.flags, o);
     uint8_t *dst = a.out + kBlockBytes * t;
     const uint64_t left = a.out_len - kBlockBytes * t;
