@@ -119,7 +119,8 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
     if (quad) k = 1;
     const uint64_t span = quad ? kQuadLeafChunks : static_cast<uint64_t>(kLeafLanes) * k;
     const uint32_t wg_slots = quad ? kQuadLeafChunks : kLeafLanes;  // nodes per leaf workgroup
-    const bool staged = use_lds_staging();
+    const bool fused = fused_levels_enabled();
+    const bool staged = use_lds_staging() && !fused;  // the fused leaf loads directly
     auto leaf = [&](const UniformLeafArgs &args, uint32_t grid) {
         return quad ? launch_quad_leaf(args, grid, s) : launch_uniform_leaf(args, k, staged, grid, s);
     };
@@ -158,6 +159,54 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
     const uint64_t nb = n_msgs < per_launch ? n_msgs : per_launch;
     const uint64_t g1 = (g + kLevelLanes - 1) / kLevelLanes;
     StreamScratch scratch(s);
+
+    if (fused) {
+        // One launch: the leaf workgroups reduce the levels themselves (last arrival of
+        // each group of 256 takes it up a level). Scratch: the CVs of every level but the
+        // root, and one zeroed ticket per group above the leaf.
+        uint64_t lg[kMaxLevels + 1] = {g, 0, 0, 0, 0};
+        uint32_t levels = 0;
+        while (lg[levels] > 1) {
+            if (levels == kMaxLevels) return B3G_ETOOBIG;
+            lg[levels + 1] = (lg[levels] + kLevelLanes - 1) / kLevelLanes;
+            ++levels;
+        }
+        size_t cv_at[kMaxLevels], ctr_at[kMaxLevels], at = 0;
+        for (uint32_t L = 0; L < levels; ++L) {
+            cv_at[L] = at;
+            at += align256(nb * lg[L] * 32);
+        }
+        const size_t ctr_begin = at;
+        for (uint32_t L = 0; L < levels; ++L) {
+            ctr_at[L] = at;
+            at += align256(nb * lg[L + 1] * 4);
+        }
+        int rc = scratch.alloc(at);
+        if (rc != B3G_OK) return rc;
+        uint8_t *d = scratch.get();
+        la.levels = levels;
+        for (uint32_t L = 0; L < levels; ++L) {
+            la.lvl_cv[L] = reinterpret_cast<uint32_t *>(d + cv_at[L]);
+            la.lvl_ctr[L] = reinterpret_cast<uint32_t *>(d + ctr_at[L]);
+        }
+        for (uint32_t L = 0; L <= levels; ++L) la.lvl_g[L] = lg[L];
+        for (uint64_t m0 = 0; m0 < n_msgs; m0 += nb) {
+            const uint64_t nm = n_msgs - m0 < nb ? n_msgs - m0 : nb;
+            rc = launched(launch_zero_words(reinterpret_cast<uint32_t *>(d + ctr_begin), (at - ctr_begin) / 4, s));
+            if (rc != B3G_OK) return rc;
+            la.base = base + m0 * stride;
+            la.n_msgs = static_cast<uint32_t>(nm);
+            la.lanes_per_msg = 0;
+            la.groups = static_cast<uint32_t>(g);
+            la.keys = keys ? keys + 8 * m0 : nullptr;
+            la.cv_out = la.lvl_cv[0];
+            la.digests = out + 32 * m0;
+            rc = launched(leaf(la, static_cast<uint32_t>(nm * g)));
+            if (rc != B3G_OK) return rc;
+        }
+        return B3G_OK;
+    }
+
     const size_t a_bytes = align256(nb * g * 32);
     int rc = scratch.alloc(a_bytes + (g1 > 1 ? align256(nb * g1 * 32) : 0));
     if (rc != B3G_OK) return rc;

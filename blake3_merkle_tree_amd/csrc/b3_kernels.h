@@ -33,6 +33,12 @@ constexpr uint32_t kLevelLanes = 256;
 //     finishes them (digests).
 //   Case B (lanes_per_msg == 0): a message spans `groups` workgroups; workgroup w reduces
 //     group (w mod groups) of message (w / groups) to one CV at cv_out + 8*w.
+// Fused level passes (case B): after writing its group CV a workgroup takes a ticket on
+// its level-1 group (256 group CVs of one message); the last of a group to arrive reduces
+// it and takes a ticket one level up, until the message's root. At most kMaxLevels steps:
+// groups per message <= 2^32.
+constexpr uint32_t kMaxLevels = 4;
+
 struct UniformLeafArgs {
     const uint8_t *base;     // message 0 (16-byte aligned)
     uint64_t stride;         // bytes from one message to the next (multiple of 16)
@@ -49,6 +55,11 @@ struct UniformLeafArgs {
     uint32_t mode;           // kKeyedHash or 0
     uint32_t *cv_out;
     uint8_t *digests;        // message m's digest at digests + 32*m
+    // fused levels (case B only; levels == 0: the leaf's CVs are the result)
+    uint32_t levels;                     // level steps after the leaf
+    uint32_t *lvl_cv[kMaxLevels];        // [0] == cv_out; [L]: n_msgs * lvl_g[L] CVs, message-major
+    uint32_t *lvl_ctr[kMaxLevels];       // [L]: n_msgs * lvl_g[L + 1] tickets, zero on entry
+    uint64_t lvl_g[kMaxLevels + 1];      // nodes per message: [0] = groups, [L + 1] = ceil([L] / 256)
 };
 
 // Uniform level pass: every message has g_in CVs, contiguous in cv_in (message m's at
@@ -96,7 +107,8 @@ struct BatchLevelArgs {
 };
 
 // chunks_per_lane (K) is 1, 2 or 4: each leaf workgroup covers 256*K chunks. `staged`
-// selects the LDS-staged input path for full waves instead of per-lane loads.
+// selects the LDS-staged input path for full waves instead of per-lane loads. With
+// a.levels != 0 (fused level passes) only per-lane loads are built: staged is rejected.
 hipError_t launch_uniform_leaf(const UniformLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
                                hipStream_t s);
 hipError_t launch_uniform_level(const UniformLevelArgs &a, uint32_t grid, hipStream_t s);
@@ -105,6 +117,9 @@ hipError_t launch_uniform_level(const UniformLevelArgs &a, uint32_t grid, hipStr
 // chunk per node (lanes_per_msg and groups count chunk slots of that workgroup).
 constexpr uint32_t kQuadLeafChunks = 64;
 hipError_t launch_quad_leaf(const UniformLeafArgs &a, uint32_t grid, hipStream_t s);
+
+// Zeroes n words (the tickets of fused levels) with a kernel, in stream order.
+hipError_t launch_zero_words(uint32_t *p, uint64_t n, hipStream_t s);
 // Extended output: output block t (64 bytes at out + 64*(t - first_block)) is the root
 // compression (cv, m, block_len, flags with ROOT) run with counter t; all 16 output words.
 constexpr uint32_t kXofLanes = 256;

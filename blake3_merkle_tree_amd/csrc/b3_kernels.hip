@@ -300,6 +300,16 @@ __device__ __forceinline__ void store_cv_pair(uint32_t *dst, uint32_t j, uint32_
     dst[4 + j] = hi;
 }
 
+// Device-coherent forms for CVs another workgroup reads in the same launch (fused levels):
+// agent-scope atomic stores and loads go to the coherence point the eight XCDs share,
+// instead of an XCD's own L2.
+__device__ __forceinline__ void store_word_coherent(uint32_t *dst, uint32_t v) {
+    __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_word_coherent(const uint32_t *src) {
+    return __hip_atomic_load(const_cast<uint32_t *>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void store_cv(uint32_t *dst, const uint32_t (&cv)[8]) {
     uint4 *d = reinterpret_cast<uint4 *>(dst);
     d[0] = make_uint4(cv[0], cv[1], cv[2], cv[3]);
@@ -329,6 +339,8 @@ struct UniformSegs {
     uint32_t key[8];
     uint32_t mode_flag;
     uint32_t *cv_out;
+    uint64_t cv_slot;    // where a segment that is not a whole message writes its CV (cv_out + 8*cv_slot)
+    bool coherent;       // that CV is read by another workgroup of this launch: device-coherent stores
     uint8_t *digests;
 
     __device__ uint32_t root_bit() const { return top_flag; }
@@ -352,12 +364,24 @@ struct UniformSegs {
         }
     }
     __device__ void emit(int s, const uint32_t (&cv)[8]) const {
-        if (whole) store_digest(digests + 32ull * (first_msg + static_cast<uint32_t>(s)), cv);
-        else store_cv(cv_out + 8ull * blockIdx.x, cv);
+        if (whole) {
+            store_digest(digests + 32ull * (first_msg + static_cast<uint32_t>(s)), cv);
+        } else if (coherent) {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) store_word_coherent(cv_out + 8ull * cv_slot + w, cv[w]);
+        } else {
+            store_cv(cv_out + 8ull * cv_slot, cv);
+        }
     }
     __device__ void emit_pair(int s, uint32_t j, uint32_t lo, uint32_t hi) const {
-        if (whole) store_digest_pair(digests + 32ull * (first_msg + static_cast<uint32_t>(s)), j, lo, hi);
-        else store_cv_pair(cv_out + 8ull * blockIdx.x, j, lo, hi);
+        if (whole) {
+            store_digest_pair(digests + 32ull * (first_msg + static_cast<uint32_t>(s)), j, lo, hi);
+        } else if (coherent) {
+            store_word_coherent(cv_out + 8ull * cv_slot + j, lo);
+            store_word_coherent(cv_out + 8ull * cv_slot + 4 + j, hi);
+        } else {
+            store_cv_pair(cv_out + 8ull * cv_slot, j, lo, hi);
+        }
     }
 };
 
@@ -466,11 +490,15 @@ __device__ __forceinline__ uint32_t lane_levels(uint32_t used) {
 // whose 16 words are the message (left node's words 0..7, then the right node's), and
 // runs on lanes 4p..4p+3; moff holds the word offsets, within a level buffer, of the 28
 // words this lane reads. The workgroup needs 2C lanes for the first of these levels.
-template <uint32_t C, class Segs>
+// InLoop: the caller runs this inside a loop; the lane's offsets are then made opaque to
+// the optimiser so that they are computed here rather than hoisted out of that loop,
+// where they would hold 28 registers across the rest of the kernel.
+template <uint32_t C, class Segs, bool InLoop = false>
 __device__ __forceinline__ void tree_levels_quad(const Segs &sg, uint32_t l, uint32_t levels,
                                                  uint32_t (*buf)[8][C]) {
     const uint32_t lane = threadIdx.x;
-    const uint32_t p = lane >> 2, j = lane & 3u;
+    uint32_t p = lane >> 2, j = lane & 3u;
+    if (InLoop) asm volatile("" : "+v"(p), "+v"(j));
     uint32_t moff[28];
 #pragma unroll
     for (int r = 0; r < 7; ++r)
@@ -517,7 +545,7 @@ __device__ __forceinline__ void tree_levels_quad(const Segs &sg, uint32_t l, uin
 // that computes it, at the level where the segment reaches a single node. Levels with
 // more than kQuadLevelNodes output positions run one lane per node; the sparse top of
 // the tree runs one quad per node, output node p on lanes 4p..4p+3.
-template <uint32_t C, class Segs>
+template <uint32_t C, class Segs, bool InLoop = false>
 __device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs &sg, uint32_t levels,
                                             uint32_t (*buf)[8][C]) {
     const uint32_t lane = threadIdx.x;
@@ -559,7 +587,7 @@ __device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs 
         for (int w = 0; w < 8; ++w) buf[(l + 1) & 1][w][lane] = node[w];
         if (l + 1 == r) sg.emit(s, node);
     }
-    if (l < levels) tree_levels_quad<C>(sg, l, levels, buf);
+    if (l < levels) tree_levels_quad<C, Segs, InLoop>(sg, l, levels, buf);
 }
 
 // ---- kernels ---------------------------------------------------------------------------
@@ -583,7 +611,53 @@ __device__ __forceinline__ void uniform_common(UniformSegs &sg, const Args &a) {
     for (int w = 0; w < 8; ++w) sg.key[w] = a.key[w];
     sg.mode_flag = a.mode;
     sg.cv_out = a.cv_out;
+    sg.cv_slot = blockIdx.x;
+    sg.coherent = false;
     sg.digests = a.digests;
+}
+
+// Fused level passes (UniformLeafArgs::levels): called by the whole workgroup after its
+// leaf tree has written group CV blockIdx.x with device-coherent stores. Each wave waits
+// for its stores to complete, a barrier, then one agent-scope atomic ticket per
+// workgroup; the last arrival of a group reads the group's CVs with device-coherent loads
+// and reduces them with the tree of the level kernel. (An agent-scope release fence per
+// workgroup instead writes back the XCD's whole L2 each time: measured 43% slower at
+// 4 GiB.)
+__device__ void fused_levels(const UniformLeafArgs &a, uint32_t *lds) {
+    const uint32_t lane = threadIdx.x;
+    auto buf = reinterpret_cast<uint32_t(*)[8][kLevelLanes]>(lds);
+    const uint32_t msg = blockIdx.x / a.groups;
+    uint64_t idx = blockIdx.x - static_cast<uint64_t>(msg) * a.groups;  // this node at level L
+    for (uint32_t L = 0; L < a.levels; ++L) {
+        const uint64_t g_in = a.lvl_g[L], g_out = a.lvl_g[L + 1];
+        const uint64_t group = idx / kLevelLanes, first = group * kLevelLanes;
+        const uint32_t count = g_in - first < kLevelLanes ? static_cast<uint32_t>(g_in - first) : kLevelLanes;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's CV stores have completed
+        __syncthreads();  // ... in every wave; the tree is done with the LDS: word 0 carries the verdict
+        if (lane == 0) lds[0] = atomicAdd(a.lvl_ctr[L] + msg * g_out + group, 1u) + 1u == count ? 1u : 0u;
+        __syncthreads();
+        const bool last = lds[0] != 0;
+        __syncthreads();  // everyone has read it before the tree writes over it
+        if (!last) return;
+        uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (lane < count) {
+            const uint32_t *src = a.lvl_cv[L] + 8 * (msg * g_in + first + lane);
+#pragma unroll
+            for (int w = 0; w < 8; ++w) cv[w] = load_word_coherent(src + w);
+        }
+        UniformSegs sg{};
+        uniform_common(sg, a);
+        sg.lanes_log2 = 8;
+        sg.nodes = count;
+        sg.segs = 1;
+        sg.first_msg = msg;
+        sg.whole = g_out == 1;
+        sg.cv_out = L + 1 < a.levels ? a.lvl_cv[L + 1] : nullptr;
+        sg.cv_slot = msg * g_out + group;
+        sg.coherent = true;
+        tree_reduce<kLevelLanes, UniformSegs, true>(cv, sg, ceil_log2(count), buf);
+        idx = group;
+    }
 }
 
 // Case A groups: `per_wg` messages per workgroup, R = 1 << lanes_log2 lanes each.
@@ -595,7 +669,9 @@ __device__ __forceinline__ void uniform_case_a(UniformSegs &sg, uint32_t lanes_p
     sg.segs = n_msgs - sg.first_msg < per_wg ? n_msgs - sg.first_msg : per_wg;
 }
 
-template <uint32_t K, bool Staged>
+// Fused: the level passes run in this launch (fused_levels); a separate instantiation, so
+// that the registers the level tree needs do not weigh on the default leaf.
+template <uint32_t K, bool Staged, bool Fused>
 __global__ __launch_bounds__(kLeafLanes) void leaf_uniform_kernel(UniformLeafArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t lds[leaf_lds_words<K, Staged>()];
     const uint32_t lane = threadIdx.x;
@@ -616,6 +692,7 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_uniform_kernel(UniformLeafArg
         sg.whole = a.may_root != 0 && a.groups == 1;
     }
     uniform_common(sg, a);
+    sg.coherent = Fused;  // group CVs are read by the fused levels
 
     const uint32_t s = lane >> sg.lanes_log2, x = lane - (s << sg.lanes_log2);
     uint32_t nl = 0, last_len = kChunkBytes;
@@ -662,6 +739,7 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_uniform_kernel(UniformLeafArg
     }
     __syncthreads();  // every wave is done with its stage buffer or slots before the tree reuses them
     tree_reduce<kLanes>(cv, sg, ceil_log2(sg.nodes), reinterpret_cast<uint32_t(*)[8][kLanes]>(lds));
+    if (Fused) fused_levels(a, lds);
 }
 
 __global__ __launch_bounds__(kLevelLanes) void level_uniform_kernel(UniformLevelArgs a) {
@@ -705,6 +783,7 @@ __device__ __forceinline__ uint4 load_piece_bounded(const uint8_t *chunk, uint32
                       load_word_bounded(chunk, off + 8, len), load_word_bounded(chunk, off + 12, len));
 }
 
+template <bool Fused>
 __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a) {
     // the staged chunks (64 KiB); afterwards the tree's level buffers
     __shared__ __attribute__((aligned(16))) uint32_t lds[kQuadLeafChunks * kChunkBytes / 4];
@@ -725,6 +804,7 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a
         sg.whole = a.may_root != 0 && a.groups == 1;
     }
     uniform_common(sg, a);
+    sg.coherent = Fused;  // group CVs are read by the fused levels
 
     // chunk slot q of the workgroup: chunk x of segment s
     const uint32_t s = q >> sg.lanes_log2, x = q - (s << sg.lanes_log2);
@@ -781,6 +861,7 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a
         if (sg.nodes == 1) sg.emit_pair(static_cast<int>(s), j, lo, hi);
     }
     tree_levels_quad<kQuadLeafChunks>(sg, 0, ceil_log2(sg.nodes), buf);
+    if (Fused) fused_levels(a, lds);
 }
 
 template <uint32_t K, bool Staged>
@@ -911,6 +992,20 @@ __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
 
 }  // namespace
 
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *p, uint64_t n) {
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<uint64_t>(gridDim.x) * 256)
+        p[i] = 0;
+}
+
+hipError_t launch_zero_words(uint32_t *p, uint64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const uint64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(blocks < 1024 ? static_cast<uint32_t>(blocks) : 1024u), dim3(256), 0,
+                       s, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_xof_expand(const XofArgs &a, uint32_t grid, hipStream_t s) {
     hipLaunchKernelGGL(xof_expand_kernel, dim3(grid), dim3(kXofLanes), 0, s, a);
     return hipGetLastError();
@@ -924,20 +1019,32 @@ hipError_t launch_xof_chunk_root(const ChunkRootArgs &a, hipStream_t s) {
 hipError_t launch_uniform_leaf(const UniformLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
                                hipStream_t s) {
     const dim3 g(grid), b(kLeafLanes);
+    if (a.levels != 0) {  // fused level passes: direct loads only
+        switch (staged ? 0 : chunks_per_lane) {
+            case 1: hipLaunchKernelGGL((leaf_uniform_kernel<1, false, true>), g, b, 0, s, a); break;
+            case 2: hipLaunchKernelGGL((leaf_uniform_kernel<2, false, true>), g, b, 0, s, a); break;
+            case 4: hipLaunchKernelGGL((leaf_uniform_kernel<4, false, true>), g, b, 0, s, a); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (chunks_per_lane * 2 + (staged ? 1 : 0)) {
-        case 2: hipLaunchKernelGGL((leaf_uniform_kernel<1, false>), g, b, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((leaf_uniform_kernel<1, true>), g, b, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((leaf_uniform_kernel<2, false>), g, b, 0, s, a); break;
-        case 5: hipLaunchKernelGGL((leaf_uniform_kernel<2, true>), g, b, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((leaf_uniform_kernel<4, false>), g, b, 0, s, a); break;
-        case 9: hipLaunchKernelGGL((leaf_uniform_kernel<4, true>), g, b, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((leaf_uniform_kernel<1, false, false>), g, b, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((leaf_uniform_kernel<1, true, false>), g, b, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((leaf_uniform_kernel<2, false, false>), g, b, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((leaf_uniform_kernel<2, true, false>), g, b, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((leaf_uniform_kernel<4, false, false>), g, b, 0, s, a); break;
+        case 9: hipLaunchKernelGGL((leaf_uniform_kernel<4, true, false>), g, b, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_quad_leaf(const UniformLeafArgs &a, uint32_t grid, hipStream_t s) {
-    hipLaunchKernelGGL(leaf_quad_kernel, dim3(grid), dim3(kLeafLanes), 0, s, a);
+    if (a.levels != 0)
+        hipLaunchKernelGGL(leaf_quad_kernel<true>, dim3(grid), dim3(kLeafLanes), 0, s, a);
+    else
+        hipLaunchKernelGGL(leaf_quad_kernel<false>, dim3(grid), dim3(kLeafLanes), 0, s, a);
     return hipGetLastError();
 }
 

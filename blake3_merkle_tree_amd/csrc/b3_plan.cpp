@@ -106,6 +106,14 @@ uint64_t quad_leaf_max_chunks() {
     return kQuadLeafMaxChunksDefault;
 }
 
+bool fused_levels_enabled() {
+    // Off by default: measured on MI355X, the ticket zeroing launch and each workgroup's
+    // wait for its coherent stores and ticket cost more than the level launches they
+    // replace (4 GiB: 1.369 vs 1.351 ms; 1 MiB: 37.0 vs 31.6 us; 256 MiB: 122 vs 113 us).
+    const char *e = getenv("BLAKE3_GPU_FUSED_LEVELS");
+    return e != nullptr && e[0] == '1' && e[1] == 0;
+}
+
 bool uniform_batch_disabled() {
     const char *e = getenv("BLAKE3_GPU_BATCH_TABLE");
     return e != nullptr && e[0] == '1' && e[1] == 0;

@@ -67,6 +67,11 @@ bool use_lds_staging();
 constexpr uint64_t kQuadLeafMaxChunksDefault = 16384;
 uint64_t quad_leaf_max_chunks();
 
+// Whether a message spanning several leaf workgroups has its level passes fused into the
+// leaf launch (last-arrival tickets) rather than run as separate level launches (the
+// default). BLAKE3_GPU_FUSED_LEVELS=1 in the environment selects the fused form.
+bool fused_levels_enabled();
+
 // Batches of equal lengths at evenly spaced offsets skip the planner (their geometry is
 // implied); BLAKE3_GPU_BATCH_TABLE=1 in the environment routes them through the task
 // table like any other batch (for tests).

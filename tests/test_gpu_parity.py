@@ -77,12 +77,15 @@ def test_brute_force_lengths_single_call(b3, dev, monkeypatch, quad):
         assert not bad, f"{len(bad)} lengths differ, first {bad[:5]}"
 
 
-@pytest.mark.parametrize("quad", ["default", QUAD_ALL])
-def test_level_boundaries(b3, dev, monkeypatch, quad):
+@pytest.mark.parametrize("quad,fused", [("default", "1"), (QUAD_ALL, "1"), ("default", "0"), (QUAD_ALL, "0")])
+def test_level_boundaries(b3, dev, monkeypatch, quad, fused):
     # 256-chunk leaf workgroups and 256-CV level workgroups: counts around 256 and 256^2;
-    # with the quad leaf, 64-chunk workgroups: counts around 64, 64*256 and 64*256^2
+    # with the quad leaf, 64-chunk workgroups: counts around 64, 64*256 and 64*256^2.
+    # fused: level passes run inside the leaf launch (last-arrival tickets), or as
+    # separate level launches
     if quad != "default":
         monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", quad)
+    monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", fused)
     from blake3_merkle_tree_amd import workloads
     chunks = [63, 64, 65, 255, 256, 257, 511, 512, 513, 16383, 16384, 16385, 65535, 65536, 65537, 131073]
     buf = workloads.random_bytes(131073 * 1024, 23, dev)
@@ -188,8 +191,18 @@ def test_workload_fp32_8192(b3, dev):
     _single_workload(b3, dev, "fp32_8192", repeats=2)
 
 
-def test_workload_gib4(b3, dev):
+def test_workload_gib4(b3, dev, monkeypatch):
     _single_workload(b3, dev, "gib4", repeats=3)
+    # the same digest with the level passes fused into the leaf launch, also through the
+    # quad leaf (4,194,305 chunks in 65,537 workgroups: three fused levels)
+    from blake3_merkle_tree_amd import workloads
+    t, key = workloads.single("gib4", dev)
+    key = bytes(key.tolist())
+    want = bytes(b3.keyed_hash(t, key).cpu().tolist())
+    monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", "1")
+    assert bytes(b3.keyed_hash(t, key).cpu().tolist()) == want
+    monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", QUAD_ALL)
+    assert bytes(b3.keyed_hash(t, key).cpu().tolist()) == want
 
 
 def test_workload_gib16(b3, dev):
@@ -300,11 +313,15 @@ UNIFORM_CASES = [
 def test_uniform_batches(b3, dev, monkeypatch, k, staging):
     # k: chunks per lane of the lane-per-chunk leaf (None: the default choice, which
     # sends small batches to the quad leaf), or "quad": the quad leaf for every batch
+    # (K = 1 also fuses the level passes into the leaf launch; the others run them as
+    # separate launches, the default)
     if k == "quad":
         monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", QUAD_ALL)
     elif k is not None:
         monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", str(k))
         monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", QUAD_OFF)
+        if k == 1:
+            monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", "1")
     monkeypatch.setenv("BLAKE3_GPU_STAGING", staging)
     from blake3_merkle_tree_amd import workloads
     for ci, (count, L, stride) in enumerate(UNIFORM_CASES):
