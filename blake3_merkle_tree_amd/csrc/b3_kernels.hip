@@ -620,9 +620,15 @@ __device__ __forceinline__ void uniform_common(UniformSegs &sg, const Args &a) {
 // leaf tree has written group CV blockIdx.x with device-coherent stores. Each wave waits
 // for its stores to complete, a barrier, then one agent-scope atomic ticket per
 // workgroup; the last arrival of a group reads the group's CVs with device-coherent loads
-// and reduces them with the tree of the level kernel. (An agent-scope release fence per
-// workgroup instead writes back the XCD's whole L2 each time: measured 43% slower at
-// 4 GiB.)
+// and reduces them with the tree of the level kernel.
+// Ordering: the CV words are only ever accessed as agent-scope atomics, which on gfx950
+// write through to, and read from, the point of coherence shared by all XCDs. A writer's
+// ticket is issued only after vmcnt(0) has seen its CV stores acknowledged there, and the
+// last arrival issues its CV loads only after its ticket has returned (the verdict reaches
+// the other waves through LDS and a barrier), so those loads find every CV of the group.
+// This relies on the hardware's in-order completion rather than on release/acquire
+// ordering: an agent-scope release fence per workgroup would also write back the XCD's
+// whole L2, and measured 43% slower at 4 GiB.
 __device__ void fused_levels(const UniformLeafArgs &a, uint32_t *lds) {
     const uint32_t lane = threadIdx.x;
     auto buf = reinterpret_cast<uint32_t(*)[8][kLevelLanes]>(lds);
