@@ -1,6 +1,7 @@
 """Benchmark: keyed BLAKE3 of one device-resident buffer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload gib4|gib16|fp32_8192|mib1|batch64k|xof_gib8]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload gib4|gib16|fp32_8192|mib1|batch64k|ragged256|xof_gib8]
 
 A step is one full hash (leaf pass + level passes, ROOT) of the workload's bytes, which
 are already in HBM when the timed region starts. Prints ONE JSON line on stdout:
@@ -32,6 +33,10 @@ HBM_PEAK_GBS = 8000.0
 # VALU lane-ops per compression on gfx950: 7 rounds x 8 quarter-rounds x 12 (2 v_add3_u32,
 # 2 v_add_u32, 4 v_xor_b32, 4 v_alignbit_b32) + 8 v_xor_b32 for the output fold.
 OPS_PER_COMPRESSION = 7 * 8 * 12 + 8
+# The BLAKE3 page's own count, 7 rounds x 8 quarter-rounds x 6 ops = 336 per 64-byte block,
+# i.e. 5.25 ops per input byte; it undercounts the quarter-round (12 VALU instructions on
+# gfx950), and is reported beside the literal count only as the page defines it.
+PAGE_OPS_PER_BYTE = 336 / 64
 LEAF_LANES = 256
 BATCH_COUNT, BATCH_LEN = 65536, 65536  # the batch workload: 65,536 messages of 64 KiB
 CPU_SHARE = 16  # host threads of one GPU's share on the benchmark machines
@@ -51,6 +56,15 @@ def leaf_compressions(length, group_chunks):
     n = full + (1 if tail else 0)
     groups = (n + group_chunks - 1) // group_chunks
     return blocks + (n - groups)
+
+
+def message_compressions(length):
+    """Compressions of one whole hash: every block of every chunk plus n - 1 parents."""
+    if length == 0:
+        return 1
+    full, tail = divmod(length, 1024)
+    n = full + (1 if tail else 0)
+    return full * 16 + (0 if tail == 0 else (tail + 63) // 64) + n - 1
 
 
 def kernel_source_digest():
@@ -188,9 +202,12 @@ def main():
         return
     if args.workload == XOF_WORKLOAD:
         return bench_xof(args, torch, b3, workloads, dev, stream)
-    batch = args.workload == "batch64k"
+    batch = args.workload in ("batch64k", "ragged256")
     if batch:
-        base, offs, lengths, keys_cpu = workloads.uniform_batch(BATCH_COUNT, BATCH_LEN, dev)
+        if args.workload == "batch64k":
+            base, offs, lengths, keys_cpu = workloads.uniform_batch(BATCH_COUNT, BATCH_LEN, dev)
+        else:
+            base, offs, lengths, keys_cpu = workloads.ragged_batch(dev)
         keys = keys_cpu.to(dev)
         nbytes = sum(lengths)
         out = torch.empty((len(lengths), 32), dtype=torch.uint8, device=dev)
@@ -229,7 +246,25 @@ def main():
 
     # the dominant kernel alone: the leaf pass, launched on the same stream
     roofline = None
-    if batch:
+    if args.workload == "ragged256":
+        # leaf and level launches over the task table: the roofline is taken over the step
+        ops = sum(message_compressions(n) for n in lengths) * OPS_PER_COMPRESSION
+        achieved = ops / (ms_per_step / 1e3) / 1e12
+        roofline = {
+            "bound": "alu",
+            "achieved": round(achieved, 3),
+            "peak": round(VALU_INT_PEAK_TOPS, 3),
+            "unit": "Tops/s (int32 VALU lane-ops)",
+            "frac": round(achieved / VALU_INT_PEAK_TOPS, 4),
+            "traffic": None,
+            "kernel": "whole step (leaf_batch_kernel + level_batch_kernel launches, task table upload)",
+            "kernel_ms": round(ms_per_step, 4),
+            "ops_per_launch": ops,
+            "hbm_gbs": round(value, 1),
+            "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        }
+        log(f"step (all kernels): {achieved:.2f} Tops/s = {achieved / VALU_INT_PEAK_TOPS:.1%} of the int-VALU peak")
+    elif batch:
         # every 64 KiB message fits one leaf workgroup: the step is the leaf kernel alone,
         # one launch, so the chain's event timing is the kernel's
         k = b3.leaf_group_chunks(nbytes) // LEAF_LANES
@@ -296,17 +331,22 @@ def main():
             sample = len(host) if args.cpu_sample_gib is None else min(len(host), int(args.cpu_sample_gib * (1 << 30)))
             c0 = time.perf_counter()
             if batch:
-                per = BATCH_LEN
-                got = oracle.hash_batch(host[:sample], [i * per for i in range(sample // per)],
-                                        [per] * (sample // per), keys_cpu.numpy().tobytes()[:32 * (sample // per)],
-                                        nthreads=cores)
-                sample = per * (sample // per)
+                # whole messages from the front of the batch, until the sample's bytes are used
+                cnt, end = 0, 0
+                while cnt < len(lengths) and offs[cnt] + lengths[cnt] <= sample:
+                    end = offs[cnt] + lengths[cnt]
+                    cnt += 1
+                got = oracle.hash_batch(host[:end], offs[:cnt], lengths[:cnt],
+                                        keys_cpu.numpy().tobytes()[:32 * cnt], nthreads=cores)
+                sample = sum(lengths[:cnt])
+                if cnt < len(lengths):
+                    got = None
             else:
                 got = oracle.hash_mt(host[:sample], key, cores)
             c_s = time.perf_counter() - c0
-            if sample == len(host):
+            if got is not None and (batch or sample == len(host)):
                 want = got
-            what = "all" if sample == len(host) else f"the first {sample}"
+            what = "all" if want is not None else f"the first {sample}"
             cpu = {"value": round(sample / 1e9 / c_s, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
                    "sample": f"{what} bytes of the same {args.workload} input ({sample} B), plain scalar C oracle "
                              f"(multi-threaded aligned-subtree form), {c_s:.2f} s wall, {cores} threads"}
@@ -329,6 +369,8 @@ def main():
             "fp32_8192": "one keyed BLAKE3 of an 8192x8192 fp32 N(0,1) tensor's bytes (seed 2, key seed 12)",
             "mib1": "one keyed BLAKE3 of 1 MiB uniform random bytes (seed 0, key seed 1)",
             "batch64k": "65,536 keyed BLAKE3 hashes of 64 KiB each (seed 4, key seed 14)",
+            "ragged256": "256 keyed BLAKE3 hashes of ragged lengths 0 B .. 1 MiB (lengths and bytes seed 5, "
+                         "key seed 15), packed with 0xA5 gaps",
         }[args.workload],
         "bytes": nbytes,
         "chunks": (nbytes + 1023) // 1024,
@@ -353,6 +395,11 @@ def main():
         "cpu_baseline": cpu,
         "digest_match": digest_match,
         "hbm_frac_chain": round(value / HBM_PEAK_GBS, 4),
+        "roof_at_page_op_count": {
+            "ops_per_byte": PAGE_OPS_PER_BYTE,
+            "roof_gbs": round(min(HBM_PEAK_GBS, VALU_INT_PEAK_TOPS * 1e3 / PAGE_OPS_PER_BYTE), 1),
+            "frac": round(value / min(HBM_PEAK_GBS, VALU_INT_PEAK_TOPS * 1e3 / PAGE_OPS_PER_BYTE), 4),
+        },
     }
     print(json.dumps(rec), flush=True)
 

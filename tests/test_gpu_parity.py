@@ -77,6 +77,36 @@ def test_brute_force_lengths_single_call(b3, dev, monkeypatch, quad):
         assert not bad, f"{len(bad)} lengths differ, first {bad[:5]}"
 
 
+@pytest.mark.parametrize("quad", ["default", QUAD_OFF])
+def test_every_tail_length(b3, dev, monkeypatch, quad):
+    # every length of a message's last chunk, 0..1024 bytes, after 0, 1 and 4 full chunks:
+    # the last chunk's final block, and within it the 16-byte piece that holds the last
+    # byte, take every position; single calls and one batch with 0xA5 gaps
+    if quad != "default":
+        monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", quad)
+    from blake3_merkle_tree_amd import workloads
+    lengths = [0] + [full * 1024 + t for full in (0, 1, 4) for t in range(1, 1025)]
+    offs, total = workloads.pack_messages(lengths)
+    base = torch.full((total,), 0xA5, dtype=torch.uint8, device=dev)
+    data = workloads.random_bytes(total, 34, dev)
+    for o, L in zip(offs, lengths):
+        base[o:o + L] = data[o:o + L]
+    host = _host(base)
+    keys = workloads.key_bytes(35, len(lengths))
+    want = oracle.hash_batch(host, offs, lengths, keys.numpy().tobytes(), nthreads=NTHREADS)
+    _say("every tail length, single calls, cases", len(lengths))
+    outs = torch.empty((len(lengths), 32), dtype=torch.uint8, device=dev)
+    for i, (o, L) in enumerate(zip(offs, lengths)):
+        b3.keyed_hash(base[o:o + L], bytes(keys[i].tolist()), out=outs[i])
+    got = _digests_to_bytes(outs)
+    bad = [L for L, g, w in zip(lengths, got, want) if g != w]
+    assert not bad, f"{len(bad)} lengths differ, first {bad[:5]}"
+    _say("every tail length, one batch")
+    got = _digests_to_bytes(b3.keyed_hash_batch(base, offs, lengths, keys.to(dev)))
+    bad = [L for L, g, w in zip(lengths, got, want) if g != w]
+    assert not bad, f"{len(bad)} lengths differ in the batch, first {bad[:5]}"
+
+
 @pytest.mark.parametrize("quad,fused", [("default", "1"), (QUAD_ALL, "1"), ("default", "0"), (QUAD_ALL, "0")])
 def test_level_boundaries(b3, dev, monkeypatch, quad, fused):
     # 256-chunk leaf workgroups and 256-CV level workgroups: counts around 256 and 256^2;
