@@ -23,9 +23,11 @@
  *    allocated and freed in stream order on `stream` from a memory pool the library
  *    creates once per device and keeps (freed blocks are reused by later calls). Each
  *    call owns its scratch, so calls on different streams may overlap.
- *  - Arguments are checked before any HIP call. Errors are returned as negative
- *    b3g_status values and nothing is enqueued; faults of the device work itself (e.g.
- *    a dev_in that is not device memory) surface at the caller's next synchronisation.
+ *  - Errors are returned as negative b3g_status values. Arguments are checked before any
+ *    HIP call, so an argument error (EINVAL, EALIGN, ETOOBIG) enqueues nothing. ENOMEM and
+ *    EHIP can come after part of the work was enqueued; the output is then unspecified.
+ *    Faults of the device work itself (e.g. a dev_in that is not device memory) surface at
+ *    the caller's next synchronisation.
  *  - Digests are the 8 output words of the final compression as little-endian bytes.
  */
 #ifndef BLAKE3_GPU_H
