@@ -16,6 +16,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -67,11 +68,17 @@ def message_compressions(length):
     return full * 16 + (0 if tail == 0 else (tail + 63) // 64) + n - 1
 
 
-def kernel_source_digest():
+def kernel_source_digest(csrc=None):
+    """Digest of the kernel sources with comments and whitespace runs removed: it changes
+    when the device code does, not when a comment does."""
+    csrc = csrc or os.path.join(ROOT, "blake3_merkle_tree_amd", "csrc")
     h = hashlib.sha256()
     for f in ("b3_device.h", "b3_kernels.hip", "b3_kernels.h"):
-        with open(os.path.join(ROOT, "blake3_merkle_tree_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -178,8 +185,8 @@ def main():
                          "bytes) --steps times: the reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the hash of one buffer "
-              "runs on a single device here. See the sharding notes in DESIGN.md.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the hash of one buffer "
+              "runs on a single device, and sharding an input across devices is not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -651,7 +651,7 @@ __device__ __forceinline__ void uniform_common(UniformSegs &sg, const Args &a) {
 // Ordering: the CV words are only ever accessed as agent-scope atomics, which on gfx950
 // write through to, and read from, the point of coherence shared by all XCDs. A writer's
 // ticket is issued only after vmcnt(0) has seen its CV stores acknowledged there, and the
-// last arrival issues its CV loads only after its ticket has returned (the verdict reaches
+// last arrival issues its CV loads only after its ticket has returned (the outcome reaches
 // the other waves through LDS and a barrier), so those loads find every CV of the group.
 // This relies on the hardware's in-order completion rather than on release/acquire
 // ordering: an agent-scope release fence per workgroup would also write back the XCD's
@@ -666,7 +666,7 @@ __device__ void fused_levels(const UniformLeafArgs &a, uint32_t *lds) {
         const uint64_t group = idx / kLevelLanes, first = group * kLevelLanes;
         const uint32_t count = g_in - first < kLevelLanes ? static_cast<uint32_t>(g_in - first) : kLevelLanes;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's CV stores have completed
-        __syncthreads();  // ... in every wave; the tree is done with the LDS: word 0 carries the verdict
+        __syncthreads();  // ... in every wave; the tree is done with the LDS: word 0 carries the outcome
         if (lane == 0) lds[0] = atomicAdd(a.lvl_ctr[L] + msg * g_out + group, 1u) + 1u == count ? 1u : 0u;
         __syncthreads();
         const bool last = lds[0] != 0;
