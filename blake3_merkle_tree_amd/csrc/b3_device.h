@@ -108,6 +108,77 @@ __device__ __forceinline__ void compress(uint32_t (&cv)[8], const uint32_t (&m)[
     for (int i = 0; i < 8; ++i) cv[i] = v[i] ^ v[i + 8];
 }
 
+// ---- chained blocks: the chaining value kept unfolded ---------------------------------
+// Within a chunk, block i+1 starts from block i's output cv[j] = s[j] ^ s[j+8] (s: the 16
+// state words after the last round). That fold need not be computed: in the first round
+// only the column quarter-rounds read cv, and there a = cv[j], b = cv[4+j] appear in
+// a + b + x and b ^ c. With gfx950's three-input ops, (s[j] ^ s[j+8]) + ((s[4+j] ^
+// s[12+j]) + x) is two v_xad_u32 and s[4+j] ^ s[12+j] ^ c one v_bitop3_b32, against two
+// xors, one v_add3_u32 and one xor: 4 instructions fewer per chained compression (676;
+// the first block of a chunk starts from the state (cv, 0) and takes 684).
+
+// (a ^ b) + c in one instruction. Both three-input forms are written as assembly: the
+// compiler would otherwise share a ^ b between the sum and the xor below and bring back the
+// separate fold.
+__device__ __forceinline__ uint32_t xad(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_xad_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// a ^ b ^ c in one instruction (v_bitop3_b32 with truth table 0x96).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// The rest of round 0 and rounds 1..6 on v, whose columns have already been mixed.
+__device__ __forceinline__ void rounds_after_columns(uint32_t (&v)[16], const uint32_t (&m)[16]) {
+    quarter(v[0], v[5], v[10], v[15], mw<0, 8>(m), mw<0, 9>(m));
+    quarter(v[1], v[6], v[11], v[12], mw<0, 10>(m), mw<0, 11>(m));
+    quarter(v[2], v[7], v[8], v[13], mw<0, 12>(m), mw<0, 13>(m));
+    quarter(v[3], v[4], v[9], v[14], mw<0, 14>(m), mw<0, 15>(m));
+    round_r<1>(v, m);
+    round_r<2>(v, m);
+    round_r<3>(v, m);
+    round_r<4>(v, m);
+    round_r<5>(v, m);
+    round_r<6>(v, m);
+}
+
+// Column j of round 0 for a block whose chaining value is the fold of the state p.
+__device__ __forceinline__ void chained_column(uint32_t pa, uint32_t pa8, uint32_t pb, uint32_t pb8, uint32_t &a,
+                                               uint32_t &b, uint32_t &c, uint32_t &d, uint32_t x, uint32_t y) {
+    a = xad(pa, pa8, xad(pb, pb8, x));  // cv[j] + cv[4+j] + x
+    d = rotr(d ^ a, 16);
+    c = c + d;
+    b = rotr(xor3(pb, pb8, c), 12);  // cv[4+j] ^ c
+    a = a + b + y;
+    d = rotr(d ^ a, 8);
+    c = c + d;
+    b = rotr(b ^ c, 7);
+}
+
+// v <- the state after compressing block m from the chaining value fold(s).
+__device__ __forceinline__ void compress_chained(const uint32_t (&s)[16], const uint32_t (&m)[16],
+                                                 uint32_t counter_lo, uint32_t counter_hi, uint32_t block_len,
+                                                 uint32_t flags, uint32_t (&v)[16]) {
+    v[8] = kIV[0], v[9] = kIV[1], v[10] = kIV[2], v[11] = kIV[3];
+    v[12] = counter_lo, v[13] = counter_hi, v[14] = block_len, v[15] = flags;
+    chained_column(s[0], s[8], s[4], s[12], v[0], v[4], v[8], v[12], mw<0, 0>(m), mw<0, 1>(m));
+    chained_column(s[1], s[9], s[5], s[13], v[1], v[5], v[9], v[13], mw<0, 2>(m), mw<0, 3>(m));
+    chained_column(s[2], s[10], s[6], s[14], v[2], v[6], v[10], v[14], mw<0, 4>(m), mw<0, 5>(m));
+    chained_column(s[3], s[11], s[7], s[15], v[3], v[7], v[11], v[15], mw<0, 6>(m), mw<0, 7>(m));
+    rounds_after_columns(v, m);
+}
+
+// The chaining value of a state: cv[i] = s[i] ^ s[i+8].
+__device__ __forceinline__ void fold_state(uint32_t (&cv)[8], const uint32_t (&s)[16]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cv[i] = s[i] ^ s[i + 8];
+}
+
 // All sixteen output words of the compression (extended output): words 0..7 as in
 // compress, words 8..15 = v[i+8] ^ cv[i].
 __device__ __forceinline__ void compress_xof(const uint32_t (&cv)[8], const uint32_t (&m)[16], uint32_t counter_lo,

@@ -59,23 +59,39 @@ __device__ __forceinline__ void compress_block(uint32_t (&cv)[8], const Block &k
 
 __device__ __forceinline__ Block load_block(const uint4 *p) { return Block{p[0], p[1], p[2], p[3]}; }
 
+// v <- the state after block k, chained from state s (see compress_chained).
+__device__ __forceinline__ void compress_block_chained(const uint32_t (&s)[16], const Block &k, uint32_t lo, uint32_t hi,
+                                                       uint32_t flags, uint32_t (&v)[16]) {
+    const uint32_t m[16] = {k.q0.x, k.q0.y, k.q0.z, k.q0.w, k.q1.x, k.q1.y, k.q1.z, k.q1.w,
+                            k.q2.x, k.q2.y, k.q2.z, k.q2.w, k.q3.x, k.q3.y, k.q3.z, k.q3.w};
+    compress_chained(s, m, lo, hi, kBlockBytes, flags, v);
+}
+
 // Full 1 KiB chunk with per-lane 16-byte loads (16-byte aligned). Blocks are handled in
 // pairs with two register sets, so the loads of a block are issued ahead of its
 // compression and no registers are copied between iterations; the reload of the even set
 // is unconditional (the last iteration re-reads block 14, which is in cache) so that the
-// loop carries no conditional register values. `end_flags` go on the last block
-// (CHUNK_END, plus ROOT when the chunk is the whole message).
+// loop carries no conditional register values. Between blocks the state stays unfolded
+// (compress_chained), alternating between two arrays; the first block starts from the
+// state (cv, 0), whose fold is cv. `end_flags` go on the last block (CHUNK_END, plus ROOT
+// when the chunk is the whole message).
 __device__ __forceinline__ void hash_full_chunk(uint32_t (&cv)[8], const uint8_t *chunk, uint32_t ctr_lo,
                                                 uint32_t ctr_hi, uint32_t mode, uint32_t end_flags) {
     const uint4 *p = reinterpret_cast<const uint4 *>(chunk);
+    // the state after an even block (st) and after an odd one (su); st starts as a state
+    // whose fold is the chaining value the chunk starts from
+    uint32_t st[16], su[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st[i] = cv[i], st[i + 8] = 0;
     Block even = load_block(p);
     for (uint32_t b = 0; b < kBlocksPerChunk; b += 2) {
         const Block odd = load_block(p + 4 * (b + 1));
-        compress_block(cv, even, ctr_lo, ctr_hi, mode | (b == 0 ? kChunkStart : 0u));
+        compress_block_chained(st, even, ctr_lo, ctr_hi, mode | (b == 0 ? kChunkStart : 0u), su);
         const uint32_t next = b + 2 < kBlocksPerChunk ? b + 2 : kBlocksPerChunk - 2;
         even = load_block(p + 4 * next);
-        compress_block(cv, odd, ctr_lo, ctr_hi, mode | (b + 2 == kBlocksPerChunk ? end_flags : 0u));
+        compress_block_chained(su, odd, ctr_lo, ctr_hi, mode | (b + 2 == kBlocksPerChunk ? end_flags : 0u), st);
     }
+    fold_state(cv, st);
 }
 
 // Sixteen zero bytes in device memory: the source of every load of a chunk piece that
