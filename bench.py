@@ -32,7 +32,9 @@ METRIC = "GB/s hashed, single keyed BLAKE3 of 4 GiB input; % of VALU/HBM rooflin
 VALU_INT_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
 # VALU lane-ops per compression on gfx950: 7 rounds x 8 quarter-rounds x 12 (2 v_add3_u32,
-# 2 v_add_u32, 4 v_xor_b32, 4 v_alignbit_b32) + 8 v_xor_b32 for the output fold.
+# 2 v_add_u32, 4 v_xor_b32, 4 v_alignbit_b32) + 8 v_xor_b32 for the output fold. This is the
+# algorithmic count the roofline uses; the leaf issues 676 for a block chained inside a
+# chunk, whose fold merges into the next block's first round.
 OPS_PER_COMPRESSION = 7 * 8 * 12 + 8
 # The BLAKE3 page's own count, 7 rounds x 8 quarter-rounds x 6 ops = 336 per 64-byte block,
 # i.e. 5.25 ops per input byte; it undercounts the quarter-round (12 VALU instructions on
