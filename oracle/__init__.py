@@ -44,6 +44,7 @@ def _load():
     lib.b3o_hash_recursive.argtypes = [_u8p, ctypes.c_uint64, _u8p, _u8p]
     lib.b3o_subtree_cv.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_uint64, _u8p, _u32p]
     lib.b3o_hash_xof.argtypes = [_u8p, ctypes.c_uint64, _u8p, _u8p, ctypes.c_uint64]
+    lib.b3o_hash_xof_at.argtypes = [_u8p, ctypes.c_uint64, _u8p, ctypes.c_uint64, _u8p, ctypes.c_uint64]
     lib.b3o_hasher_new.argtypes = [_u8p]
     lib.b3o_hasher_new.restype = ctypes.c_void_p
     lib.b3o_hasher_free.argtypes = [ctypes.c_void_p]
@@ -138,13 +139,13 @@ def subtree_cv(data, chunk_base=0, key=None):
     return list(out)
 
 
-def hash_xof(data, key=None, out_len=32):
-    """Extended output: out_len bytes of the root node's output stream (blocks of 64
-    bytes, counter 0, 1, ...); the first 32 bytes are the hash."""
+def hash_xof(data, key=None, out_len=32, offset=0):
+    """Extended output: bytes [offset, offset + out_len) of the root node's output stream
+    (blocks of 64 bytes, counter 0, 1, ...); the first 32 bytes are the hash."""
     arr, ptr = _as_u8(data)
     _k, kp = _key(key)
     out = (ctypes.c_uint8 * max(int(out_len), 1))()
-    _load().b3o_hash_xof(ptr, arr.size, kp, out, int(out_len))
+    _load().b3o_hash_xof_at(ptr, arr.size, kp, int(offset), out, int(out_len))
     return bytes(out)[:int(out_len)]
 
 

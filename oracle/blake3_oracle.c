@@ -248,8 +248,11 @@ void b3o_subtree_cv(const uint8_t *data, uint64_t len, uint64_t chunk_base, cons
  * the two top subtrees (left: the largest power of two of chunks below n). Output block
  * t (64 bytes) is that compression run again with counter t and ROOT, all sixteen output
  * words (specification, "Extendable output"); its first 32 bytes for t = 0 are the hash.
- * The page leaves extendable output out ("Future work"). key32 == NULL: default mode. */
-void b3o_hash_xof(const uint8_t *data, uint64_t len, const uint8_t *key32, uint8_t *out, uint64_t out_len) {
+ * b3o_hash_xof_at writes stream bytes [offset, offset + out_len), so any part of the stream
+ * can be read without the blocks before it. The page leaves extendable output out ("Future
+ * work"). key32 == NULL: default mode. */
+void b3o_hash_xof_at(const uint8_t *data, uint64_t len, const uint8_t *key32, uint64_t offset, uint8_t *out,
+                     uint64_t out_len) {
     uint32_t kw[8], mode, cv[8], m[16], o[16], blen, flags;
     mode_setup(key32, kw, &mode);
     uint64_t n = num_chunks(len);
@@ -273,13 +276,22 @@ void b3o_hash_xof(const uint8_t *data, uint64_t len, const uint8_t *key32, uint8
         blen = B3O_BLOCK_LEN;
         flags = mode | B3O_PARENT;
     }
-    for (uint64_t t = 0; t * B3O_BLOCK_LEN < out_len; t++) {
+    /* stream byte s = offset + j lies in block s / 64 at position s % 64 */
+    for (uint64_t j = 0; j < out_len;) {
+        uint64_t s = offset + j, t = s / B3O_BLOCK_LEN;
         uint8_t block[B3O_BLOCK_LEN];
         b3o_compress(cv, m, t, blen, flags | B3O_ROOT, o);
         for (int i = 0; i < 16; i++) store_le32(block + 4 * i, o[i]);
-        uint64_t take = out_len - t * B3O_BLOCK_LEN < B3O_BLOCK_LEN ? out_len - t * B3O_BLOCK_LEN : B3O_BLOCK_LEN;
-        memcpy(out + t * B3O_BLOCK_LEN, block, (size_t)take);
+        uint64_t at = s % B3O_BLOCK_LEN, take = B3O_BLOCK_LEN - at;
+        if (take > out_len - j) take = out_len - j;
+        memcpy(out + j, block + at, (size_t)take);
+        j += take;
     }
+}
+
+/* The first out_len bytes of the stream. */
+void b3o_hash_xof(const uint8_t *data, uint64_t len, const uint8_t *key32, uint8_t *out, uint64_t out_len) {
+    b3o_hash_xof_at(data, len, key32, 0, out, out_len);
 }
 
 /* ---- Incremental (stack-merge) form --------------------------------------------- */

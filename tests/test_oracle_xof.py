@@ -6,6 +6,7 @@ What fixes what:
     subtrees) and its ROOT flag to the digest, which the Xet cross-check in
     test_oracle_pins.py pins to an independent BLAKE3.
   * The stream is one sequence: a longer request extends a shorter one.
+  * Reading from an offset gives the same bytes as the stream read from its start.
   * Output blocks past the first 32 bytes (the root compression re-run with counter
     t = 0, 1, ..., and the second half of each 64-byte block, words v[i+8] ^ cv[i]) come
     from the BLAKE3 specification's text only: no independent extendable-output
@@ -48,3 +49,28 @@ def test_output_blocks_differ():
     out = oracle.hash_xof(_data(3000, 13), None, 64 * 40)
     blocks = {out[64 * i:64 * i + 64] for i in range(40)}
     assert len(blocks) == 40
+
+
+@pytest.mark.parametrize("n", [0, 100, 1024, 3000])
+def test_reading_from_an_offset_matches_the_stream(n):
+    data = _data(n, 14)
+    key = _data(32, 15)
+    full = oracle.hash_xof(data, key, 1200)
+    for off in (0, 1, 31, 32, 63, 64, 65, 100, 640, 1000):
+        for k in (0, 1, 63, 64, 65, 129):
+            if off + k <= len(full):
+                assert oracle.hash_xof(data, key, k, offset=off) == full[off:off + k], (off, k)
+
+
+def test_offsets_past_the_32_bit_block_counter():
+    # blocks 2^32 - 1 and 2^32 differ (the counter's high word enters the state) and a read
+    # across that boundary is the concatenation of reads on either side
+    data = _data(2500, 16)
+    base = 64 * (1 << 32)
+    a = oracle.hash_xof(data, None, 64, offset=base - 64)
+    b = oracle.hash_xof(data, None, 64, offset=base)
+    assert a != b
+    assert oracle.hash_xof(data, None, 128, offset=base - 64) == a + b
+    assert oracle.hash_xof(data, None, 50, offset=base - 20) == a[44:] + b[:30]
+    # block t = 2^32 is not block 0: the high word is not dropped
+    assert b != oracle.hash_xof(data, None, 64)
