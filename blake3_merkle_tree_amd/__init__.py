@@ -7,7 +7,8 @@ library's HIP kernels. The functions mirror the C entry points:
     hash(t)                              -> 32-byte digest tensor on t's device
     keyed_hash(t, key)                   -> 32-byte digest tensor (key: 32 bytes)
     keyed_hash_batch(base, offsets, lengths, keys=None) -> (n, 32) digest tensor
-    hash_xof(t, key=None, out_len=32)    -> out_len bytes of extended output
+    hash_xof(t, key=None, out_len=32, offset=0) -> bytes [offset, offset + out_len) of the
+                                         extended output
     subtree_cv(t, key=None, chunk_base=0) -> CV (no ROOT) of the tree over t's chunks
 
 A tensor is hashed as its raw bytes in memory order (a contiguous fp32 tensor as its
@@ -56,6 +57,7 @@ def _load():
     lib.blake3_gpu_group_cvs.argtypes = [vp, u64, u64, ctypes.POINTER(ctypes.c_uint32), ctypes.c_uint32, vp, vp]
     lib.blake3_gpu_subtree_cv.argtypes = [vp, u64, u64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
     lib.blake3_gpu_hash_xof.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_uint32), vp, u64, vp]
+    lib.blake3_gpu_hash_xof_at.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_uint32), u64, vp, u64, vp]
     lib.blake3_gpu_leaf_group_chunks.argtypes = [u64]
     lib.blake3_gpu_leaf_group_chunks.restype = ctypes.c_uint32
     lib.blake3_gpu_strerror.argtypes = [ctypes.c_int]
@@ -65,7 +67,7 @@ def _load():
     lib.debug_plan.argtypes = [ctypes.POINTER(u64), u64, ctypes.POINTER(u64), u64]
     lib.debug_plan.restype = ctypes.c_int64
     for f in ("blake3_gpu_hash", "blake3_gpu_keyed_hash", "blake3_gpu_keyed_hash_batch", "blake3_gpu_group_cvs",
-              "blake3_gpu_subtree_cv", "blake3_gpu_hash_xof", "blake3_gpu_version"):
+              "blake3_gpu_subtree_cv", "blake3_gpu_hash_xof", "blake3_gpu_hash_xof_at", "blake3_gpu_version"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -199,22 +201,22 @@ def keyed_hash_batch(base: torch.Tensor, offsets, lengths, keys=None, out=None, 
     return out
 
 
-def hash_xof(t: torch.Tensor, key=None, out_len: int = 32, out=None, stream=None) -> torch.Tensor:
-    """Extendable output: out_len bytes of the root node's output stream for the tensor's
-    bytes (key: 32 bytes for keyed mode, None for default mode); a uint8 device tensor.
-    Its first 32 bytes are the hash."""
+def hash_xof(t: torch.Tensor, key=None, out_len: int = 32, out=None, stream=None, offset: int = 0) -> torch.Tensor:
+    """Extendable output: bytes [offset, offset + out_len) of the root node's output stream
+    for the tensor's bytes (key: 32 bytes for keyed mode, None for default mode); a uint8
+    device tensor. Bytes 0..31 of the stream are the hash."""
     t = _device_bytes(t)
-    out_len = int(out_len)
-    if out_len < 0:
-        raise ValueError("out_len must be non-negative")
+    out_len, offset = int(out_len), int(offset)
+    if out_len < 0 or offset < 0:
+        raise ValueError("out_len and offset must be non-negative")
     out = _out(out, t.device, out_len)
     kw = _key_words(key) if key is not None else None
     nbytes = t.numel() * t.element_size()
     with torch.cuda.device(t.device):
-        rc = _load().blake3_gpu_hash_xof(ctypes.c_void_p(t.data_ptr() if nbytes else 0), nbytes, kw,
-                                         ctypes.c_void_p(out.data_ptr() if out_len else 0), out_len,
-                                         _stream_handle(t.device, stream))
-    _check(rc, "blake3_gpu_hash_xof")
+        rc = _load().blake3_gpu_hash_xof_at(ctypes.c_void_p(t.data_ptr() if nbytes else 0), nbytes, kw, offset,
+                                            ctypes.c_void_p(out.data_ptr() if out_len else 0), out_len,
+                                            _stream_handle(t.device, stream))
+    _check(rc, "blake3_gpu_hash_xof_at")
     return out
 
 

@@ -286,9 +286,12 @@ int subtree_cv(const void *in, uint64_t len, uint64_t chunk_base, const uint32_t
 // kernel chains the chunk's blocks up to the last one and copies the last block; for
 // more, the two top subtrees (left: the largest power of two of chunks below n) are
 // hashed without ROOT into one 64-byte block. Then every output block t is the root
-// compression with counter t, one lane each.
-int hash_xof(const void *in, uint64_t len, const uint32_t *key, void *out, uint64_t out_len, void *stream) {
+// compression with counter t, one lane each; out receives stream bytes
+// [out_offset, out_offset + out_len).
+int hash_xof(const void *in, uint64_t len, const uint32_t *key, uint64_t out_offset, void *out, uint64_t out_len,
+             void *stream) {
     if ((out == nullptr && out_len > 0) || (in == nullptr && len > 0)) return B3G_EINVAL;
+    if (out_offset + out_len < out_offset) return B3G_EINVAL;
     if (reinterpret_cast<uintptr_t>(in) % 16 != 0) return B3G_EALIGN;
     if (len > kMaxMessageBytes || out_len > kMaxXofBytes) return B3G_ETOOBIG;
     if (out_len == 0) return B3G_OK;
@@ -306,6 +309,7 @@ int hash_xof(const void *in, uint64_t len, const uint32_t *key, void *out, uint6
     memcpy(x.key, kw, sizeof(x.key));
     x.m = rec_m;
     x.out = static_cast<uint8_t *>(out);
+    x.out_offset = out_offset;
     x.out_len = out_len;
     const uint64_t n = chunks_of(len);
     if (n == 1) {
@@ -331,13 +335,21 @@ int hash_xof(const void *in, uint64_t len, const uint32_t *key, void *out, uint6
         x.block_len = kBlockBytes;
         x.flags = mode | kParent | kRoot;
     }
-    const uint64_t blocks = (out_len + kBlockBytes - 1) / kBlockBytes;
+    // blocks first_b .. end_b - 1, in launches that never cross a multiple of 2^32 blocks
+    const uint64_t first_b = out_offset / kBlockBytes;
+    const uint64_t last_byte = out_offset + out_len - 1;
+    const uint64_t end_b = last_byte / kBlockBytes + 1;
     constexpr uint64_t kPerLaunch = kMaxGrid * kXofLanes;
-    for (uint64_t b0 = 0; b0 < blocks; b0 += kPerLaunch) {
+    for (uint64_t b0 = first_b; b0 < end_b;) {
+        const uint64_t to_wrap = (1ull << 32) - (b0 & 0xFFFFFFFFull);
+        uint64_t nblk = end_b - b0;
+        if (nblk > kPerLaunch) nblk = kPerLaunch;
+        if (nblk > to_wrap) nblk = to_wrap;
         x.first_block = b0;
-        x.n_blocks = blocks - b0 < kPerLaunch ? blocks - b0 : kPerLaunch;
-        rc = launched(launch_xof_expand(x, static_cast<uint32_t>((x.n_blocks + kXofLanes - 1) / kXofLanes), s));
+        x.n_blocks = nblk;
+        rc = launched(launch_xof_expand(x, static_cast<uint32_t>((nblk + kXofLanes - 1) / kXofLanes), s));
         if (rc != B3G_OK) return rc;
+        b0 += nblk;
     }
     return B3G_OK;
 }
@@ -499,7 +511,12 @@ int blake3_gpu_subtree_cv(const void *dev_in, uint64_t len, uint64_t chunk_base,
 
 int blake3_gpu_hash_xof(const void *dev_in, uint64_t len, const uint32_t key[8], void *dev_out, uint64_t out_len,
                         void *stream) {
-    return b3g::hash_xof(dev_in, len, key, dev_out, out_len, stream);
+    return b3g::hash_xof(dev_in, len, key, 0, dev_out, out_len, stream);
+}
+
+int blake3_gpu_hash_xof_at(const void *dev_in, uint64_t len, const uint32_t key[8], uint64_t out_offset,
+                           void *dev_out, uint64_t out_len, void *stream) {
+    return b3g::hash_xof(dev_in, len, key, out_offset, dev_out, out_len, stream);
 }
 
 int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, const uint32_t key[8],

@@ -129,10 +129,12 @@ struct XofArgs {
     const uint32_t *m;    // device: the root compression's 16 message words
     uint32_t block_len;
     uint32_t flags;       // includes ROOT
-    uint64_t first_block; // counter of the first block of this launch
+    uint64_t first_block; // counter of the first block of this launch; a launch never
+                          // crosses a multiple of 2^32 blocks (one counter high word)
     uint64_t n_blocks;    // blocks of this launch
-    uint8_t *out;         // stream byte 64*first_block goes to out[64*first_block]
-    uint64_t out_len;     // total bytes wanted
+    uint8_t *out;         // receives stream bytes [out_offset, out_offset + out_len)
+    uint64_t out_offset;
+    uint64_t out_len;
 };
 hipError_t launch_xof_expand(const XofArgs &a, uint32_t grid, hipStream_t s);
 

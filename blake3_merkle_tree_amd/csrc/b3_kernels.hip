@@ -1006,14 +1006,45 @@ __global__ __launch_bounds__(64) void xof_chunk_root_kernel(ChunkRootArgs a) {
     for (int w = 0; w < 8; ++w) a.cv_out[w] = cv[w];
 }
 
-// One 64-byte output block per lane; the last block of the request is cut to out_len.
+// Rotation of a wave-uniform word on the scalar unit (which has no rotate: a shift pair
+// and an or). Written as assembly so that the compiler keeps the chain off the VALU.
+template <int K>
+__device__ __forceinline__ uint32_t srotr(uint32_t x) {
+    uint32_t r, t;
+    asm("s_lshr_b32 %0, %2, %3\n\ts_lshl_b32 %1, %2, %4\n\ts_or_b32 %0, %0, %1"
+        : "=&s"(r), "=&s"(t)
+        : "s"(x), "n"(K), "n"(32 - K)
+        : "scc");
+    return r;
+}
+
+// Quarter-round on wave-uniform words, on the scalar unit.
+__device__ __forceinline__ void quarter_uniform(uint32_t &a, uint32_t &b, uint32_t &c, uint32_t &d, uint32_t x,
+                                                uint32_t y) {
+    a = a + b + x;
+    d = srotr<16>(d ^ a);
+    c = c + d;
+    b = srotr<12>(b ^ c);
+    a = a + b + y;
+    d = srotr<8>(d ^ a);
+    c = c + d;
+    b = srotr<7>(b ^ c);
+}
+
+// One 64-byte output block per lane: block t is the root compression run with counter t,
+// all sixteen output words. Only the counter differs between lanes, and in round 0 it
+// enters column 0 (low word) and column 1 (high word, the same for the whole launch).
+// Columns 1..3 and the first sum of column 0 therefore read only wave-uniform words and
+// run once per wave on the scalar unit, which takes 37 of the block's 688 VALU
+// instructions off the vector unit. The stores keep to the requested byte range.
 __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
     const uint64_t i = static_cast<uint64_t>(blockIdx.x) * kXofLanes + threadIdx.x;
     if (i >= a.n_blocks) return;
     const uint64_t t = a.first_block + i;
+    const uint32_t t_hi = static_cast<uint32_t>(a.first_block >> 32);
     // the root's inputs are the same for every lane and nothing here writes them: scalar loads
     const uint32_t *__restrict__ src_m = a.m;
-    uint32_t cv[8], m[16], o[16];
+    uint32_t cv[8], m[16], v[16];
     if (a.cv) {
         const uint32_t *__restrict__ src_cv = a.cv;
 #pragma unroll
@@ -1024,18 +1055,48 @@ __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
     }
 #pragma unroll
     for (int w = 0; w < 16; ++w) m[w] = src_m[w];
-    compress_xof(cv, m, static_cast<uint32_t>(t), static_cast<uint32_t>(t >> 32), a.block_len, a.flags, o);
-    uint8_t *dst = a.out + kBlockBytes * t;
-    const uint64_t left = a.out_len - kBlockBytes * t;
-    if (left >= kBlockBytes && reinterpret_cast<uintptr_t>(dst) % 16 == 0) {
-        uint4 *d = reinterpret_cast<uint4 *>(dst);
+    // round 0, columns (the schedule of round 0 is the identity)
+    v[1] = cv[1], v[5] = cv[5], v[9] = kIV[1], v[13] = t_hi;
+    quarter_uniform(v[1], v[5], v[9], v[13], m[2], m[3]);
+    v[2] = cv[2], v[6] = cv[6], v[10] = kIV[2], v[14] = a.block_len;
+    quarter_uniform(v[2], v[6], v[10], v[14], m[4], m[5]);
+    v[3] = cv[3], v[7] = cv[7], v[11] = kIV[3], v[15] = a.flags;
+    quarter_uniform(v[3], v[7], v[11], v[15], m[6], m[7]);
+    {
+        uint32_t &pa = v[0], &pb = v[4], &pc = v[8], &pd = v[12];
+        pa = cv[0] + cv[4] + m[0];  // uniform
+        pb = cv[4], pc = kIV[0], pd = static_cast<uint32_t>(t);
+        pd = rotr(pd ^ pa, 16);
+        pc = pc + pd;
+        pb = rotr(pb ^ pc, 12);
+        pa = pa + pb + m[1];
+        pd = rotr(pd ^ pa, 8);
+        pc = pc + pd;
+        pb = rotr(pb ^ pc, 7);
+    }
+    rounds_after_columns(v, m);
+    uint32_t o[16];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        o[w] = v[w] ^ v[w + 8];
+        o[w + 8] = v[w + 8] ^ cv[w];
+    }
+    // stream bytes [s0, s0 + 64) of this block, clipped to [out_offset, end)
+    const uint64_t s0 = kBlockBytes * t, end = a.out_offset + a.out_len;
+    if (s0 >= a.out_offset && s0 + kBlockBytes <= end &&
+        reinterpret_cast<uintptr_t>(a.out + (s0 - a.out_offset)) % 16 == 0) {
+        uint4 *d = reinterpret_cast<uint4 *>(a.out + (s0 - a.out_offset));
         d[0] = make_uint4(o[0], o[1], o[2], o[3]);
         d[1] = make_uint4(o[4], o[5], o[6], o[7]);
         d[2] = make_uint4(o[8], o[9], o[10], o[11]);
         d[3] = make_uint4(o[12], o[13], o[14], o[15]);
     } else {
-        const uint32_t n = left < kBlockBytes ? static_cast<uint32_t>(left) : kBlockBytes;
-        for (uint32_t k = 0; k < n; ++k) dst[k] = static_cast<uint8_t>(o[k / 4] >> (8 * (k % 4)));
+        const uint64_t lo = s0 > a.out_offset ? s0 : a.out_offset;
+        const uint64_t hi = s0 + kBlockBytes < end ? s0 + kBlockBytes : end;
+        for (uint64_t x = lo; x < hi; ++x) {
+            const uint32_t k = static_cast<uint32_t>(x - s0);
+            a.out[x - a.out_offset] = static_cast<uint8_t>(o[k / 4] >> (8 * (k % 4)));
+        }
     }
 }
 

@@ -134,6 +134,19 @@ int blake3_gpu_hash_xof(const void *dev_in, uint64_t len, const uint32_t key[8],
                         void *stream);
 
 /*
+ * The same output stream read from any position: stream bytes [out_offset, out_offset +
+ * out_len) of the extendable output of dev_in[0 .. len), written to dev_out[0 .. out_len)
+ * (BLAKE3 specification, extendable output: block t of the stream depends only on t, so no
+ * earlier block is computed). blake3_gpu_hash_xof is the case out_offset == 0. Useful for
+ * consumers that each take a slice of one long output stream.
+ *   out_offset  any byte offset; out_offset + out_len must not exceed 2^64 - 1.
+ * Other arguments as blake3_gpu_hash_xof. Errors: as blake3_gpu_hash_xof, and EINVAL when
+ * out_offset + out_len overflows 64 bits.
+ */
+int blake3_gpu_hash_xof_at(const void *dev_in, uint64_t len, const uint32_t key[8], uint64_t out_offset,
+                           void *dev_out, uint64_t out_len, void *stream);
+
+/*
  * The first tree level that one workgroup produces: the chaining value (CV) of every
  * aligned group of group_chunks consecutive 1 KiB chunks of dev_in[0 .. len) (the last
  * group may be shorter), with chunk counters starting at chunk_base and no ROOT flag

@@ -72,6 +72,13 @@ def test_subtree_and_xof_argument_checks():
     assert lib.blake3_gpu_hash_xof(MISALIGNED, 5, None, ALIGNED, 10, None) == b3.EALIGN
     assert lib.blake3_gpu_hash_xof(ALIGNED, 5, None, ALIGNED, (1 << 42) + 1, None) == b3.ETOOBIG
     assert lib.blake3_gpu_hash_xof(ALIGNED, 5, None, None, 0, None) == b3.OK  # nothing to write
+    lib.blake3_gpu_hash_xof_at.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
+                                           ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    assert lib.blake3_gpu_hash_xof_at(ALIGNED, 5, None, (1 << 64) - 10, ALIGNED, 20, None) == b3.EINVAL  # wraps
+    assert lib.blake3_gpu_hash_xof_at(ALIGNED, 5, None, 7, None, 10, None) == b3.EINVAL
+    assert lib.blake3_gpu_hash_xof_at(MISALIGNED, 5, None, 7, ALIGNED, 10, None) == b3.EALIGN
+    assert lib.blake3_gpu_hash_xof_at(ALIGNED, 5, None, 7, ALIGNED, (1 << 42) + 1, None) == b3.ETOOBIG
+    assert lib.blake3_gpu_hash_xof_at(ALIGNED, 5, None, (1 << 64) - 1, None, 0, None) == b3.OK
 
 
 def test_batch_argument_checks():

@@ -406,6 +406,31 @@ def test_xof_matches_oracle(b3, dev, keyed):
 
 
 @pytest.mark.parametrize("keyed", [True, False])
+def test_xof_from_an_offset_matches_oracle(b3, dev, keyed):
+    # reads that start mid-block, span several launches' worth of lanes, end mid-block, and
+    # sit at and across multiples of 2^32 blocks (the counter's high word changes there,
+    # and no launch may cross it); a misaligned destination with untouched bytes around it
+    from blake3_merkle_tree_amd import workloads
+    buf = workloads.random_bytes(70 * 1024 + 9, 74, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(75)[0].tolist()) if keyed else None
+    wrap = 64 << 32
+    cases = [(L, off, n) for L in (0, 100, 1024, 70 * 1024 + 9)
+             for off, n in ((0, 64), (1, 63), (63, 2), (64, 64), (100, 1000), (5, 64 * 300 + 7),
+                            (wrap - 64, 128), (wrap - 21, 50), (wrap, 64), (wrap - 64 * 700 - 3, 64 * 1400 + 9),
+                            (3 * wrap + 17, 300), ((1 << 62) + 1, 200))]
+    for L, off, n in cases:
+        _say("xof at", off, "length", n, "input", L, "keyed", keyed)
+        got = bytes(b3.hash_xof(buf[:L], key, n, offset=off).cpu().numpy().tobytes())
+        assert got == oracle.hash_xof(host[:L].tobytes(), key, n, offset=off), (L, off, n)
+    dst = torch.full((200 + 10,), 7, dtype=torch.uint8, device=dev)
+    b3.hash_xof(buf[:1000], key, 200, out=dst[5:205], offset=wrap - 100)
+    d = dst.cpu().numpy()
+    assert bytes(d[5:205].tobytes()) == oracle.hash_xof(host[:1000].tobytes(), key, 200, offset=wrap - 100)
+    assert (d[:5] == 7).all() and (d[205:] == 7).all()
+
+
+@pytest.mark.parametrize("keyed", [True, False])
 def test_subtree_cv_matches_oracle(b3, dev, keyed):
     from blake3_merkle_tree_amd import workloads
     buf = workloads.random_bytes(70000 * 1024, 72, dev)
