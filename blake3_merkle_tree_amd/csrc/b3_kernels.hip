@@ -832,10 +832,17 @@ __device__ __forceinline__ uint4 load_piece_bounded(const uint8_t *chunk, uint32
                       load_word_bounded(chunk, off + 8, len), load_word_bounded(chunk, off + 12, len));
 }
 
+// Words per staged chunk row in LDS: 256 data words plus 4 of padding. Rows 256 words apart
+// would put the same word of every quad's chunk in one bank, and each message read of
+// the compression (four words per lane per round, a different quad per chunk) would be an
+// 8-way bank conflict per half-wave; at 260 it averages 1.8-way (3 at worst), the 64 lanes
+// of a wave spread over the 32 banks.
+constexpr uint32_t kQuadRowWords = kChunkBytes / 4 + 4;
+
 template <bool Fused>
 __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a) {
-    // the staged chunks (64 KiB); afterwards the tree's level buffers
-    __shared__ __attribute__((aligned(16))) uint32_t lds[kQuadLeafChunks * kChunkBytes / 4];
+    // the staged chunks (65 KiB); afterwards the tree's level buffers
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kQuadLeafChunks * kQuadRowWords];
     const uint32_t lane = threadIdx.x, q = lane >> 2, j = lane & 3u;
     UniformSegs sg{};
     uint64_t first_chunk = 0;
@@ -858,7 +865,7 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a
     // chunk slot q of the workgroup: chunk x of segment s
     const uint32_t s = q >> sg.lanes_log2, x = q - (s << sg.lanes_log2);
     const bool active = s < sg.segs && x < sg.nodes;  // the same for the quad's 4 lanes
-    uint32_t *mine = lds + q * (kChunkBytes / 4);
+    uint32_t *mine = lds + q * kQuadRowWords;
     uint32_t lo = 0, hi = 0;  // this lane's CV words j and 4 + j
     uint32_t clen = 0;
     if (active) {
