@@ -93,11 +93,12 @@ uint32_t choose_chunks_per_lane(uint64_t total_chunks) {
         const int k = atoi(e);
         if (k == 1 || k == 2 || k == 4) return static_cast<uint32_t>(k);
     }
-    // Four chunks per lane once the 1024-chunk workgroups still give every CU at least
-    // two (256 CUs): it cuts the lane-sparse top of each workgroup tree and the fold work
-    // by 4x. Measured on MI355X: 4 GiB and 16 GiB inputs run ~2% faster than at one chunk
-    // per lane, 256 MiB runs equal; smaller inputs need the extra workgroups.
-    if (total_chunks >= (1ull << 19)) return 4;
+    // Four chunks per lane from 2 GiB of input: it cuts the lane-sparse top of each
+    // workgroup tree and the fold work by 4x once the 1024-chunk workgroups are many rounds
+    // of the chip. Measured on MI355X (ms at K = 1 / 2 / 4): 512 MiB 0.197 / 0.197 / 0.206,
+    // 1 GiB 0.362 / 0.360 / 0.368, 2 GiB 0.699 / 0.704 / 0.696, 4 GiB 1.416 / 1.390 / 1.384,
+    // 8 GiB 2.988 / 2.808 / 2.768; below 2 GiB the extra workgroups of K = 1 win.
+    if (total_chunks >= (1ull << 21)) return 4;
     return 1;
 }
 

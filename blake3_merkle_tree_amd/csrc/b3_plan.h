@@ -50,10 +50,10 @@ struct BatchPlan {
 uint64_t chunks_of(uint64_t len);       // max(1, ceil(len / 1024))
 uint32_t ceil_log2_host(uint64_t n);     // 0 for n <= 1
 
-// Chunks per leaf lane (1, 2 or 4) for an input of `total_chunks` chunks: 4 once the grid
-// of 1024-chunk workgroups still gives every CU two of them, 1 for smaller inputs so
-// that they keep enough waves in flight. BLAKE3_GPU_CHUNKS_PER_LANE (1, 2 or 4) in the
-// environment overrides the choice (for tests and benchmarks).
+// Chunks per leaf lane (1, 2 or 4) for an input of `total_chunks` chunks: 4 from 2 GiB
+// of input, 1 for smaller inputs so that they keep enough waves in flight.
+// BLAKE3_GPU_CHUNKS_PER_LANE (1, 2 or 4) in the environment overrides the choice (for
+// tests and benchmarks).
 uint32_t choose_chunks_per_lane(uint64_t total_chunks);
 
 // Input path of full leaf waves: per-lane loads (default) or staged through LDS with
