@@ -126,9 +126,7 @@ bool use_lds_staging() {
 }
 
 uint32_t ceil_log2_host(uint64_t n) {
-    uint32_t r = 0;
-    while ((1ull << r) < n) ++r;
-    return r;
+    return n <= 1 ? 0u : 64u - static_cast<uint32_t>(__builtin_clzll(n - 1));
 }
 
 int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_t chunks_per_lane,
@@ -149,19 +147,21 @@ int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_
         const uint64_t per_node = pass == 0 ? chunks_per_lane : 1;
         const uint64_t lanes = pass == 0 ? leaf_lanes : level_lanes;
         const uint64_t span = lanes * per_node;  // units (chunks or CVs) per full group
+        // all three are powers of two: shifts instead of divisions in the per-message loop
+        const uint32_t node_shift = ceil_log2_host(per_node), span_shift = ceil_log2_host(span);
         std::vector<Group> groups;
         groups.reserve(pass == 0 ? n : n / 4 + 16);
         uint64_t out_cvs = 0;
         for (uint64_t i = 0; i < n; ++i) {
             if (nodes[i] == 0) continue;
-            const uint64_t ngroups = (nodes[i] + span - 1) / span;
+            const uint64_t ngroups = (nodes[i] + span - 1) >> span_shift;
             const bool final = ngroups == 1;
             out_base[i] = out_cvs;
             if (!final) out_cvs += ngroups;
             for (uint64_t k = 0; k < ngroups; ++k) {
                 const uint64_t first = (pass == 0 ? 0 : in_base[i]) + k * span;
                 const uint64_t units = std::min<uint64_t>(span, nodes[i] - k * span);
-                const uint64_t count = (units + per_node - 1) / per_node;
+                const uint64_t count = (units + per_node - 1) >> node_shift;
                 if (first >= (1ull << 32) || out_base[i] + k >= (1ull << 32)) return kTooBig;
                 groups.push_back(Group{static_cast<uint32_t>(i), static_cast<uint32_t>(first),
                                        static_cast<uint32_t>(count),
