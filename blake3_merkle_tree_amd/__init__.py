@@ -269,8 +269,10 @@ def group_cvs(t: torch.Tensor, key=None, chunk_base: int = 0, group_chunks: int 
 def debug_plan_batch(lengths):
     """The batch planner's launch plan for messages of these byte lengths (no GPU work):
     a list of passes, each a dict with lanes, chunks_per_lane, in_cvs, out_cvs,
-    wg_first_seg, wg_levels and segs as (msg, first, dst, lane_start, nodes, final)
-    tuples (pass 0: `first` is a chunk index and a node covers chunks_per_lane chunks)."""
+    wg_first_seg, wg_levels and segs as (msg, first, dst, lane_start, nodes, final, pair)
+    tuples (pass 0: `first` is a chunk index and a node covers chunks_per_lane chunks;
+    `pair`: the segment's last node is the parent of input CVs first+nodes-1 and
+    first+nodes)."""
     lib = _load()
     lens = (ctypes.c_uint64 * len(lengths))(*[int(x) for x in lengths])
     need = lib.debug_plan(lens, len(lens), None, 0)
@@ -291,7 +293,8 @@ def debug_plan_batch(lengths):
         segs = []
         for i in range(nseg):
             msg, f, dst, info = words[pos + 4 * i:pos + 4 * i + 4]
-            segs.append((msg, f, dst, info & 0xFFF, ((info >> 12) & 0xFFF) + 1, bool(info >> 31)))
+            segs.append((msg, f, dst, info & 0xFFF, ((info >> 12) & 0xFFF) + 1, bool(info >> 31),
+                         bool((info >> 30) & 1)))
         pos += 4 * nseg
         passes.append(dict(lanes=lanes, chunks_per_lane=cpl, in_cvs=in_cvs, out_cvs=out_cvs,
                            wg_first_seg=first, wg_levels=levels, segs=segs))

@@ -83,6 +83,7 @@ struct UniformLevelArgs {
 __host__ __device__ inline uint32_t seg_lane(uint32_t info) { return info & 0xFFFu; }
 __host__ __device__ inline uint32_t seg_count(uint32_t info) { return ((info >> 12) & 0xFFFu) + 1u; }
 __host__ __device__ inline bool seg_final(uint32_t info) { return (info & kSegFinal) != 0; }
+__host__ __device__ inline bool seg_pair(uint32_t info) { return (info & kSegPair) != 0; }
 
 struct BatchLeafArgs {
     const uint8_t *base;          // message buffer (16-byte aligned)

@@ -113,12 +113,25 @@ __device__ __forceinline__ uint4 load_tail_piece(const uint8_t *chunk, uint32_t 
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// 16-byte piece at byte `at` of a chunk holding `len` valid bytes when it lies wholly
+// inside them, else zeros (loaded from the zero piece, so that the load needs no branch).
+__device__ __forceinline__ uint4 load_piece_or_zero(const uint8_t *chunk, uint32_t at, uint32_t len) {
+    return *reinterpret_cast<const uint4 *>(at + 16 <= len ? chunk + at : g_zero_piece);
+}
+
+__device__ __forceinline__ Block load_block_or_zero(const uint8_t *chunk, uint32_t off, uint32_t len) {
+    return Block{load_piece_or_zero(chunk, off, len), load_piece_or_zero(chunk, off + 16, len),
+                 load_piece_or_zero(chunk, off + 32, len), load_piece_or_zero(chunk, off + 48, len)};
+}
+
 // Chunk of `len` <= 1024 bytes with per-lane loads that never read past `len`:
 // max(1, ceil(len/64)) blocks, the last one of length len - 64*(blocks-1). The loads are
 // branch-free: a 16-byte piece wholly inside the chunk is one 16-byte load, a piece past
 // the end is loaded from the zero piece, and the piece holding the last byte, loaded once
 // (load_tail_piece), is substituted at its offset. (Bounded loads with branches cost a
-// quarter more VALU instructions and three hundred scalar ones per block.)
+// quarter more VALU instructions and three hundred scalar ones per block.) Each block is
+// loaded when its compression starts, which keeps the kernels that hash single messages
+// at their register count: their short chunks are a message's last.
 __device__ void hash_short_chunk(uint32_t (&cv)[8], const uint8_t *chunk, uint32_t len, uint32_t ctr_lo,
                                  uint32_t ctr_hi, uint32_t mode, uint32_t end_flags) {
     const uint32_t nb = len == 0 ? 1u : (len + kBlockBytes - 1) / kBlockBytes;
@@ -129,14 +142,38 @@ __device__ void hash_short_chunk(uint32_t (&cv)[8], const uint8_t *chunk, uint32
         uint4 q[4];
 #pragma unroll
         for (uint32_t p = 0; p < 4; ++p) {
-            const uint32_t at = off + 16 * p;
-            q[p] = *reinterpret_cast<const uint4 *>(at + 16 <= len ? chunk + at : g_zero_piece);
-            if (at == tail_off) q[p] = tail;
+            q[p] = load_piece_or_zero(chunk, off + 16 * p, len);
+            if (off + 16 * p == tail_off) q[p] = tail;
         }
         const bool last = b + 1 == nb;
         const uint32_t flags = mode | (b == 0 ? kChunkStart : 0u) | (last ? end_flags : 0u);
         compress_block(cv, Block{q[0], q[1], q[2], q[3]}, ctr_lo, ctr_hi, flags, last ? len - off : kBlockBytes);
     }
+}
+
+// The same chunk hash with each block's loads issued while the block before it is
+// compressed (16 more registers), for waves that hold only message ends and often run
+// alone on their SIMD at the end of a batch's grid, where a load per block would wait
+// for memory every time. Every block but the last lies wholly inside the chunk; a lane's
+// loop runs its own block count and the wave's last blocks are compressed together, with
+// the piece holding the last byte substituted.
+__device__ void hash_short_chunk_ahead(uint32_t (&cv)[8], const uint8_t *chunk, uint32_t len, uint32_t ctr_lo,
+                                       uint32_t ctr_hi, uint32_t mode, uint32_t end_flags) {
+    const uint32_t nb = len == 0 ? 1u : (len + kBlockBytes - 1) / kBlockBytes;
+    const uint4 tail = load_tail_piece(chunk, len);
+    const uint32_t tail_off = len & ~15u;
+    Block cur = load_block_or_zero(chunk, 0, len);
+    for (uint32_t b = 0; b + 1 < nb; ++b) {
+        const Block next = load_block_or_zero(chunk, (b + 1) * kBlockBytes, len);
+        compress_block(cv, cur, ctr_lo, ctr_hi, mode | (b == 0 ? kChunkStart : 0u));
+        cur = next;
+    }
+    const uint32_t off = (nb - 1) * kBlockBytes;
+    if (off == tail_off) cur.q0 = tail;
+    if (off + 16 == tail_off) cur.q1 = tail;
+    if (off + 32 == tail_off) cur.q2 = tail;
+    if (off + 48 == tail_off) cur.q3 = tail;
+    compress_block(cv, cur, ctr_lo, ctr_hi, mode | (nb == 1 ? kChunkStart : 0u) | end_flags, len - off);
 }
 
 constexpr uint32_t kLanes = kLeafLanes;
@@ -191,7 +228,7 @@ __device__ __forceinline__ void fold_chunk(uint32_t (&c)[8], uint32_t k, uint32_
 // per-lane and bounded by the byte count. The last chunk has last_len bytes (1024 unless
 // it ends the message). `root`: this node is the whole message, so its final compression
 // carries ROOT.
-template <uint32_t K>
+template <uint32_t K, bool Ahead = false>
 __device__ __forceinline__ void lane_subtree(uint32_t (&c)[8], const uint8_t *ptr, uint32_t nl,
                                              uint32_t last_len, uint64_t ctr0, const uint32_t (&key)[8],
                                              uint32_t mode, bool root) {
@@ -204,7 +241,9 @@ __device__ __forceinline__ void lane_subtree(uint32_t (&c)[8], const uint8_t *pt
         const uint32_t lo = static_cast<uint32_t>(ctr), hi = static_cast<uint32_t>(ctr >> 32);
         const uint32_t end_flags = kChunkEnd | (root && nl == 1 ? kRoot : 0u);
         const uint8_t *chunk = ptr + static_cast<uint64_t>(k) * kChunkBytes;
-        hash_short_chunk(c, chunk, k + 1 == nl ? last_len : kChunkBytes, lo, hi, mode, end_flags);
+        const uint32_t len = k + 1 == nl ? last_len : kChunkBytes;
+        if (Ahead) hash_short_chunk_ahead(c, chunk, len, lo, hi, mode, end_flags);
+        else hash_short_chunk(c, chunk, len, lo, hi, mode, end_flags);
         if (K > 1) fold_chunk<K>(c, k, slot1c, slot2c, k + 1 < nl, fin_k, key, mode);
     }
     // nl not a power of two (only 3 when K <= 4): the 2-chunk subtree on the left remains
@@ -968,7 +1007,9 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_batch_kernel(BatchLeafArgs a)
             direct_subtree<K>(cv, ptr, c0, key, sg.mode(), root ? kRoot : 0u, lds + lane);
         }
     } else if (nl > 0) {
-        lane_subtree<K>(cv, ptr, nl, last_len, c0, key, sg.mode(), root);
+        // the ends of a batch's messages: whole workgroups of them, often alone on their
+        // SIMDs at the end of the grid, so their loads are issued a block ahead
+        lane_subtree<K, true>(cv, ptr, nl, last_len, c0, key, sg.mode(), root);
     }
     __syncthreads();  // every wave is done with its stage buffer before the tree reuses it
     tree_reduce<kLanes>(cv, sg, a.wg_levels[blockIdx.x], reinterpret_cast<uint32_t(*)[8][kLanes]>(lds));
@@ -982,11 +1023,21 @@ __global__ __launch_bounds__(kLevelLanes) void level_batch_kernel(BatchLevelArgs
     const uint32_t lane = threadIdx.x;
     const int s = s_seg_of[lane];
     uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    BatchSegs sg{s_seg, s_seg_of, a.keys, a.cv_out, a.digests};
     if (s >= 0) {
         const Seg g = s_seg[s];
-        load_cv(cv, a.cv_in + 8ull * (g.first + (lane - seg_lane(g.info))));
+        const uint32_t x = lane - seg_lane(g.info);
+        load_cv(cv, a.cv_in + 8ull * (g.first + x));
+        if (seg_pair(g.info) && x + 1 == seg_count(g.info)) {
+            // the message's end was split in two subtrees in pass 0: this node is their parent
+            uint32_t left[8], key[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) left[w] = cv[w];
+            load_cv(cv, a.cv_in + 8ull * (g.first + x + 1));
+            sg.key_words(s, key);
+            parent_left(cv, left, key, sg.mode(), false);
+        }
     }
-    BatchSegs sg{s_seg, s_seg_of, a.keys, a.cv_out, a.digests};
     tree_reduce<kLevelLanes>(cv, sg, a.wg_levels[blockIdx.x], buf);
 }
 

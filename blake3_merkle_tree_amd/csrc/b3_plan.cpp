@@ -8,81 +8,63 @@
 // subtree is complete and at least as large as the right), the tree over the group
 // roots is the BLAKE3 tree of the message, one level up.
 //
-// Packing. A full group fills a workgroup alone. Smaller groups are bucketed by the next
-// power of two R of their size (largest first, in one linear pass) and laid out back to
-// back; because the sizes are non-increasing powers of two, every group then starts at a
-// multiple of its own R, which keeps the in-workgroup pairing from mixing groups.
+// Split message ends. In pass 0 a message's last group, when it is not the message's
+// only group, holds more nodes than half a workgroup and is not a complete power of two,
+// would fill a workgroup alone with idle lanes. It is cut instead into its left subtree
+// (the largest power of two below its node count: the BLAKE3 tree's left child of that
+// group's root) and the rest, two groups with two output CVs; in pass 1 the message's
+// last node is their parent, which the lane holding that node computes before the
+// workgroup's tree (the segment's pair bit). This keeps the lanes of pass 0 dense
+// without changing the tree or the number of passes.
+//
+// Packing. Every group takes R lanes, the next power of two of its node count (a full
+// group: the whole workgroup). Groups are bucketed by R and laid out back to back, the
+// largest R first and in message order within a bucket; because the sizes are
+// non-increasing powers of two that divide the workgroup, every group starts at a
+// multiple of its own R (which keeps the in-workgroup pairing from mixing groups) and
+// never straddles two workgroups. A group's lane position is therefore a prefix sum: one
+// pass over the messages counts the groups per bucket, a second writes each task entry
+// in place, and the workgroup boundaries follow from the bucket layout.
 #include "b3_plan.h"
 
 #include <stdlib.h>
 
-#include <algorithm>
 
 namespace b3g {
 
 namespace {
 constexpr int kOk = 0;
 constexpr int kTooBig = -5;
+constexpr uint32_t kMaxBuckets = 13;  // lanes per workgroup <= 4096
 
-uint32_t next_pow2(uint32_t n) {
-    uint32_t r = 1;
-    while (r < n) r <<= 1;
-    return r;
-}
+uint32_t floor_log2_host(uint64_t n) { return 63u - static_cast<uint32_t>(__builtin_clzll(n)); }
 
-struct Group {
-    uint32_t msg, first, count, dst;
-    bool final;
-};
-
-// Lays groups out over workgroups of `lanes` lanes (a power of two).
-int pack(const std::vector<Group> &groups, uint32_t lanes, PassPlan *p) {
-    p->lanes = lanes;  // g.count is in nodes (lanes)
-    // bucket the partial groups by log2 of their power of two (stable within a bucket)
-    const uint32_t top = ceil_log2_host(lanes);
-    std::vector<uint64_t> bucket_size(top + 2, 0);
-    uint64_t full = 0;
-    for (const Group &g : groups) {
-        if (g.count == lanes) ++full;
-        else ++bucket_size[ceil_log2_host(g.count)];
+// Calls f(first, count, bucket, dst_offset, final, pair) for the groups of one message in
+// one pass (see the grouping and split rules above). `nodes`: the message's units
+// entering the pass; `first0`: its first unit's index in the pass input; `pair_end`: its
+// last node is a pair; `split`: set when its end is split. dst_offset is the group's
+// output CV relative to the message's first one.
+template <class F>
+inline void for_each_group(uint64_t nodes, uint64_t first0, uint32_t per_node_shift, uint32_t span_shift,
+                           uint64_t lanes, bool may_split, bool pair_end, bool *split, F &&f) {
+    const uint64_t span = 1ull << span_shift;
+    const uint64_t ngroups = (nodes + span - 1) >> span_shift;
+    const bool final = ngroups == 1;
+    for (uint64_t k = 0; k + 1 < ngroups; ++k)
+        f(first0 + k * span, lanes, floor_log2_host(lanes), k, false, false);
+    const uint64_t k = ngroups - 1;
+    const uint64_t tail_units = nodes - k * span;
+    const uint64_t count = (tail_units + (1ull << per_node_shift) - 1) >> per_node_shift;
+    *split = may_split && !final && 2 * count > lanes && (count & (count - 1)) != 0;
+    if (*split) {
+        const uint32_t lb = floor_log2_host(count);
+        const uint64_t left = 1ull << lb;
+        f(first0 + k * span, left, lb, k, false, false);
+        f(first0 + k * span + (left << per_node_shift), count - left, ceil_log2_host(count - left), k + 1, false,
+          false);
+    } else {
+        f(first0 + k * span, count, ceil_log2_host(count), k, final, pair_end);
     }
-    std::vector<uint64_t> bucket_at(top + 2, 0);  // largest power first
-    uint64_t pos = 0;
-    for (int b = static_cast<int>(top); b >= 0; --b) {
-        bucket_at[b] = pos;
-        pos += bucket_size[b];
-    }
-    std::vector<uint32_t> order(pos);
-    p->segs.reserve(groups.size());
-    p->wg_first_seg.reserve(full + pos / 2 + 2);
-    p->wg_levels.reserve(full + pos / 2 + 1);
-    for (size_t i = 0; i < groups.size(); ++i) {
-        const Group &g = groups[i];
-        if (g.count == lanes) {
-            p->wg_first_seg.push_back(static_cast<uint32_t>(p->segs.size()));
-            p->wg_levels.push_back(static_cast<uint8_t>(ceil_log2_host(g.count)));
-            p->segs.push_back(Seg{g.msg, g.first, g.dst, seg_info(0, g.count, g.final)});
-        } else {
-            order[bucket_at[ceil_log2_host(g.count)]++] = static_cast<uint32_t>(i);
-        }
-    }
-    uint32_t offset = lanes;  // forces a new workgroup for the first partial group
-    for (uint32_t i : order) {
-        const Group &g = groups[i];
-        const uint32_t r = next_pow2(g.count);
-        if (offset + r > lanes) {
-            p->wg_first_seg.push_back(static_cast<uint32_t>(p->segs.size()));
-            p->wg_levels.push_back(0);
-            offset = 0;
-        }
-        p->segs.push_back(Seg{g.msg, g.first, g.dst, seg_info(offset, g.count, g.final)});
-        uint8_t &lv = p->wg_levels.back();
-        lv = std::max<uint8_t>(lv, static_cast<uint8_t>(ceil_log2_host(g.count)));
-        offset += r;
-    }
-    if (p->segs.size() >= (1ull << 32) || p->wg_levels.size() >= (1ull << 31)) return kTooBig;
-    p->wg_first_seg.push_back(static_cast<uint32_t>(p->segs.size()));
-    return kOk;
 }
 }  // namespace
 
@@ -140,44 +122,96 @@ int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_
         if (lengths[i] > kMaxMessageBytes) return kTooBig;
         nodes[i] = chunks_of(lengths[i]);
     }
-    // in_base[i]: where message i's input CVs start in the current pass's input array
+    // in_base[i]: where message i's input CVs start in the current pass's input array;
+    // pair_end[i]: its last node in this pass is the parent of its last two input CVs
     std::vector<uint64_t> in_base(n, 0), out_base(n, 0);
+    std::vector<uint8_t> pair_end(n, 0), split(n, 0);
     for (uint32_t pass = 0;; ++pass) {
         // a pass-0 node is a lane's run of chunks_per_lane chunks; later nodes are CVs
         const uint64_t per_node = pass == 0 ? chunks_per_lane : 1;
         const uint64_t lanes = pass == 0 ? leaf_lanes : level_lanes;
-        const uint64_t span = lanes * per_node;  // units (chunks or CVs) per full group
-        // all three are powers of two: shifts instead of divisions in the per-message loop
-        const uint32_t node_shift = ceil_log2_host(per_node), span_shift = ceil_log2_host(span);
-        std::vector<Group> groups;
-        groups.reserve(pass == 0 ? n : n / 4 + 16);
+        const uint32_t top = floor_log2_host(lanes);
+        if (top >= kMaxBuckets) return kTooBig;
+        const uint32_t node_shift = ceil_log2_host(per_node), span_shift = top + node_shift;
+        const bool may_split = pass == 0;
+        // groups per bucket (bucket b: groups of 2^b lanes) and each message's output CVs
+        uint64_t bucket_n[kMaxBuckets] = {};
         uint64_t out_cvs = 0;
         for (uint64_t i = 0; i < n; ++i) {
             if (nodes[i] == 0) continue;
-            const uint64_t ngroups = (nodes[i] + span - 1) >> span_shift;
-            const bool final = ngroups == 1;
+            bool sp = false, final = false;
+            for_each_group(nodes[i], pass == 0 ? 0 : in_base[i], node_shift, span_shift, lanes, may_split,
+                           pair_end[i] != 0, &sp,
+                           [&](uint64_t, uint64_t, uint32_t b, uint64_t, bool fin, bool) {
+                               ++bucket_n[b];
+                               final = fin;
+                           });
+            split[i] = sp;
             out_base[i] = out_cvs;
-            if (!final) out_cvs += ngroups;
-            for (uint64_t k = 0; k < ngroups; ++k) {
-                const uint64_t first = (pass == 0 ? 0 : in_base[i]) + k * span;
-                const uint64_t units = std::min<uint64_t>(span, nodes[i] - k * span);
-                const uint64_t count = (units + per_node - 1) >> node_shift;
-                if (first >= (1ull << 32) || out_base[i] + k >= (1ull << 32)) return kTooBig;
-                groups.push_back(Group{static_cast<uint32_t>(i), static_cast<uint32_t>(first),
-                                       static_cast<uint32_t>(count),
-                                       final ? 0u : static_cast<uint32_t>(out_base[i] + k), final});
-            }
-            nodes[i] = final ? 0 : ngroups;
+            if (!final) out_cvs += ((nodes[i] + (1ull << span_shift) - 1) >> span_shift) + (sp ? 1 : 0);
         }
-        if (groups.empty()) break;
+        uint64_t total = 0;
+        for (uint32_t b = 0; b <= top; ++b) total += bucket_n[b];
+        if (total == 0) break;
+        if (total >= (1ull << 32) || out_cvs >= (1ull << 32)) return kTooBig;
+        // bucket layout, largest groups first: first task entry and first lane position
+        uint64_t seg_at[kMaxBuckets], lane_at[kMaxBuckets], seg_pos = 0, lane_pos = 0;
+        for (int b = static_cast<int>(top); b >= 0; --b) {
+            seg_at[b] = seg_pos;
+            lane_at[b] = lane_pos;
+            seg_pos += bucket_n[b];
+            lane_pos += bucket_n[b] << b;
+        }
+        const uint64_t workgroups = (lane_pos + lanes - 1) >> top;
+        if (workgroups >= (1ull << 31)) return kTooBig;
         PassPlan p;
+        p.lanes = static_cast<uint32_t>(lanes);
         p.chunks_per_lane = static_cast<uint32_t>(per_node);
         p.in_cvs = pass == 0 ? 0 : out->passes.back().out_cvs;
         p.out_cvs = out_cvs;
-        const int rc = pack(groups, static_cast<uint32_t>(lanes), &p);
-        if (rc != kOk) return rc;
+        // workgroup boundaries: a workgroup starts at every multiple of `lanes`, with the
+        // group that begins there (the largest of the workgroup: its tree's level count)
+        p.wg_first_seg.reserve(workgroups + 1);
+        p.wg_levels.reserve(workgroups);
+        for (int b = static_cast<int>(top); b >= 0; --b) {
+            const uint64_t l0 = lane_at[b], l1 = l0 + (bucket_n[b] << b);
+            for (uint64_t at = (l0 + lanes - 1) & ~(lanes - 1); at < l1; at += lanes) {
+                p.wg_first_seg.push_back(static_cast<uint32_t>(seg_at[b] + ((at - l0) >> b)));
+                p.wg_levels.push_back(static_cast<uint8_t>(b));
+            }
+        }
+        p.wg_first_seg.push_back(static_cast<uint32_t>(total));
+        // task entries in place
+        p.segs.resize(total);
+        Seg *segs = p.segs.data();
+        bool too_big = false;  // a unit index past 32 bits
+        for (uint64_t i = 0; i < n; ++i) {
+            if (nodes[i] == 0) continue;
+            const uint64_t base = out_base[i];
+            bool sp = false;
+            for_each_group(nodes[i], pass == 0 ? 0 : in_base[i], node_shift, span_shift, lanes, may_split,
+                           pair_end[i] != 0, &sp,
+                           [&](uint64_t first, uint64_t count, uint32_t b, uint64_t k, bool fin, bool pair) {
+                               const uint64_t lane = lane_at[b];
+                               lane_at[b] += 1ull << b;
+                               too_big |= first >= (1ull << 32);
+                               segs[seg_at[b]++] =
+                                   Seg{static_cast<uint32_t>(i), static_cast<uint32_t>(first),
+                                       fin ? 0u : static_cast<uint32_t>(base + k),
+                                       seg_info(static_cast<uint32_t>(lane & (lanes - 1)),
+                                                static_cast<uint32_t>(count), fin, pair)};
+                           });
+        }
+        if (too_big) return kTooBig;
+        // next pass: a message's nodes are its groups (a split end counts once)
+        for (uint64_t i = 0; i < n; ++i) {
+            if (nodes[i] == 0) continue;
+            const uint64_t ngroups = (nodes[i] + (1ull << span_shift) - 1) >> span_shift;
+            nodes[i] = ngroups == 1 ? 0 : ngroups;
+        }
         out->passes.push_back(std::move(p));
         in_base.swap(out_base);
+        pair_end.swap(split);
     }
     return kOk;
 }

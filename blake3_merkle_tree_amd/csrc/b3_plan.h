@@ -18,13 +18,16 @@ struct Seg {
     uint32_t msg;    // message index: key (keys + 8*msg) and digest slot (out + 32*msg)
     uint32_t first;  // pass 0: first chunk index within the message; pass t: first input CV
     uint32_t dst;    // index of the resulting CV in the pass's output array (if not final)
-    uint32_t info;   // bits 0..11 lane start, bits 12..23 node count - 1, bit 31 final
+    uint32_t info;   // bits 0..11 lane start, bits 12..23 node count - 1, bit 30 pair, bit 31 final
 };
 static_assert(sizeof(Seg) == 16, "Seg is a 16-byte table entry");
 
 constexpr uint32_t kSegFinal = 1u << 31;
-inline constexpr uint32_t seg_info(uint32_t lane, uint32_t count, bool final) {
-    return (lane & 0xFFFu) | (((count - 1) & 0xFFFu) << 12) | (final ? kSegFinal : 0u);
+// The segment's last node is the parent of two input CVs, first + count - 1 and
+// first + count (the two halves of a message end split in pass 0).
+constexpr uint32_t kSegPair = 1u << 30;
+inline constexpr uint32_t seg_info(uint32_t lane, uint32_t count, bool final, bool pair = false) {
+    return (lane & 0xFFFu) | (((count - 1) & 0xFFFu) << 12) | (final ? kSegFinal : 0u) | (pair ? kSegPair : 0u);
 }
 
 // Largest message accepted (bytes): chunk indices of a message fit in 32 bits.

@@ -183,6 +183,33 @@ def test_batch_mixed_lengths_with_gaps(b3, dev):
     assert singles == _digests_to_bytes(b3.keyed_hash_batch(base, offs, lengths, keys.to(dev)))
 
 
+@pytest.mark.parametrize("chunks_per_lane", ["1", "2", "4"])
+def test_batch_split_message_ends(b3, dev, monkeypatch, chunks_per_lane):
+    # a message's last group of more than half a workgroup that is not a power of two is
+    # split in the leaf pass into its left subtree and the rest, whose parent the level
+    # pass computes: 456 chunks split at one chunk per lane, 813 at two, 1725 at one and
+    # four; 70,100 chunks put the pair node in a level pass that is not the last
+    monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", chunks_per_lane)
+    from blake3_merkle_tree_amd import workloads
+    lengths = [456 * 1024 + 7, 813 * 1024, 1725 * 1024 + 11, 3000, 70100 * 1024 - 100, 1, 200 * 1024 + 5]
+    plan = b3.debug_plan_batch(lengths)
+    assert any(s[6] for p in plan[1:] for s in p["segs"]), "the plan has a split message end"
+    offs, total = workloads.pack_messages(lengths)
+    base = torch.full((total,), 0xA5, dtype=torch.uint8, device=dev)
+    data = workloads.random_bytes(total, 36, dev)
+    for o, L in zip(offs, lengths):
+        base[o:o + L] = data[o:o + L]
+    host = _host(base)
+    keys = workloads.key_bytes(37, len(lengths))
+    _say("batch split message ends, chunks per lane", chunks_per_lane)
+    out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))
+    want = oracle.hash_batch(host, offs, lengths, keys.numpy().tobytes(), nthreads=NTHREADS)
+    assert _digests_to_bytes(out) == want
+    out = b3.keyed_hash_batch(base, offs, lengths, None)
+    want = oracle.hash_batch(host, offs, lengths, None, nthreads=NTHREADS)
+    assert _digests_to_bytes(out) == want
+
+
 def test_batch_deep_messages(b3, dev):
     # messages with more than 256^2 chunks need a second level pass inside the batch
     from blake3_merkle_tree_amd import workloads

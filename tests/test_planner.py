@@ -42,6 +42,10 @@ LENGTH_SETS = [
     [1024 * 1024 + 1] + [17] * 300,
     list(np.random.Generator(np.random.PCG64(3)).integers(0, 600 * 1024, size=60)),
     [65 * 1024 * 1024 + 3, 2048],  # three passes for the first message
+    # message ends split in pass 0 (a last group of more than half a workgroup that is not a
+    # power of two): 456 chunks at one chunk per lane, 813 at two, 1725 at one and at four
+    [456 * 1024 + 7, 813 * 1024, 1725 * 1024 + 11, 3000],
+    [70100 * 1024 - 100],  # split end, then a pair node in a pass that is not the last
 ]
 
 
@@ -56,28 +60,27 @@ def test_plan_invariants(lengths, chunks_per_lane):
     plan = b3.debug_plan_batch(lengths)
     n = len(lengths)
     finals = [0] * n
-    units = {i: _chunks(L) for i, L in enumerate(lengths)}  # chunks (pass 0) or CVs entering the pass
+    units = {i: _chunks(int(L)) for i, L in enumerate(lengths)}  # chunks (pass 0) or nodes entering the pass
+    inputs = {}  # message -> the input CV indices of its nodes' subtrees, in tree order
+    splits = 0
     for pi, p in enumerate(plan):
         lanes = p["lanes"]
         per_node = chunks_per_lane if pi == 0 else 1
         assert lanes == 256 and p["chunks_per_lane"] == per_node
         span = lanes * per_node
-        covered = {}
+        by_msg = {}
         out_seen = set()
         first_idx = p["wg_first_seg"]
         for w in range(len(p["wg_levels"])):
             segs = p["segs"][first_idx[w]:first_idx[w + 1]]
             assert segs, "every workgroup holds a segment"
             used = 0
-            for (msg, first, dst, lane, count, final) in segs:
+            for (msg, first, dst, lane, count, final, pair) in segs:
                 assert 1 <= count <= lanes
                 assert lane % _next_pow2(count) == 0, "segment not aligned to its power of two"
                 assert lane >= used and lane + count <= lanes, "segments overlap or overflow"
                 used = lane + count
-                covered.setdefault(msg, []).append((first, count))
-                if pi == 0:
-                    seg_units = min(span, units[msg] - first)
-                    assert count == (seg_units + per_node - 1) // per_node
+                by_msg.setdefault(msg, []).append((first, count, dst, final, pair))
                 if final:
                     finals[msg] += 1
                 else:
@@ -85,18 +88,52 @@ def test_plan_invariants(lengths, chunks_per_lane):
                     out_seen.add(dst)
             assert p["wg_levels"][w] == max(_ceil_log2(s[4]) for s in segs)
         assert len(out_seen) == p["out_cvs"]
-        # each message still open is covered exactly once, in aligned groups of `span` units
-        for msg, spans in covered.items():
+        next_inputs = {}
+        for msg, spans in by_msg.items():
             spans.sort()
-            base = spans[0][0]
-            for k, (first, count) in enumerate(spans):
-                assert first == base + k * span
-            last_first, last_count = spans[-1]
-            assert (len(spans) - 1) * span + min(span, units[msg] - (last_first - base)) == units[msg]
             if pi == 0:
-                assert base == 0
-        units = {msg: len(spans) for msg, spans in covered.items() if len(spans) > 1}
+                # aligned groups of `span` chunks from chunk 0; the last may be split into its
+                # left subtree (the largest power of two below its node count) and the rest
+                assert not any(sp[4] for sp in spans), "no pair nodes in pass 0"
+                k_groups = (units[msg] + span - 1) // span
+                assert len(spans) in (k_groups, k_groups + 1)
+                for k in range(k_groups - 1):
+                    assert spans[k][0] == k * span and spans[k][1] == span // per_node
+                tail_units = units[msg] - (k_groups - 1) * span
+                tail_nodes = (tail_units + per_node - 1) // per_node
+                if len(spans) == k_groups + 1:
+                    splits += 1
+                    (fa, ca, _, _, _), (fb, cb, _, _, _) = spans[-2:]
+                    assert k_groups > 1, "a message's only group is never split"
+                    assert 2 * tail_nodes > lanes and tail_nodes & (tail_nodes - 1)
+                    assert ca == 1 << (tail_nodes.bit_length() - 1) and ca + cb == tail_nodes
+                    assert fa == (k_groups - 1) * span and fb == fa + ca * per_node
+                else:
+                    assert spans[-1][0] == (k_groups - 1) * span and spans[-1][1] == tail_nodes
+            else:
+                # nodes in aligned groups of `span`; a pair node only at the message's end,
+                # reading the two CVs its pass-0 split produced
+                nodes = inputs[msg]
+                for k, (first, count, dst, final, pair) in enumerate(spans):
+                    got = [[first + x] for x in range(count)]
+                    if pair:
+                        assert k == len(spans) - 1
+                        got[-1] = [first + count - 1, first + count]
+                    assert got == nodes[k * span:k * span + count]
+                assert sum(sp[1] for sp in spans) == len(nodes)
+            if not spans[0][3]:
+                # CVs of this pass in tree order; a split end's two CVs form one next node
+                dsts = [sp[2] for sp in spans]
+                if pi == 0 and len(spans) == (units[msg] + span - 1) // span + 1:
+                    next_inputs[msg] = [[d] for d in dsts[:-2]] + [dsts[-2:]]
+                else:
+                    next_inputs[msg] = [[d] for d in dsts]
+                assert [d for ds in next_inputs[msg] for d in ds] == list(range(dsts[0], dsts[0] + len(dsts)))
+        units = {msg: len(v) for msg, v in next_inputs.items()}
+        inputs = next_inputs
     assert finals == [1] * n, "every message is finished exactly once"
+    if lengths == LENGTH_SETS[-2]:
+        assert splits >= 1, "this set splits a message end at every chunks-per-lane setting"
 
 
 def _pair_reduce(nodes, kw, mode, final):
@@ -118,7 +155,7 @@ def _execute_plan(data, offsets, lengths, keys):
     for pi, p in enumerate(plan):
         cvs_out = [None] * p["out_cvs"]
         K = p["chunks_per_lane"]
-        for (msg, first, dst, lane, count, final) in p["segs"]:
+        for (msg, first, dst, lane, count, final, pair) in p["segs"]:
             kw = list(struct.unpack("<8I", keys[msg])) if keys else oracle.iv()
             mode = oracle.KEYED_HASH if keys else 0
             if pi == 0:
@@ -136,6 +173,10 @@ def _execute_plan(data, offsets, lengths, keys):
                     nodes.append(_pair_reduce(cvs, kw, mode, lone))
             else:
                 nodes = cvs_in[first:first + count]
+                if pair:
+                    # the two subtrees of a message end split in pass 0
+                    nodes[-1] = oracle.parent_cv(kw, mode, cvs_in[first + count - 1], cvs_in[first + count],
+                                                 is_root=False)
             top = _pair_reduce(nodes, kw, mode, final)
             if final:
                 digests[msg] = struct.pack("<8I", *top)
@@ -149,7 +190,8 @@ def _execute_plan(data, offsets, lengths, keys):
 def test_executed_plan_matches_oracle(keyed, chunks_per_lane):
     rng = np.random.Generator(np.random.PCG64(11))
     lengths = [0, 1, 63, 64, 65, 1023, 1024, 1025, 13 * 1024 + 17, 3 * 1024 + 1000, 65 * 1024 + 5,
-               256 * 1024, 256 * 1024 + 1, 511 * 1024 + 9] + rng.integers(0, 300 * 1024, size=12).tolist()
+               256 * 1024, 256 * 1024 + 1, 511 * 1024 + 9, 456 * 1024 + 7, 813 * 1024, 1725 * 1024 + 11] + \
+        rng.integers(0, 300 * 1024, size=12).tolist()
     offsets, pos = [], 0
     for L in lengths:
         offsets.append(pos)
@@ -172,6 +214,20 @@ def test_executed_plan_deep_tree(monkeypatch):
     plan = b3.debug_plan_batch([L])
     assert len(plan) == 3
     assert _execute_plan(data, [0], [L], [key])[0] == oracle.hash(data, key)
+
+
+def test_executed_plan_split_end_deep_tree(monkeypatch):
+    # 70,100 chunks at one chunk per lane: the last group (212 chunks) is split into 128 + 84
+    # in pass 0; pass 1 has 274 nodes, the last a pair, in two groups; pass 2 finishes
+    monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", "1")
+    rng = np.random.Generator(np.random.PCG64(13))
+    L = 70100 * 1024 - 100
+    data = rng.bytes(L)
+    plan = b3.debug_plan_batch([L])
+    assert len(plan) == 3
+    assert [s[4] for s in plan[0]["segs"] if s[4] != 256] == [128, 84]
+    assert [s[6] for s in plan[1]["segs"]] == [False, True]
+    assert _execute_plan(data, [0], [L], None)[0] == oracle.hash(data)
 
 
 def test_chunks_per_lane_choice(monkeypatch):
