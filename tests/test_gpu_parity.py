@@ -111,14 +111,17 @@ def test_every_tail_length(b3, dev, monkeypatch, quad):
 def test_level_boundaries(b3, dev, monkeypatch, quad, fused):
     # 256-chunk leaf workgroups and 256-CV level workgroups: counts around 256 and 256^2;
     # with the quad leaf, 64-chunk workgroups: counts around 64, 64*256 and 64*256^2.
+    # 200,000, 262,144 and 262,145 chunks leave 782, 1024 and 1025 leaf CVs: the first
+    # level pass ends with 4, 4 and 5 CVs.
     # fused: level passes run inside the leaf launch (last-arrival tickets), or as
     # separate level launches
     if quad != "default":
         monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", quad)
     monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", fused)
     from blake3_merkle_tree_amd import workloads
-    chunks = [63, 64, 65, 255, 256, 257, 511, 512, 513, 16383, 16384, 16385, 65535, 65536, 65537, 131073]
-    buf = workloads.random_bytes(131073 * 1024, 23, dev)
+    chunks = [63, 64, 65, 255, 256, 257, 511, 512, 513, 16383, 16384, 16385, 65535, 65536, 65537, 131073,
+              200000, 262144, 262145]
+    buf = workloads.random_bytes(262145 * 1024, 23, dev)
     host = _host(buf)
     key = bytes(workloads.key_bytes(24)[0].tolist())
     lengths = [(n - 1) * 1024 + t for n in chunks for t in (1, 1000, 1024)]
@@ -362,6 +365,7 @@ UNIFORM_CASES = [
     (3, 4 * 1024 * 1024, 4 * 1024 * 1024),
     (40, 64 * 1024 + 1, 65 * 1024),  # 65 chunks: just past one quad-leaf workgroup
     (2, 65537 * 1024 + 3, 65537 * 1024 + 16),  # at one chunk per lane: two level passes
+    (3, 600 * 256 * 1024 + 77, 600 * 256 * 1024 + 80),  # 600 leaf CVs a message at one chunk per lane
 ]
 
 
