@@ -103,9 +103,9 @@ constexpr uint64_t kMaxGrid = 0xFFFFFFFFull / kLeafLanes;
 // arithmetic), keyed by keys + 8*m (device) or all by `key` (host words). A leaf
 // workgroup covers `span` chunks (256*K, or 64 with the quad leaf for small inputs). A
 // message of at most `span` chunks is finished by the leaf pass, span/R messages per
-// workgroup. A longer one spans G leaf workgroups, whose CVs the level passes reduce 256 to one
-// workgroup until at most 256 remain, which one last pass finishes. Pass outputs
-// ping-pong between two CV arrays.
+// workgroup. A longer one spans G leaf workgroups, whose CVs the level passes reduce,
+// 256 to a workgroup, until at most 256 remain, which one last pass finishes. Pass
+// outputs ping-pong between two CV arrays.
 int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_msgs, const uint32_t *keys,
                  const uint32_t key[8], uint32_t mode, uint64_t chunk_base, uint32_t root_flag, uint8_t *out,
                  hipStream_t s) {

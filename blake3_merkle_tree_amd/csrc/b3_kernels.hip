@@ -18,14 +18,14 @@
 // gfx950 design. In the leaf kernel each lane hashes K consecutive chunks (K = 1, 2 or 4,
 // chosen by input size) and folds them into one subtree node in registers, so the first
 // log2(K) tree levels cost no cross-lane traffic and the lane-sparse top of the workgroup
-// tree is paid once per 256*K chunks. Lane x of the workgroup owns tree node x; level l+1 node q is computed by
-// lane q from level-l nodes 2q and 2q+1, so the active lanes stay packed at the bottom of
-// the workgroup (dense waves) instead of spreading out. Keeping the node of an odd last
-// position unchanged ("carry") at each level produces exactly the BLAKE3 shape: the left
-// child of every node is then a complete power-of-two subtree and at least as large as
-// the right one. Several independent segments (batch mode) share one workgroup by
-// sitting at lane offsets aligned to the next power of two of their size, so that the
-// same pairing never mixes two segments.
+// tree is paid once per 256*K chunks. Lane x of the workgroup owns tree node x; level l+1
+// node q is computed by lane q from level-l nodes 2q and 2q+1, so the active lanes stay
+// packed at the bottom of the workgroup (dense waves) instead of spreading out. Keeping
+// the node of an odd last position unchanged ("carry") at each level produces exactly the
+// BLAKE3 shape: the left child of every node is then a complete power-of-two subtree and
+// at least as large as the right one. Several independent segments (batch mode) share
+// one workgroup by sitting at lane offsets aligned to the next power of two of their
+// size, so that the same pairing never mixes two segments.
 #include "b3_device.h"
 #include "b3_kernels.h"
 
@@ -571,7 +571,8 @@ __device__ __forceinline__ uint32_t lane_levels(uint32_t used) {
 // (word w of node x at buf[.][w][x]). Output node p is the parent of nodes 2p and 2p+1,
 // whose 16 words are the message (left node's words 0..7, then the right node's), and
 // runs on lanes 4p..4p+3; moff holds the word offsets, within a level buffer, of the 28
-// words this lane reads. The workgroup needs 2C lanes for the first of these levels.
+// words this lane reads. A level over n nodes takes 2n lanes (four per output node);
+// lane_levels leaves to the quads only levels with at most kQuadLevelNodes output nodes.
 // InLoop: the caller runs this inside a loop; the lane's offsets are then made opaque to
 // the optimiser so that they are computed here rather than hoisted out of that loop,
 // where they would hold 28 registers across the rest of the kernel.
