@@ -319,7 +319,7 @@ def main():
             "unit": "Tops/s (int32 VALU lane-ops)",
             "frac": round(achieved / VALU_INT_PEAK_TOPS, 4),
             "traffic": measured_traffic(args.workload),
-            "kernel": f"leaf_uniform_kernel<{group // LEAF_LANES}>",
+            "kernel": "leaf_quad_kernel" if group < LEAF_LANES else f"leaf_uniform_kernel<{group // LEAF_LANES}>",
             "kernel_ms": round(leaf_ms, 4),
             "ops_per_launch": ops,
             "hbm_gbs": round(nbytes / 1e9 / (leaf_ms / 1e3), 1),

@@ -245,9 +245,9 @@ def leaf_group_chunks(nbytes: int) -> int:
 
 def group_cvs(t: torch.Tensor, key=None, chunk_base: int = 0, group_chunks: int = 256, out=None,
               stream=None) -> torch.Tensor:
-    """CVs (no ROOT) of the aligned groups of group_chunks chunks (256, 512 or 1024) of the
-    tensor's bytes, chunk counters starting at chunk_base: a (groups, 8) int32 device
-    tensor of little-endian words."""
+    """CVs (no ROOT) of the aligned groups of group_chunks chunks (64: the small-input leaf
+    with four lanes per chunk; 256, 512 or 1024) of the tensor's bytes, chunk counters
+    starting at chunk_base: a (groups, 8) int32 device tensor of little-endian words."""
     t = _device_bytes(t)
     nbytes = t.numel() * t.element_size()
     if nbytes == 0:

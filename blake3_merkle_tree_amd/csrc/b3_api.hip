@@ -359,7 +359,8 @@ int hash_xof(const void *in, uint64_t len, const uint32_t *key, uint64_t out_off
 int group_cvs(const void *in, uint64_t len, uint64_t chunk_base, const uint32_t *key, uint32_t group_chunks,
               void *out, void *stream) {
     if (out == nullptr || len == 0 || in == nullptr) return B3G_EINVAL;
-    if (group_chunks != kLeafLanes && group_chunks != 2 * kLeafLanes && group_chunks != 4 * kLeafLanes)
+    const bool quad = group_chunks == kQuadLeafChunks;
+    if (!quad && group_chunks != kLeafLanes && group_chunks != 2 * kLeafLanes && group_chunks != 4 * kLeafLanes)
         return B3G_EINVAL;
     if (reinterpret_cast<uintptr_t>(in) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
         return B3G_EALIGN;
@@ -382,8 +383,9 @@ int group_cvs(const void *in, uint64_t len, uint64_t chunk_base, const uint32_t 
     la.mode = key ? kKeyedHash : 0u;
     la.cv_out = static_cast<uint32_t *>(out);
     la.digests = nullptr;
-    return launched(launch_uniform_leaf(la, group_chunks / kLeafLanes, use_lds_staging(), la.groups,
-                                        static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (quad) return launched(launch_quad_leaf(la, la.groups, s));
+    return launched(launch_uniform_leaf(la, group_chunks / kLeafLanes, use_lds_staging(), la.groups, s));
 }
 
 template <class T>
@@ -525,7 +527,9 @@ int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, 
 }
 
 uint32_t blake3_gpu_leaf_group_chunks(uint64_t len) {
-    return b3g::kLeafLanes * b3g::choose_chunks_per_lane(b3g::chunks_of(len));
+    const uint64_t c = b3g::chunks_of(len);
+    if (c <= b3g::quad_leaf_max_chunks()) return b3g::kQuadLeafChunks;
+    return b3g::kLeafLanes * b3g::choose_chunks_per_lane(c);
 }
 
 const char *blake3_gpu_strerror(int status) {

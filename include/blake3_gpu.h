@@ -159,8 +159,9 @@ int blake3_gpu_hash_xof_at(const void *dev_in, uint64_t len, const uint32_t key[
  *   dev_in       device pointer, 16-byte aligned, len > 0 bytes.
  *   chunk_base   counter of the first chunk of dev_in.
  *   key          host pointer to 8 key words (keyed mode), or NULL (default mode).
- *   group_chunks 256, 512 or 1024 (blake3_gpu_leaf_group_chunks(len) is what the hash
- *                entry points use for an input of len bytes).
+ *   group_chunks 64 (four lanes per chunk, the small-input leaf), 256, 512 or 1024
+ *                (blake3_gpu_leaf_group_chunks(len) is what the hash entry points use for
+ *                an input of len bytes).
  *   dev_cvs      device pointer, 16-byte aligned, to ceil(ceil(len/1024)/group_chunks) * 32
  *                bytes; group g's CV (8 little-endian words) at byte 32*g.
  * Errors: EINVAL (NULL dev_in or dev_cvs, len == 0, other group_chunks, counter
@@ -169,8 +170,10 @@ int blake3_gpu_hash_xof_at(const void *dev_in, uint64_t len, const uint32_t key[
 int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, const uint32_t key[8],
                          uint32_t group_chunks, void *dev_cvs, void *stream);
 
-/* Chunks per leaf workgroup (256, 512 or 1024) that the hash entry points use for an
- * input of len bytes: larger inputs fold more chunks per lane before the workgroup tree. */
+/* Chunks per leaf workgroup that the hash entry points use for an input of len bytes: 64
+ * for inputs of at most 16384 chunks (four lanes per chunk; the environment variable
+ * BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS moves that bound), else 256, 512 or 1024 (larger
+ * inputs fold more chunks per lane before the workgroup tree). */
 uint32_t blake3_gpu_leaf_group_chunks(uint64_t len);
 
 /* Static, human-readable text for a b3g_status value (never NULL). */

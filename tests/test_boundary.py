@@ -81,6 +81,30 @@ def test_subtree_and_xof_argument_checks():
     assert lib.blake3_gpu_hash_xof_at(ALIGNED, 5, None, (1 << 64) - 1, None, 0, None) == b3.OK
 
 
+def test_group_cvs_argument_checks_and_leaf_group_size(monkeypatch):
+    lib = _lib()
+    lib.blake3_gpu_group_cvs.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
+                                         ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.blake3_gpu_leaf_group_chunks.argtypes = [ctypes.c_uint64]
+    lib.blake3_gpu_leaf_group_chunks.restype = ctypes.c_uint32
+    for g in (0, 32, 128, 2048):  # only 64 (quad leaf), 256, 512 and 1024 are workgroup sizes
+        assert lib.blake3_gpu_group_cvs(ALIGNED, 5000, 0, None, g, ALIGNED, None) == b3.EINVAL
+    for g in (64, 256, 512, 1024):
+        assert lib.blake3_gpu_group_cvs(ALIGNED, 0, 0, None, g, ALIGNED, None) == b3.EINVAL
+        assert lib.blake3_gpu_group_cvs(None, 5000, 0, None, g, ALIGNED, None) == b3.EINVAL
+        assert lib.blake3_gpu_group_cvs(ALIGNED, 5000, 0, None, g, None, None) == b3.EINVAL
+        assert lib.blake3_gpu_group_cvs(MISALIGNED, 5000, 0, None, g, ALIGNED, None) == b3.EALIGN
+    # what the hash entry points use: the quad leaf up to 16384 chunks, then 256 * K
+    monkeypatch.delenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", raising=False)
+    monkeypatch.delenv("BLAKE3_GPU_CHUNKS_PER_LANE", raising=False)
+    assert [lib.blake3_gpu_leaf_group_chunks(n) for n in
+            (0, 1 << 20, 16384 * 1024, 16384 * 1024 + 1, 256 << 20, 2 << 30, (4 << 30) + 1000)] == \
+        [64, 64, 64, 256, 256, 1024, 1024]
+    monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", "0")
+    assert lib.blake3_gpu_leaf_group_chunks(1 << 20) == 256
+    assert b3.leaf_group_chunks(1 << 20) == 256
+
+
 def test_batch_argument_checks():
     lib = _lib()
     offs = (ctypes.c_uint64 * 2)(0, 32)

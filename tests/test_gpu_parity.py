@@ -294,14 +294,15 @@ def test_workload_batch64k(b3, dev, monkeypatch):
 
 
 @pytest.mark.parametrize("staging", ["direct", "lds"])
-@pytest.mark.parametrize("group_chunks", [256, 512, 1024])
+@pytest.mark.parametrize("group_chunks", [64, 256, 512, 1024])
 def test_group_cvs_with_counter_offsets(b3, dev, monkeypatch, group_chunks, staging):
     monkeypatch.setenv("BLAKE3_GPU_STAGING", staging)
     # the leaf pass alone: one CV per aligned group, no ROOT; chunk_base above 2^32
-    # exercises the counter's high word
+    # exercises the counter's high word; 64-chunk groups run the quad leaf
     from blake3_merkle_tree_amd import workloads
     n_groups = 4
-    buf = workloads.random_bytes((n_groups - 1) * group_chunks * 1024 + 100 * 1024 + 77, 34, dev)
+    tail_kib = min(100, group_chunks - 27)  # the last group: a partial one, with a short last chunk
+    buf = workloads.random_bytes((n_groups - 1) * group_chunks * 1024 + tail_kib * 1024 + 77, 34, dev)
     host = _host(buf)
     key = bytes(workloads.key_bytes(35)[0].tolist())
     G = group_chunks * 1024
