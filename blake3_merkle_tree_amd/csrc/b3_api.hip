@@ -66,12 +66,18 @@ class StreamScratch {
     }
     int alloc(size_t bytes) {
         if (bytes == 0) return B3G_OK;
+        if (bytes > scratch_limit()) return B3G_ENOMEM;  // test hook: a forced allocation failure
         hipMemPool_t pool = device_pool();
         const hipError_t e = pool ? hipMallocFromPoolAsync(&p_, bytes, pool, s_) : hipMallocAsync(&p_, bytes, s_);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             p_ = nullptr;
             return B3G_ENOMEM;
+        }
+        const int fill = scratch_fill_byte();  // test hook: scratch of known, arbitrary contents
+        if (fill >= 0 && hipMemsetAsync(p_, fill, bytes, s_) != hipSuccess) {
+            (void)hipGetLastError();
+            return B3G_EHIP;
         }
         return B3G_OK;
     }

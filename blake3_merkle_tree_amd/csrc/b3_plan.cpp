@@ -89,6 +89,20 @@ uint64_t quad_leaf_max_chunks() {
     return kQuadLeafMaxChunksDefault;
 }
 
+uint64_t scratch_limit() {
+    const char *e = getenv("BLAKE3_GPU_SCRATCH_LIMIT");
+    if (e == nullptr || e[0] < '0' || e[0] > '9') return UINT64_MAX;
+    return strtoull(e, nullptr, 10);
+}
+
+int scratch_fill_byte() {
+    const char *e = getenv("BLAKE3_GPU_SCRATCH_FILL");
+    if (e == nullptr || e[0] == 0) return -1;
+    char *end = nullptr;
+    const long v = strtol(e, &end, 0);
+    return (*end == 0 && v >= 0 && v <= 255) ? static_cast<int>(v) : -1;
+}
+
 bool fused_levels_enabled() {
     // Off by default: measured on MI355X, the ticket zeroing launch and each workgroup's
     // wait for its coherent stores and ticket cost more than the level launches they

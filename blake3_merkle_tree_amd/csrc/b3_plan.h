@@ -75,6 +75,14 @@ uint64_t quad_leaf_max_chunks();
 // default). BLAKE3_GPU_FUSED_LEVELS=1 in the environment selects the fused form.
 bool fused_levels_enabled();
 
+// Test hooks for the scratch of a call (stream-ordered device memory). A request of more
+// than BLAKE3_GPU_SCRATCH_LIMIT bytes fails with B3G_ENOMEM before any HIP call, as an
+// allocation failure would; BLAKE3_GPU_SCRATCH_FILL=<byte> (0..255) fills new scratch
+// with that byte before the call's kernels run, so that tests can show that no result
+// depends on what the memory held before. Unset, neither changes anything.
+uint64_t scratch_limit();   // UINT64_MAX when unset
+int scratch_fill_byte();    // -1 when unset
+
 // Batches of equal lengths at evenly spaced offsets skip the planner (their geometry is
 // implied); BLAKE3_GPU_BATCH_TABLE=1 in the environment routes them through the task
 // table like any other batch (for tests).

@@ -128,6 +128,26 @@ def test_batch_argument_checks():
                                            None, ALIGNED, 2, None) == b3.EINVAL
 
 
+def test_forced_scratch_failure_returns_enomem_before_any_hip_call(monkeypatch):
+    # BLAKE3_GPU_SCRATCH_LIMIT caps a call's scratch request: every call that needs
+    # scratch fails with ENOMEM before its first HIP call (no device here, so any HIP
+    # call would fail with EHIP instead), launching nothing
+    lib = _lib()
+    monkeypatch.setenv("BLAKE3_GPU_SCRATCH_LIMIT", "0")
+    key = (ctypes.c_uint32 * 8)()
+    assert lib.blake3_gpu_hash(ALIGNED, 1 << 20, ALIGNED, None) == b3.ENOMEM  # leaf CVs + a level pass
+    assert lib.blake3_gpu_keyed_hash(ALIGNED, (4 << 30) + 1000, ctypes.addressof(key), ALIGNED, None) == b3.ENOMEM
+    offs = (ctypes.c_uint64 * 3)(0, 1 << 20, 3 << 20)
+    lens = (ctypes.c_uint64 * 3)(300 * 1024, 2 << 20, 5)  # not uniform: the task table path
+    assert lib.blake3_gpu_keyed_hash_batch(ALIGNED, ctypes.addressof(offs), ctypes.addressof(lens), None, ALIGNED,
+                                           3, None) == b3.ENOMEM
+    assert lib.blake3_gpu_hash_xof(ALIGNED, 1 << 20, None, ALIGNED, 64, None) == b3.ENOMEM
+    assert lib.blake3_gpu_subtree_cv(ALIGNED, 1 << 20, 0, None, ALIGNED, None) == b3.ENOMEM
+    monkeypatch.setenv("BLAKE3_GPU_SCRATCH_LIMIT", str(1 << 40))  # a limit no call reaches: no effect
+    monkeypatch.setenv("BLAKE3_GPU_SCRATCH_LIMIT", "")  # unset or empty: no limit
+    assert lib.blake3_gpu_hash(MISALIGNED, 1 << 20, ALIGNED, None) == b3.EALIGN  # checks come first
+
+
 def test_strerror_and_version():
     for code in (b3.OK, b3.EINVAL, b3.EALIGN, b3.ENOMEM, b3.EHIP, b3.ETOOBIG):
         assert b3.strerror(code) and b3.strerror(code) != "unknown status"

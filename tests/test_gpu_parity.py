@@ -408,6 +408,76 @@ def test_uniform_batches(b3, dev, monkeypatch, k, staging):
         monkeypatch.delenv("BLAKE3_GPU_BATCH_TABLE")
 
 
+# ---- scratch: allocation failure, prior contents, repeated runs ------------------------------
+
+def test_forced_allocation_failure_writes_nothing(b3, dev, monkeypatch):
+    # a call whose scratch cannot be had returns ENOMEM and launches nothing: its output
+    # keeps its prior contents; calls that need no scratch still run
+    from blake3_merkle_tree_amd import workloads
+    buf = workloads.random_bytes(1 << 20, 40, dev)
+    key = bytes(workloads.key_bytes(41)[0].tolist())
+    out = torch.full((32,), 0x5C, dtype=torch.uint8, device=dev)
+    monkeypatch.setenv("BLAKE3_GPU_SCRATCH_LIMIT", "0")
+    with pytest.raises(b3.Blake3GpuError) as err:
+        b3.keyed_hash(buf, key, out=out)
+    assert err.value.status == b3.ENOMEM
+    offs, lengths = [0, 300 * 1024], [300 * 1024, 700 * 1024]
+    outs = torch.full((2, 32), 0x5C, dtype=torch.uint8, device=dev)
+    with pytest.raises(b3.Blake3GpuError) as err:
+        b3.keyed_hash_batch(buf, offs, lengths, None, out=outs)
+    assert err.value.status == b3.ENOMEM
+    torch.cuda.synchronize()
+    assert out.eq(0x5C).all() and outs.eq(0x5C).all()
+    small = b3.keyed_hash(buf[:3000], key)  # three chunks: one leaf workgroup, no scratch
+    host = _host(buf)
+    assert bytes(small.cpu().tolist()) == oracle.hash(host[:3000].tobytes(), key)
+    monkeypatch.delenv("BLAKE3_GPU_SCRATCH_LIMIT")
+    b3.keyed_hash(buf, key, out=out)
+    assert bytes(out.cpu().tolist()) == oracle.hash(host.tobytes(), key)
+
+
+@pytest.mark.parametrize("fill", ["0x00", "0xA5", "0xFF"])
+def test_results_do_not_depend_on_scratch_contents(b3, dev, monkeypatch, fill):
+    # scratch filled with a known byte before every call's kernels: the level passes, the
+    # fused level tickets, split message ends and the XOF root inputs read only what the
+    # call wrote
+    monkeypatch.setenv("BLAKE3_GPU_SCRATCH_FILL", fill)
+    from blake3_merkle_tree_amd import workloads
+    size = 70100 * 1024 - 100
+    buf = workloads.random_bytes(size, 42, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(43)[0].tolist())
+    for L in (1 << 20, 300 * 1024 + 5, size):
+        for fused in ("0", "1"):
+            monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", fused)
+            _say("scratch fill", fill, "length", L, "fused", fused)
+            assert bytes(b3.keyed_hash(buf[:L], key).cpu().tolist()) == oracle.hash(host[:L].tobytes(), key)
+    monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", "0")
+    lengths = [456 * 1024 + 7, 813 * 1024, 1725 * 1024 + 11, 3000, 1, 200 * 1024 + 5]
+    offs, total = workloads.pack_messages(lengths)
+    out = b3.keyed_hash_batch(buf[:total], offs, lengths, None)
+    assert _digests_to_bytes(out) == oracle.hash_batch(host[:total], offs, lengths, None, nthreads=NTHREADS)
+    xof = b3.hash_xof(buf[:1 << 20], key, out_len=4096 + 17)
+    assert bytes(xof.cpu().tolist()) == oracle.hash_xof(host[:1 << 20].tobytes(), key, out_len=4096 + 17)
+
+
+def test_repeated_runs_give_identical_digests(b3, dev):
+    # determinism and race smoke test: the same calls, many times over, one result each
+    from blake3_merkle_tree_amd import workloads
+    buf = workloads.random_bytes(64 << 20, 44, dev)
+    key = bytes(workloads.key_bytes(45)[0].tolist())
+    outs = torch.empty((100, 32), dtype=torch.uint8, device=dev)
+    for i in range(100):
+        b3.keyed_hash(buf, key, out=outs[i])
+    assert outs.eq(outs[0]).all()
+    assert bytes(outs[0].cpu().tolist()) == oracle.hash(_host(buf).tobytes(), key)
+    base, offs, lengths, keys_cpu = workloads.ragged_batch(dev)
+    keys = keys_cpu.to(dev)
+    first = b3.keyed_hash_batch(base, offs, lengths, keys)
+    for _ in range(20):
+        assert torch.equal(b3.keyed_hash_batch(base, offs, lengths, keys), first)
+
+
 # ---- extendable output and subtree CVs ----------------------------------------------------
 
 XOF_LENGTHS = [0, 1, 63, 64, 65, 1023, 1024, 1025, 2048, 2049, 5 * 1024 + 7, 64 * 1024, 300 * 1024 + 9,
