@@ -15,6 +15,7 @@ A tensor is hashed as its raw bytes in memory order (a contiguous fp32 tensor as
 little-endian element bytes). There is no CPU fallback: if the library is missing or
 no HIP device is present the calls raise.
 """
+import contextlib
 import ctypes
 import os
 import struct
@@ -86,24 +87,33 @@ def _check(rc, where):
         raise Blake3GpuError(rc, where)
 
 
-def _device_bytes(t: torch.Tensor) -> torch.Tensor:
-    """The tensor's bytes as a contiguous, 16-byte-aligned device tensor (no copy if it
-    already is one)."""
+def _check_tensor(t, what="the tensor"):
     if not isinstance(t, torch.Tensor):
-        raise TypeError("expected a torch.Tensor")
+        raise TypeError(f"expected a torch.Tensor for {what}")
     if t.device.type != "cuda":
-        raise ValueError("the tensor must be on a HIP device")
+        raise ValueError(f"{what} must be on a HIP device")
+
+
+@contextlib.contextmanager
+def _on(device, stream):
+    """Device and stream of one call (stream None: the device's current stream); yields
+    the stream's handle. The copies and outputs the binding makes are made inside it, on
+    the call's stream, so that a copy is ordered before the kernels that read it and the
+    allocator reuses its memory only in that stream's order."""
+    with torch.cuda.device(device):
+        s = stream if stream is not None else torch.cuda.current_stream(device)
+        with torch.cuda.stream(s):
+            yield ctypes.c_void_p(s.cuda_stream)
+
+
+def _aligned(t: torch.Tensor) -> torch.Tensor:
+    """The tensor's bytes as a contiguous, 16-byte-aligned device tensor (no copy if it
+    already is one). Call inside _on."""
     if not t.is_contiguous():
         t = t.contiguous()
     if t.numel() and t.data_ptr() % 16 != 0:
         t = t.clone()  # fresh allocations are 256-byte aligned
     return t
-
-
-def _stream_handle(device, stream):
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
 
 
 def _key_words(key):
@@ -142,25 +152,27 @@ def _out(out, device, n):
 
 def hash(t: torch.Tensor, out=None, stream=None) -> torch.Tensor:  # noqa: A001
     """Default-mode BLAKE3 of the tensor's bytes; returns a 32-byte uint8 device tensor."""
-    t = _device_bytes(t)
-    out = _out(out, t.device, 32)
-    nbytes = t.numel() * t.element_size()
-    with torch.cuda.device(t.device):
+    _check_tensor(t)
+    with _on(t.device, stream) as sh:
+        t = _aligned(t)
+        out = _out(out, t.device, 32)
+        nbytes = t.numel() * t.element_size()
         rc = _load().blake3_gpu_hash(ctypes.c_void_p(t.data_ptr() if nbytes else 0), nbytes,
-                                     ctypes.c_void_p(out.data_ptr()), _stream_handle(t.device, stream))
+                                     ctypes.c_void_p(out.data_ptr()), sh)
     _check(rc, "blake3_gpu_hash")
     return out
 
 
 def keyed_hash(t: torch.Tensor, key, out=None, stream=None) -> torch.Tensor:
     """Keyed-mode BLAKE3 (key: 32 bytes) of the tensor's bytes; 32-byte device tensor."""
-    t = _device_bytes(t)
+    _check_tensor(t)
     kw = _key_words(key)
-    out = _out(out, t.device, 32)
-    nbytes = t.numel() * t.element_size()
-    with torch.cuda.device(t.device):
+    with _on(t.device, stream) as sh:
+        t = _aligned(t)
+        out = _out(out, t.device, 32)
+        nbytes = t.numel() * t.element_size()
         rc = _load().blake3_gpu_keyed_hash(ctypes.c_void_p(t.data_ptr() if nbytes else 0), nbytes, kw,
-                                           ctypes.c_void_p(out.data_ptr()), _stream_handle(t.device, stream))
+                                           ctypes.c_void_p(out.data_ptr()), sh)
     _check(rc, "blake3_gpu_keyed_hash")
     return out
 
@@ -170,7 +182,8 @@ def keyed_hash_batch(base: torch.Tensor, offsets, lengths, keys=None, out=None, 
     tensor's bytes, multiples of 16; offsets and lengths are sequences, numpy arrays or
     CPU tensors). keys: None (default mode) or a device tensor with 32 bytes per message,
     shape (n, 32) uint8 or (n, 8) int32. Returns (n, 32) uint8. Equal lengths at evenly
-    spaced offsets take a faster path that needs no launch table."""
+    spaced offsets take a faster path that needs no launch table. A base or keys tensor
+    that is not 16-byte aligned is copied first (on the call's stream)."""
     if not isinstance(base, torch.Tensor) or base.device.type != "cuda":
         raise ValueError("base must be a tensor on a HIP device")
     if not base.is_contiguous():
@@ -183,20 +196,19 @@ def keyed_hash_batch(base: torch.Tensor, offsets, lengths, keys=None, out=None, 
     nbytes = base.numel() * base.element_size()
     if n and bool(np.any((offs > nbytes) | (lens > nbytes - np.minimum(offs, nbytes)))):
         raise ValueError("a message runs past the end of base")
-    kp = ctypes.c_void_p(0)
     if keys is not None:
         if not isinstance(keys, torch.Tensor) or keys.device != base.device or not keys.is_contiguous():
             raise ValueError("keys must be a contiguous tensor on base's device")
         if keys.numel() * keys.element_size() != 32 * n:
             raise ValueError("keys must hold 32 bytes per message")
-        kp = ctypes.c_void_p(keys.data_ptr())
-    out = _out(out, base.device, 32 * n).view(n, 32) if n else torch.empty((0, 32), dtype=torch.uint8,
-                                                                           device=base.device)
-    with torch.cuda.device(base.device):
+    with _on(base.device, stream) as sh:
+        base = _aligned(base)
+        kp = ctypes.c_void_p(_aligned(keys).data_ptr() if keys is not None else 0)
+        out = _out(out, base.device, 32 * n).view(n, 32) if n else torch.empty((0, 32), dtype=torch.uint8,
+                                                                               device=base.device)
         rc = _load().blake3_gpu_keyed_hash_batch(ctypes.c_void_p(base.data_ptr() if nbytes else 0),
                                                  offs.ctypes.data, lens.ctypes.data,
-                                                 kp, ctypes.c_void_p(out.data_ptr()),
-                                                 n, _stream_handle(base.device, stream))
+                                                 kp, ctypes.c_void_p(out.data_ptr()), n, sh)
     _check(rc, "blake3_gpu_keyed_hash_batch")
     return out
 
@@ -205,17 +217,17 @@ def hash_xof(t: torch.Tensor, key=None, out_len: int = 32, out=None, stream=None
     """Extendable output: bytes [offset, offset + out_len) of the root node's output stream
     for the tensor's bytes (key: 32 bytes for keyed mode, None for default mode); a uint8
     device tensor. Bytes 0..31 of the stream are the hash."""
-    t = _device_bytes(t)
+    _check_tensor(t)
     out_len, offset = int(out_len), int(offset)
     if out_len < 0 or offset < 0:
         raise ValueError("out_len and offset must be non-negative")
-    out = _out(out, t.device, out_len)
     kw = _key_words(key) if key is not None else None
-    nbytes = t.numel() * t.element_size()
-    with torch.cuda.device(t.device):
+    with _on(t.device, stream) as sh:
+        t = _aligned(t)
+        out = _out(out, t.device, out_len)
+        nbytes = t.numel() * t.element_size()
         rc = _load().blake3_gpu_hash_xof_at(ctypes.c_void_p(t.data_ptr() if nbytes else 0), nbytes, kw, offset,
-                                            ctypes.c_void_p(out.data_ptr() if out_len else 0), out_len,
-                                            _stream_handle(t.device, stream))
+                                            ctypes.c_void_p(out.data_ptr() if out_len else 0), out_len, sh)
     _check(rc, "blake3_gpu_hash_xof_at")
     return out
 
@@ -223,17 +235,18 @@ def hash_xof(t: torch.Tensor, key=None, out_len: int = 32, out=None, stream=None
 def subtree_cv(t: torch.Tensor, key=None, chunk_base: int = 0, out=None, stream=None) -> torch.Tensor:
     """CV (no ROOT) of the subtree over all chunks of the tensor's bytes, chunk counters
     from chunk_base: an (8,) int32 device tensor of little-endian words."""
-    t = _device_bytes(t)
-    if out is None:
-        out = torch.empty(8, dtype=torch.int32, device=t.device)
-    elif out.device != t.device or out.numel() * out.element_size() != 32 or not out.is_contiguous():
+    _check_tensor(t)
+    if out is not None and (out.device != t.device or out.numel() * out.element_size() != 32
+                            or not out.is_contiguous()):
         raise ValueError("out must be a contiguous device tensor of 32 bytes")
     kw = _key_words(key) if key is not None else None
-    nbytes = t.numel() * t.element_size()
-    with torch.cuda.device(t.device):
+    with _on(t.device, stream) as sh:
+        t = _aligned(t)
+        if out is None:
+            out = torch.empty(8, dtype=torch.int32, device=t.device)
+        nbytes = t.numel() * t.element_size()
         rc = _load().blake3_gpu_subtree_cv(ctypes.c_void_p(t.data_ptr() if nbytes else 0), nbytes,
-                                           int(chunk_base), kw, ctypes.c_void_p(out.data_ptr()),
-                                           _stream_handle(t.device, stream))
+                                           int(chunk_base), kw, ctypes.c_void_p(out.data_ptr()), sh)
     _check(rc, "blake3_gpu_subtree_cv")
     return out
 
@@ -248,20 +261,21 @@ def group_cvs(t: torch.Tensor, key=None, chunk_base: int = 0, group_chunks: int 
     """CVs (no ROOT) of the aligned groups of group_chunks chunks (64: the small-input leaf
     with four lanes per chunk; 256, 512 or 1024) of the tensor's bytes, chunk counters
     starting at chunk_base: a (groups, 8) int32 device tensor of little-endian words."""
-    t = _device_bytes(t)
+    _check_tensor(t)
     nbytes = t.numel() * t.element_size()
     if nbytes == 0:
         raise ValueError("group_cvs needs at least one byte")
     groups = ((nbytes + 1023) // 1024 + group_chunks - 1) // group_chunks
-    if out is None:
-        out = torch.empty((groups, 8), dtype=torch.int32, device=t.device)
-    elif out.device != t.device or out.numel() * out.element_size() != 32 * groups or not out.is_contiguous():
+    if out is not None and (out.device != t.device or out.numel() * out.element_size() != 32 * groups
+                            or not out.is_contiguous()):
         raise ValueError(f"out must be a contiguous device tensor of {32 * groups} bytes")
     kw = _key_words(key) if key is not None else None
-    with torch.cuda.device(t.device):
+    with _on(t.device, stream) as sh:
+        t = _aligned(t)
+        if out is None:
+            out = torch.empty((groups, 8), dtype=torch.int32, device=t.device)
         rc = _load().blake3_gpu_group_cvs(ctypes.c_void_p(t.data_ptr()), nbytes, int(chunk_base), kw,
-                                          int(group_chunks), ctypes.c_void_p(out.data_ptr()),
-                                          _stream_handle(t.device, stream))
+                                          int(group_chunks), ctypes.c_void_p(out.data_ptr()), sh)
     _check(rc, "blake3_gpu_group_cvs")
     return out
 

@@ -404,6 +404,7 @@ int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *length
     if (n == 0) return B3G_OK;
     if (offsets == nullptr || lengths == nullptr || out == nullptr) return B3G_EINVAL;
     if (reinterpret_cast<uintptr_t>(base) % 16 != 0) return B3G_EALIGN;
+    if (reinterpret_cast<uintptr_t>(keys) % 16 != 0) return B3G_EALIGN;  // read as 16-byte words
     for (uint64_t i = 0; i < n; ++i) {
         if (offsets[i] % 16 != 0) return B3G_EALIGN;
         if (lengths[i] > kMaxMessageBytes) return B3G_ETOOBIG;

@@ -82,8 +82,8 @@ int blake3_gpu_keyed_hash(const void *dev_in, uint64_t len, const uint32_t key[8
  *   host_offsets  host array of n byte offsets, each a multiple of 16. Messages may be
  *                 in any order and may overlap (they are only read).
  *   host_lengths  host array of n byte counts (each 0 .. 2^42).
- *   dev_keys      device array of n*8 uint32 key words (message i's key at 8*i), or NULL
- *                 for default (unkeyed) mode for every message.
+ *   dev_keys      device array of n*8 uint32 key words (message i's key at 8*i), 16-byte
+ *                 aligned, or NULL for default (unkeyed) mode for every message.
  *   dev_out       device pointer to n*32 writable bytes; digest i at byte 32*i.
  *   n             message count (0 enqueues nothing and returns B3G_OK); at most 2^32-1
  *                 unless the batch is uniform (below).
@@ -93,7 +93,8 @@ int blake3_gpu_keyed_hash(const void *dev_in, uint64_t len, const uint32_t key[8
  * batch is planned on the host into a task table that is copied to device scratch in
  * stream order before the call returns. Both give the same digests.
  * Errors: EINVAL (NULL arrays with n > 0, NULL dev_out, NULL dev_base with a non-empty
- * message, offset + length overflowing 64 bits), EALIGN (misaligned dev_base or offset), ETOOBIG, ENOMEM, EHIP.
+ * message, offset + length overflowing 64 bits), EALIGN (misaligned dev_base, offset or
+ * dev_keys), ETOOBIG, ENOMEM, EHIP.
  */
 int blake3_gpu_keyed_hash_batch(const void *dev_base, const uint64_t *host_offsets,
                                 const uint64_t *host_lengths, const uint32_t *dev_keys, void *dev_out,

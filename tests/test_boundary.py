@@ -122,6 +122,8 @@ def test_batch_argument_checks():
     big = (ctypes.c_uint64 * 2)(10, (1 << 42) + 1)
     assert lib.blake3_gpu_keyed_hash_batch(ALIGNED, o, ctypes.addressof(big), None, ALIGNED, 2,
                                            None) == b3.ETOOBIG
+    # the key array is read with 16-byte loads: it must be 16-byte aligned
+    assert lib.blake3_gpu_keyed_hash_batch(ALIGNED, o, ln, ALIGNED + 4, ALIGNED, 2, None) == b3.EALIGN
     wrap_offs = (ctypes.c_uint64 * 2)(0, (1 << 64) - 16)
     wrap_lens = (ctypes.c_uint64 * 2)(10, 32)  # second message would wrap past 2^64
     assert lib.blake3_gpu_keyed_hash_batch(ALIGNED, ctypes.addressof(wrap_offs), ctypes.addressof(wrap_lens),

@@ -408,6 +408,36 @@ def test_uniform_batches(b3, dev, monkeypatch, k, staging):
         monkeypatch.delenv("BLAKE3_GPU_BATCH_TABLE")
 
 
+def test_copies_run_on_the_calls_stream(b3, dev):
+    # a misaligned input view and a misaligned key array are copied by the binding; the
+    # copies must run on the stream the hash runs on: with torch's current stream held busy
+    # by a bounded spin kernel, a copy made there would still be pending when a hash on the
+    # side stream read it
+    from blake3_merkle_tree_amd import workloads
+    buf = workloads.random_bytes((1 << 20) + 64, 46, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(47)[0].tolist())
+    view = buf[4:4 + (1 << 20)]
+    assert view.data_ptr() % 16 == 4
+    lengths = [300 * 1024, 700 * 1024 + 3]
+    offs = [0, 300 * 1024]
+    key_bytes = workloads.key_bytes(48, 2).to(dev)
+    raw = torch.empty(64 + 4, dtype=torch.uint8, device=dev)
+    keys_view = raw[4:]
+    keys_view.copy_(key_bytes.view(-1))
+    assert keys_view.data_ptr() % 16 == 4
+    side = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)  # the current stream is busy for tens of milliseconds
+    got = b3.keyed_hash(view, key, stream=side)
+    got_batch = b3.keyed_hash_batch(buf, offs, lengths, keys_view, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert bytes(got.cpu().tolist()) == oracle.hash(host[4:4 + (1 << 20)].tobytes(), key)
+    assert _digests_to_bytes(got_batch) == oracle.hash_batch(host, offs, lengths, key_bytes.cpu().numpy().tobytes(),
+                                                             nthreads=NTHREADS)
+
+
 # ---- scratch: allocation failure, prior contents, repeated runs ------------------------------
 
 def test_forced_allocation_failure_writes_nothing(b3, dev, monkeypatch):
