@@ -57,23 +57,61 @@ hipMemPool_t device_pool() {
     return g_pools[dev];
 }
 
-// Scratch of one call: allocated and released in stream order on the caller's stream.
+// Library-owned scratch slots, a few per device, each kept for the life of the process
+// and grown when a call needs more. A call takes a slot that no other host thread holds,
+// preferring one whose last use has finished on the device; its stream then waits on the
+// slot's event (a device-side wait: the host does not block), and when the call has
+// enqueued its work it records the slot's event on its stream. Calls on any streams thus
+// use the memory one after another in the order in which they took it, without a
+// stream-ordered allocation per call: such an allocation costs ~10 us of host time on an
+// idle stream and ~100 us or more on a stream held behind long work, where the pool cannot
+// reuse the block the same stream freed until the device has passed the free.
+constexpr int kSlotsPerDevice = 4;
+constexpr size_t kSlotMaxBytes = size_t(64) << 20;  // larger requests use the pool
+
+struct ScratchSlot {
+    void *p = nullptr;
+    size_t bytes = 0;
+    hipEvent_t done = nullptr;       // recorded after the work of the slot's last call
+    hipStream_t last = nullptr;      // that call's stream (a preference only: every reuse waits on done)
+    bool used = false;               // done has been recorded
+    bool held = false;               // taken by a call that has not yet returned
+};
+struct DeviceSlots {
+    std::mutex mu;
+    ScratchSlot slot[kSlotsPerDevice];
+};
+DeviceSlots g_slots[kMaxDevices];
+
+// Scratch of one call: a slot (above), or, for large requests or when every slot is held,
+// a stream-ordered allocation released in stream order on the caller's stream.
 class StreamScratch {
   public:
     explicit StreamScratch(hipStream_t s) : s_(s) {}
     ~StreamScratch() {
-        if (p_) (void)hipFreeAsync(p_, s_);
+        if (slot_ != nullptr) {
+            std::lock_guard<std::mutex> lock(slots_->mu);
+            if (hipEventRecord(slot_->done, s_) != hipSuccess) {
+                // the device could not be told when this call's work ends: never reuse the memory
+                (void)hipGetLastError();
+                slot_->p = nullptr;
+                slot_->bytes = 0;
+                slot_->used = false;
+            } else {
+                slot_->last = s_;
+                slot_->used = true;
+            }
+            slot_->held = false;
+        } else if (p_) {
+            (void)hipFreeAsync(p_, s_);
+        }
     }
     int alloc(size_t bytes) {
         if (bytes == 0) return B3G_OK;
         if (bytes > scratch_limit()) return B3G_ENOMEM;  // test hook: a forced allocation failure
-        hipMemPool_t pool = device_pool();
-        const hipError_t e = pool ? hipMallocFromPoolAsync(&p_, bytes, pool, s_) : hipMallocAsync(&p_, bytes, s_);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            p_ = nullptr;
-            return B3G_ENOMEM;
-        }
+        int rc = bytes <= kSlotMaxBytes ? take_slot(bytes) : B3G_ENOMEM;
+        if (rc != B3G_OK) rc = from_pool(bytes);
+        if (rc != B3G_OK) return rc;
         const int fill = scratch_fill_byte();  // test hook: scratch of known, arbitrary contents
         if (fill >= 0 && hipMemsetAsync(p_, fill, bytes, s_) != hipSuccess) {
             (void)hipGetLastError();
@@ -84,8 +122,98 @@ class StreamScratch {
     uint8_t *get() const { return static_cast<uint8_t *>(p_); }
 
   private:
+    int take_slot(size_t bytes) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+            (void)hipGetLastError();
+            return B3G_ENOMEM;
+        }
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s_, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
+            (void)hipGetLastError();
+            return B3G_ENOMEM;  // under graph capture: the stream-ordered pool, as recorded nodes
+        }
+        DeviceSlots &ds = g_slots[dev];
+        ScratchSlot *sl = nullptr;
+        bool wait = false;
+        {
+            std::lock_guard<std::mutex> lock(ds.mu);
+            // Preference: large enough and idle on the device (4); large enough and last used
+            // on this stream, so that waiting for it costs nothing (3); idle but too small, to
+            // be grown (2); large enough but in use on another stream, a device-side wait (1).
+            // A slot still in use and too small is never taken: growing it would block the host.
+            int best = -1, score = 0;
+            for (int i = 0; i < kSlotsPerDevice; ++i) {
+                ScratchSlot &c = ds.slot[i];
+                if (c.held) continue;
+                bool idle = !c.used;
+                if (!idle) {
+                    idle = hipEventQuery(c.done) == hipSuccess;
+                    if (!idle) (void)hipGetLastError();  // not ready yet
+                }
+                const bool fits = c.bytes >= bytes;
+                const int sc = fits ? (idle ? 4 : (c.last == s_ ? 3 : 1)) : (idle ? 2 : 0);
+                if (sc > score) {
+                    best = i;
+                    score = sc;
+                }
+            }
+            if (best < 0) return B3G_ENOMEM;  // the pool instead
+            sl = &ds.slot[best];
+            sl->held = true;
+            wait = sl->used && score != 4 && score != 2;
+        }
+        if (sl->done == nullptr && hipEventCreateWithFlags(&sl->done, hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
+            sl->done = nullptr;
+            return release_unused(ds, sl);
+        }
+        if (sl->bytes < bytes) {  // grow an idle slot (its last call's work has finished)
+            if (sl->p != nullptr && hipFree(sl->p) != hipSuccess) {
+                (void)hipGetLastError();
+                sl->p = nullptr;
+                sl->bytes = 0;
+                return release_unused(ds, sl);
+            }
+            sl->p = nullptr;
+            sl->bytes = 0;
+            size_t grown = size_t(1) << 20;
+            while (grown < bytes) grown <<= 1;
+            if (hipMalloc(&sl->p, grown) != hipSuccess) {
+                (void)hipGetLastError();
+                sl->p = nullptr;
+                return release_unused(ds, sl);
+            }
+            sl->bytes = grown;
+        } else if (wait && hipStreamWaitEvent(s_, sl->done, 0) != hipSuccess) {  // after its last call
+            (void)hipGetLastError();
+            return release_unused(ds, sl);
+        }
+        slot_ = sl;
+        slots_ = &ds;
+        p_ = sl->p;
+        return B3G_OK;
+    }
+    static int release_unused(DeviceSlots &ds, ScratchSlot *sl) {
+        std::lock_guard<std::mutex> lock(ds.mu);
+        sl->held = false;
+        return B3G_ENOMEM;
+    }
+    int from_pool(size_t bytes) {
+        hipMemPool_t pool = device_pool();
+        const hipError_t e = pool ? hipMallocFromPoolAsync(&p_, bytes, pool, s_) : hipMallocAsync(&p_, bytes, s_);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            p_ = nullptr;
+            return B3G_ENOMEM;
+        }
+        return B3G_OK;
+    }
+
     hipStream_t s_;
     void *p_ = nullptr;
+    ScratchSlot *slot_ = nullptr;
+    DeviceSlots *slots_ = nullptr;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }

@@ -20,9 +20,14 @@
  *    enqueued on it; no entry point synchronises the host with the device. A digest is
  *    in dev_out once the stream reaches that point; read it after a stream sync.
  *  - Scratch (chaining values of intermediate tree levels, the batch task table) is
- *    allocated and freed in stream order on `stream` from a memory pool the library
- *    creates once per device and keeps (freed blocks are reused by later calls). Each
- *    call owns its scratch, so calls on different streams may overlap.
+ *    library-owned device memory. Up to 64 MiB per call comes from a few slots per device
+ *    that the library allocates on first use, grows when needed and keeps for the life of
+ *    the process: a call makes `stream` wait (on the device, not the host) until the
+ *    slot's previous call has finished with it, and records its own completion for the
+ *    next. Larger requests, calls that find every slot in use by other host threads, and
+ *    calls on a stream under graph capture allocate and free their scratch in stream order
+ *    on `stream` from a memory pool the library keeps per device. Calls on different
+ *    streams and host threads may overlap; entry points are thread-safe.
  *  - Errors are returned as negative b3g_status values. Arguments are checked before any
  *    HIP call, so an argument error (EINVAL, EALIGN, ETOOBIG) enqueues nothing. ENOMEM and
  *    EHIP can come after part of the work was enqueued; the output is then unspecified.
@@ -44,7 +49,7 @@ typedef enum {
     B3G_OK = 0,
     B3G_EINVAL = -1,  /* a required pointer is NULL, or a batch offset + length overflows */
     B3G_EALIGN = -2,  /* dev_in / dev_base + offset is not 16-byte aligned */
-    B3G_ENOMEM = -3,  /* stream-ordered scratch allocation failed */
+    B3G_ENOMEM = -3,  /* scratch allocation failed */
     B3G_EHIP = -4,    /* a HIP runtime call or a kernel launch failed (incl. no device) */
     B3G_ETOOBIG = -5, /* the request exceeds what the planner represents (see below) */
 } b3g_status;

@@ -491,6 +491,63 @@ def test_results_do_not_depend_on_scratch_contents(b3, dev, monkeypatch, fill):
     assert bytes(xof.cpu().tolist()) == oracle.hash_xof(host[:1 << 20].tobytes(), key, out_len=4096 + 17)
 
 
+def test_calls_on_several_streams_threads_and_behind_a_busy_stream(b3, dev):
+    # the library's scratch slots are shared by calls on all streams and host threads:
+    # every call must still get its own digest
+    import threading
+    from blake3_merkle_tree_amd import workloads
+    sizes = [1 << 20, (3 << 20) + 5, 300 * 1024 + 5, 8 << 20]
+    bufs = [workloads.random_bytes(n, 60 + i, dev) for i, n in enumerate(sizes)]
+    key = bytes(workloads.key_bytes(64)[0].tolist())
+    want = [oracle.hash(_host(b).tobytes(), key) for b in bufs]
+    base, offs, lengths, keys_cpu = workloads.ragged_batch(dev)
+    keys = keys_cpu.to(dev)
+    want_batch = oracle.hash_batch(_host(base), offs, lengths, keys_cpu.numpy().tobytes(), nthreads=NTHREADS)
+    streams = [torch.cuda.Stream(dev) for _ in range(4)]
+    torch.cuda.synchronize()
+    _say("four streams, round robin, no host synchronisation")
+    outs = []
+    for r in range(6):
+        for i, st in enumerate(streams):
+            outs.append((i, b3.keyed_hash(bufs[i], key, stream=st)))
+        outs.append((-1, b3.keyed_hash_batch(base, offs, lengths, keys, stream=streams[r % 4])))
+    torch.cuda.synchronize()
+    for i, o in outs:
+        if i < 0:
+            assert _digests_to_bytes(o) == want_batch
+        else:
+            assert bytes(o.cpu().tolist()) == want[i], i
+    _say("four host threads, one stream each")
+    results, errors = {}, []
+
+    def work(i):
+        try:
+            with torch.cuda.device(dev):
+                res = [b3.keyed_hash(bufs[(i + r) % 4], key, stream=streams[i]) for r in range(8)]
+                streams[i].synchronize()
+                results[i] = [bytes(x.cpu().tolist()) for x in res]
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(4):
+        assert results[i] == [want[(i + r) % 4] for r in range(8)], i
+    _say("calls queued behind a busy stream")
+    st = streams[0]
+    with torch.cuda.stream(st):
+        torch.cuda._sleep(100_000_000)  # a bounded spin: the host runs far ahead of the device
+    queued = [b3.keyed_hash(bufs[r % 4], key, stream=st) for r in range(12)]
+    xof = b3.hash_xof(bufs[1], key, out_len=200, stream=st)
+    st.synchronize()
+    assert [bytes(o.cpu().tolist()) for o in queued] == [want[r % 4] for r in range(12)]
+    assert bytes(xof.cpu().tolist()) == oracle.hash_xof(_host(bufs[1]).tobytes(), key, out_len=200)
+
+
 def test_repeated_runs_give_identical_digests(b3, dev):
     # determinism and race smoke test: the same calls, many times over, one result each
     from blake3_merkle_tree_amd import workloads
