@@ -10,10 +10,16 @@ library's HIP kernels. The functions mirror the C entry points:
     hash_xof(t, key=None, out_len=32, offset=0) -> bytes [offset, offset + out_len) of the
                                          extended output
     subtree_cv(t, key=None, chunk_base=0) -> CV (no ROOT) of the tree over t's chunks
+    group_cvs(t, key=None, chunk_base=0, group_chunks=256) -> the leaf pass's group CVs
+    leaf_group_chunks(nbytes)            -> chunks per leaf workgroup the hashes use
 
-A tensor is hashed as its raw bytes in memory order (a contiguous fp32 tensor as its
-little-endian element bytes). There is no CPU fallback: if the library is missing or
-no HIP device is present the calls raise.
+Each of the device calls also takes out= (a preallocated contiguous device tensor of the
+result's size) and stream= (a torch.cuda.Stream; default: the device's current stream).
+All work, including the copy the binding makes of a non-contiguous or misaligned input,
+is enqueued on that stream and nothing waits for it: read a result after synchronising
+the stream. A tensor is hashed as its raw bytes in memory order (a contiguous fp32 tensor
+as its little-endian element bytes). There is no CPU fallback: if the library is missing
+or no HIP device is present the calls raise.
 """
 import contextlib
 import ctypes
