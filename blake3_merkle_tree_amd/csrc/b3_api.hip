@@ -1,5 +1,5 @@
 // b3_api.hip - the C ABI (include/blake3_gpu.h): argument checks, launch planning,
-// stream-ordered scratch, kernel launches.
+// scratch (library-owned slots, a stream-ordered pool), kernel launches.
 //
 // The chain of launches is the one of the page "BLAKE3 on GPU: 400x faster hashing"
 // (qfminer.top), sections "Our implementation" and "Kernels 2 and 3": a leaf pass that
@@ -20,7 +20,7 @@
 namespace b3g {
 namespace {
 
-constexpr int kAbiVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kAbiVersion = 1 * 10000 + 1 * 100 + 0;
 
 // Stream-ordered scratch comes from one memory pool per device, created on first use and
 // kept for the life of the process, with a release threshold of "never" so that freed
@@ -671,7 +671,7 @@ const char *blake3_gpu_strerror(int status) {
     switch (status) {
         case B3G_OK: return "success";
         case B3G_EINVAL: return "invalid argument (NULL pointer or offset overflow)";
-        case B3G_EALIGN: return "device input or batch offset is not 16-byte aligned";
+        case B3G_EALIGN: return "a device pointer or batch offset is not 16-byte aligned";
         case B3G_ENOMEM: return "scratch allocation failed";
         case B3G_EHIP: return "HIP runtime call or kernel launch failed";
         case B3G_ETOOBIG: return "request exceeds the supported size";

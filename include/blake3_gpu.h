@@ -48,7 +48,7 @@ extern "C" {
 typedef enum {
     B3G_OK = 0,
     B3G_EINVAL = -1,  /* a required pointer is NULL, or a batch offset + length overflows */
-    B3G_EALIGN = -2,  /* dev_in / dev_base + offset is not 16-byte aligned */
+    B3G_EALIGN = -2,  /* dev_in, dev_base + offset or dev_keys is not 16-byte aligned */
     B3G_ENOMEM = -3,  /* scratch allocation failed */
     B3G_EHIP = -4,    /* a HIP runtime call or a kernel launch failed (incl. no device) */
     B3G_ETOOBIG = -5, /* the request exceeds what the planner represents (see below) */
