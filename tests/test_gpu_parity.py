@@ -186,6 +186,49 @@ def test_batch_mixed_lengths_with_gaps(b3, dev):
     assert singles == _digests_to_bytes(b3.keyed_hash_batch(base, offs, lengths, keys.to(dev)))
 
 
+def test_random_batches_match_oracle(b3, dev, monkeypatch):
+    # seeded random batches through the task table: lengths mixing empty, sub-block,
+    # chunk-boundary, multi-workgroup and split-end messages, random 16-byte gaps, keyed
+    # and default mode, at one, two and four chunks per lane
+    from blake3_merkle_tree_amd import workloads
+    rng = np.random.Generator(np.random.PCG64(2024))
+
+    def length():
+        kind = rng.integers(0, 6)
+        if kind == 0:
+            return int(rng.integers(0, 65))
+        if kind == 1:
+            return int(rng.integers(1, 9)) * 1024 + int(rng.integers(-1, 2))
+        if kind == 2:
+            return int(rng.integers(0, 64 * 1024))
+        if kind == 3:  # a last leaf group of 129..255 chunks after whole groups: split ends
+            return (256 * int(rng.integers(1, 3)) + int(rng.integers(129, 256))) * 1024 - int(rng.integers(0, 1024))
+        if kind == 4:
+            return int(rng.integers(0, 600 * 1024))
+        return int(rng.integers(0, 3 << 20))
+
+    for trial in range(12):
+        monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", str((1, 2, 4)[trial % 3]))
+        n = int(rng.integers(1, 120))
+        lengths = [max(0, length()) for _ in range(n)]
+        offs, pos = [], 0
+        for L in lengths:
+            pos += 16 * int(rng.integers(0, 3))  # random gaps
+            offs.append(pos)
+            pos += (L + 15) // 16 * 16
+        base = torch.full((pos + 16,), 0xA5, dtype=torch.uint8, device=dev)
+        data = workloads.random_bytes(pos + 16, 70 + trial, dev)
+        for o, L in zip(offs, lengths):
+            base[o:o + L] = data[o:o + L]
+        host = _host(base)
+        keyed = trial % 2 == 0
+        keys = workloads.key_bytes(90 + trial, n)
+        _say("random batch", trial, "messages", n, "bytes", sum(lengths), "keyed", keyed)
+        out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev) if keyed else None)
+        want = oracle.hash_batch(host, offs, lengths, keys.numpy().tobytes() if keyed else None, nthreads=NTHREADS)
+        assert _digests_to_bytes(out) == want, (trial, n)
+
+
 @pytest.mark.parametrize("chunks_per_lane", ["1", "2", "4"])
 def test_batch_split_message_ends(b3, dev, monkeypatch, chunks_per_lane):
     # a message's last group of more than half a workgroup that is not a power of two is
