@@ -23,6 +23,7 @@ or no HIP device is present the calls raise.
 """
 import contextlib
 import ctypes
+import functools
 import os
 import struct
 
@@ -105,7 +106,11 @@ def _on(device, stream):
     """Device and stream of one call (stream None: the device's current stream); yields
     the stream's handle. The copies and outputs the binding makes are made inside it, on
     the call's stream, so that a copy is ordered before the kernels that read it and the
-    allocator reuses its memory only in that stream's order."""
+    allocator reuses its memory only in that stream's order. When the call runs on the
+    current device's current stream there is nothing to switch."""
+    if stream is None and device.index == torch.cuda.current_device():
+        yield ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+        return
     with torch.cuda.device(device):
         s = stream if stream is not None else torch.cuda.current_stream(device)
         with torch.cuda.stream(s):
@@ -128,6 +133,12 @@ def _key_words(key):
     key = bytes(key)
     if len(key) != 32:
         raise ValueError("BLAKE3 keys are 32 bytes")
+    return _words_of_key(key)
+
+
+@functools.lru_cache(maxsize=64)
+def _words_of_key(key: bytes):
+    # the C call reads the words during the call only, so one array can serve every call
     return (ctypes.c_uint32 * 8)(*struct.unpack("<8I", key))
 
 
@@ -200,8 +211,10 @@ def keyed_hash_batch(base: torch.Tensor, offsets, lengths, keys=None, out=None, 
     if len(lens) != n:
         raise ValueError("offsets and lengths differ in size")
     nbytes = base.numel() * base.element_size()
-    if n and bool(np.any((offs > nbytes) | (lens > nbytes - np.minimum(offs, nbytes)))):
-        raise ValueError("a message runs past the end of base")
+    if n:
+        ends = offs + lens  # uint64: a wrap shows as an end below its offset
+        if bool((ends < offs).any()) or int(ends.max()) > nbytes:
+            raise ValueError("a message runs past the end of base")
     if keys is not None:
         if not isinstance(keys, torch.Tensor) or keys.device != base.device or not keys.is_contiguous():
             raise ValueError("keys must be a contiguous tensor on base's device")

@@ -9,6 +9,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <memory>
 #include <mutex>
 #include <vector>
 
@@ -223,6 +224,150 @@ int launched(hipError_t e) {
     (void)hipGetLastError();
     return B3G_EHIP;
 }
+
+// Pinned host buffers for the batch task tables, up to 16 per device, allocated on first use
+// (coherent, device-visible), grown when needed and kept. A table is built in one and
+// uploaded by a copy kernel on the caller's stream, which reads it over the bus: the
+// kernels after it wait for nothing but the stream's order, where a copy-engine transfer
+// from pageable memory left ~18 us between a batch's launches. The buffer's event,
+// recorded after that kernel, must have completed before the host writes the buffer
+// again. A call that finds no such buffer free builds its table in pageable memory and
+// copies it with hipMemcpyAsync: the host never waits for the device here.
+constexpr int kStagesPerDevice = 16;
+constexpr size_t kStageArenaSlice = size_t(256) << 10;  // each buffer's first size, from one arena
+constexpr size_t kStageMaxBytes = size_t(64) << 20;
+
+struct HostStage {
+    void *p = nullptr;          // host address
+    void *dev = nullptr;        // the same memory as the device addresses it
+    size_t bytes = 0;
+    hipEvent_t done = nullptr;  // recorded after the last upload from this buffer
+    bool own = false;           // allocated on its own (else a slice of the arena)
+    bool used = false;
+    bool held = false;
+};
+struct DeviceStages {
+    std::mutex mu;
+    bool arena_tried = false;  // one pinned allocation for every buffer's first size: a pinned
+                               // allocation can wait for the device, so it is made once
+    HostStage stage[kStagesPerDevice];
+};
+DeviceStages g_stages[kMaxDevices];
+
+class TableStage {
+  public:
+    ~TableStage() {
+        if (st_ != nullptr) {
+            std::lock_guard<std::mutex> lock(ds_->mu);
+            st_->held = false;
+        }
+    }
+    // A pinned buffer of at least `bytes` that no upload still reads, or nullptr.
+    uint8_t *take(size_t bytes) {
+        int dev = 0;
+        if (bytes == 0 || bytes > kStageMaxBytes || hipGetDevice(&dev) != hipSuccess || dev < 0 ||
+            dev >= kMaxDevices) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        DeviceStages &ds = g_stages[dev];
+        HostStage *st = nullptr;
+        {
+            std::lock_guard<std::mutex> lock(ds.mu);
+            if (!ds.arena_tried) {
+                ds.arena_tried = true;
+                void *a = nullptr, *da = nullptr;
+                if (hipHostMalloc(&a, kStagesPerDevice * kStageArenaSlice, hipHostMallocCoherent) == hipSuccess &&
+                    hipHostGetDevicePointer(&da, a, 0) == hipSuccess && da != nullptr) {
+                    for (int i = 0; i < kStagesPerDevice; ++i) {
+                        ds.stage[i].p = static_cast<uint8_t *>(a) + i * kStageArenaSlice;
+                        ds.stage[i].dev = static_cast<uint8_t *>(da) + i * kStageArenaSlice;
+                        ds.stage[i].bytes = kStageArenaSlice;
+                    }
+                } else {
+                    (void)hipGetLastError();
+                    if (a != nullptr) (void)hipHostFree(a);
+                }
+            }
+            int best = -1;
+            for (int i = 0; i < kStagesPerDevice; ++i) {
+                HostStage &c = ds.stage[i];
+                if (c.held) continue;
+                if (c.used && hipEventQuery(c.done) != hipSuccess) {
+                    (void)hipGetLastError();  // an upload still reads it
+                    continue;
+                }
+                // idle: the smallest that fits, else the largest (to grow)
+                if (best < 0) {
+                    best = i;
+                    continue;
+                }
+                const HostStage &b = ds.stage[best];
+                const bool cf = c.bytes >= bytes, bf = b.bytes >= bytes;
+                if ((cf && (!bf || c.bytes < b.bytes)) || (!cf && !bf && c.bytes > b.bytes)) best = i;
+            }
+            if (best < 0) return nullptr;
+            st = &ds.stage[best];
+            st->held = true;
+        }
+        st_ = st;
+        ds_ = &ds;
+        if (st->done == nullptr && hipEventCreateWithFlags(&st->done, hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
+            st->done = nullptr;
+            return release();
+        }
+        if (st->bytes < bytes) {
+            if (st->own) (void)hipHostFree(st->p);  // idle: no upload reads it
+            st->p = st->dev = nullptr;
+            st->bytes = 0;
+            st->own = false;
+            size_t grown = kStageArenaSlice;
+            while (grown < bytes) grown <<= 1;
+            void *p = nullptr, *dp = nullptr;
+            if (hipHostMalloc(&p, grown, hipHostMallocCoherent) != hipSuccess) {
+                (void)hipGetLastError();
+                return release();
+            }
+            if (hipHostGetDevicePointer(&dp, p, 0) != hipSuccess || dp == nullptr) {
+                (void)hipGetLastError();
+                (void)hipHostFree(p);
+                return release();
+            }
+            st->p = p;
+            st->dev = dp;
+            st->bytes = grown;
+            st->own = true;
+        }
+        return static_cast<uint8_t *>(st->p);
+    }
+    // Uploads the first `bytes` (a multiple of 16) of the buffer to dst on s.
+    int upload(void *dst, size_t bytes, hipStream_t s) {
+        const int rc = launched(launch_copy_words16(st_->dev, dst, bytes / 16, s));
+        if (rc != B3G_OK) return rc;
+        std::lock_guard<std::mutex> lock(ds_->mu);
+        if (hipEventRecord(st_->done, s) == hipSuccess) {
+            st_->used = true;
+        } else {  // unknown when the upload ends: never write this buffer again
+            (void)hipGetLastError();
+            st_->p = st_->dev = nullptr;
+            st_->bytes = 0;
+            st_->own = false;
+            st_->used = false;
+        }
+        return B3G_OK;
+    }
+
+  private:
+    uint8_t *release() {
+        std::lock_guard<std::mutex> lock(ds_->mu);
+        st_->held = false;
+        st_ = nullptr;
+        return nullptr;
+    }
+    HostStage *st_ = nullptr;
+    DeviceStages *ds_ = nullptr;
+};
 
 uint32_t next_pow2_u32(uint64_t x) {
     uint32_t r = 1;
@@ -523,8 +668,8 @@ int group_cvs(const void *in, uint64_t len, uint64_t chunk_base, const uint32_t 
 }
 
 template <class T>
-void append_bytes(std::vector<uint8_t> &img, size_t at, const std::vector<T> &v) {
-    if (!v.empty()) memcpy(img.data() + at, v.data(), v.size() * sizeof(T));
+void copy_bytes(uint8_t *img, size_t at, const std::vector<T> &v) {
+    if (!v.empty()) memcpy(img + at, v.data(), v.size() * sizeof(T));
 }
 
 int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *lengths, const uint32_t *keys,
@@ -582,21 +727,35 @@ int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *length
         lay[p].cv_out = at;
         at += align256(plan.passes[p].out_cvs * 32);
     }
-    std::vector<uint8_t> img(table_bytes, 0);
-    memcpy(img.data() + msg_off_at, offsets, n * 8);
-    memcpy(img.data() + msg_len_at, lengths, n * 8);
-    for (size_t p = 0; p < plan.passes.size(); ++p) {
-        append_bytes(img, lay[p].segs, plan.passes[p].segs);
-        append_bytes(img, lay[p].first, plan.passes[p].wg_first_seg);
-        append_bytes(img, lay[p].levels, plan.passes[p].wg_levels);
-    }
-
     StreamScratch scratch(s);
     rc = scratch.alloc(at);
     if (rc != B3G_OK) return rc;
     uint8_t *d = scratch.get();
-    if (hipMemcpyAsync(d, img.data(), table_bytes, hipMemcpyHostToDevice, s) != hipSuccess)
+
+    // the table image (the alignment padding between its parts is never read and left as
+    // it is): in a pinned buffer, uploaded by a copy kernel, when one is free; else in
+    // pageable memory, copied by the runtime
+    TableStage stage;
+    std::unique_ptr<uint8_t[]> pageable;
+    uint8_t *img = stage.take(table_bytes);
+    const bool pinned = img != nullptr;
+    if (!pinned) {
+        pageable.reset(new uint8_t[table_bytes]);
+        img = pageable.get();
+    }
+    memcpy(img + msg_off_at, offsets, n * 8);
+    memcpy(img + msg_len_at, lengths, n * 8);
+    for (size_t p = 0; p < plan.passes.size(); ++p) {
+        copy_bytes(img, lay[p].segs, plan.passes[p].segs);
+        copy_bytes(img, lay[p].first, plan.passes[p].wg_first_seg);
+        copy_bytes(img, lay[p].levels, plan.passes[p].wg_levels);
+    }
+    if (pinned) {
+        rc = stage.upload(d, table_bytes, s);
+        if (rc != B3G_OK) return rc;
+    } else if (hipMemcpyAsync(d, img, table_bytes, hipMemcpyHostToDevice, s) != hipSuccess) {
         return launched(hipErrorUnknown);
+    }
 
     for (size_t p = 0; p < plan.passes.size(); ++p) {
         const PassPlan &pp = plan.passes[p];

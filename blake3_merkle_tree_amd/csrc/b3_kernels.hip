@@ -1161,6 +1161,24 @@ __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
 
 }  // namespace
 
+// dst[i] = src[i] for n 16-byte words: the upload of a batch's task table from pinned host
+// memory, as a kernel on the caller's stream, so that the kernels after it wait only for
+// the stream's own order (a copy-engine transfer costs a wait across engines).
+__global__ __launch_bounds__(256) void copy_words16_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                           uint64_t n) {
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<uint64_t>(gridDim.x) * 256)
+        dst[i] = src[i];
+}
+
+hipError_t launch_copy_words16(const void *src, void *dst, uint64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const uint64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(copy_words16_kernel, dim3(blocks < 512 ? static_cast<uint32_t>(blocks) : 512u), dim3(256), 0,
+                       s, static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n);
+    return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *p, uint64_t n) {
     for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
          i += static_cast<uint64_t>(gridDim.x) * 256)

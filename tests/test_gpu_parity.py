@@ -586,9 +586,13 @@ def test_calls_on_several_streams_threads_and_behind_a_busy_stream(b3, dev):
         torch.cuda._sleep(100_000_000)  # a bounded spin: the host runs far ahead of the device
     queued = [b3.keyed_hash(bufs[r % 4], key, stream=st) for r in range(12)]
     xof = b3.hash_xof(bufs[1], key, out_len=200, stream=st)
+    # more batches than the library keeps pinned table buffers: the later ones are built
+    # while the earlier tables still wait to be uploaded
+    batches = [b3.keyed_hash_batch(base, offs, lengths, keys, stream=st) for _ in range(8)]
     st.synchronize()
     assert [bytes(o.cpu().tolist()) for o in queued] == [want[r % 4] for r in range(12)]
     assert bytes(xof.cpu().tolist()) == oracle.hash_xof(_host(bufs[1]).tobytes(), key, out_len=200)
+    assert all(_digests_to_bytes(o) == want_batch for o in batches)
 
 
 def test_repeated_runs_give_identical_digests(b3, dev):
