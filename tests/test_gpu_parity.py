@@ -566,9 +566,15 @@ def test_calls_on_several_streams_threads_and_behind_a_busy_stream(b3, dev):
     def work(i):
         try:
             with torch.cuda.device(dev):
-                res = [b3.keyed_hash(bufs[(i + r) % 4], key, stream=streams[i]) for r in range(8)]
+                res, batches = [], []
+                for r in range(8):  # single hashes (scratch slots) and batches (slots and table buffers)
+                    res.append(b3.keyed_hash(bufs[(i + r) % 4], key, stream=streams[i]))
+                    if r % 2 == i % 2:
+                        batches.append(b3.keyed_hash_batch(base, offs, lengths, keys, stream=streams[i]))
                 streams[i].synchronize()
                 results[i] = [bytes(x.cpu().tolist()) for x in res]
+                if not all(_digests_to_bytes(o) == want_batch for o in batches):
+                    errors.append(AssertionError(f"thread {i}: a batch digest differs"))
         except Exception as e:  # reported below
             errors.append(e)
 
