@@ -29,6 +29,8 @@
 
 #include <stdlib.h>
 
+#include <memory>
+
 
 namespace b3g {
 
@@ -130,17 +132,23 @@ int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_
     out->passes.clear();
     if (n == 0) return kOk;
     if (n >= (1ull << 32)) return kTooBig;
-    // nodes[i]: node count of message i entering the current pass (0 once finished)
-    std::vector<uint64_t> nodes(n);
+    // The messages still open entering a pass, in message order; each pass keeps, in place,
+    // those that go on to the next.
+    struct Open {
+        uint64_t nodes;     // units entering the pass (chunks in pass 0, CVs after)
+        uint64_t in_base;   // where its input CVs start in the pass's input array
+        uint64_t out_base;  // where its output CVs start in the pass's output array
+        uint32_t msg;
+        bool pair_end;      // its last node in this pass is the parent of its last two input CVs
+        bool split;         // its end is split in this pass
+    };
+    std::unique_ptr<Open[]> open(new Open[n]);
+    uint64_t n_open = n;
     for (uint64_t i = 0; i < n; ++i) {
         if (lengths[i] > kMaxMessageBytes) return kTooBig;
-        nodes[i] = chunks_of(lengths[i]);
+        open[i] = Open{chunks_of(lengths[i]), 0, 0, static_cast<uint32_t>(i), false, false};
     }
-    // in_base[i]: where message i's input CVs start in the current pass's input array;
-    // pair_end[i]: its last node in this pass is the parent of its last two input CVs
-    std::vector<uint64_t> in_base(n, 0), out_base(n, 0);
-    std::vector<uint8_t> pair_end(n, 0), split(n, 0);
-    for (uint32_t pass = 0;; ++pass) {
+    for (uint32_t pass = 0; n_open > 0; ++pass) {
         // a pass-0 node is a lane's run of chunks_per_lane chunks; later nodes are CVs
         const uint64_t per_node = pass == 0 ? chunks_per_lane : 1;
         const uint64_t lanes = pass == 0 ? leaf_lanes : level_lanes;
@@ -151,22 +159,20 @@ int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_
         // groups per bucket (bucket b: groups of 2^b lanes) and each message's output CVs
         uint64_t bucket_n[kMaxBuckets] = {};
         uint64_t out_cvs = 0;
-        for (uint64_t i = 0; i < n; ++i) {
-            if (nodes[i] == 0) continue;
+        for (uint64_t j = 0; j < n_open; ++j) {
+            Open &m = open[j];
             bool sp = false, final = false;
-            for_each_group(nodes[i], pass == 0 ? 0 : in_base[i], node_shift, span_shift, lanes, may_split,
-                           pair_end[i] != 0, &sp,
+            for_each_group(m.nodes, m.in_base, node_shift, span_shift, lanes, may_split, m.pair_end, &sp,
                            [&](uint64_t, uint64_t, uint32_t b, uint64_t, bool fin, bool) {
                                ++bucket_n[b];
                                final = fin;
                            });
-            split[i] = sp;
-            out_base[i] = out_cvs;
-            if (!final) out_cvs += ((nodes[i] + (1ull << span_shift) - 1) >> span_shift) + (sp ? 1 : 0);
+            m.split = sp;
+            m.out_base = out_cvs;
+            if (!final) out_cvs += ((m.nodes + (1ull << span_shift) - 1) >> span_shift) + (sp ? 1 : 0);
         }
         uint64_t total = 0;
         for (uint32_t b = 0; b <= top; ++b) total += bucket_n[b];
-        if (total == 0) break;
         if (total >= (1ull << 32) || out_cvs >= (1ull << 32)) return kTooBig;
         // bucket layout, largest groups first: first task entry and first lane position
         uint64_t seg_at[kMaxBuckets], lane_at[kMaxBuckets], seg_pos = 0, lane_pos = 0;
@@ -195,37 +201,32 @@ int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_
             }
         }
         p.wg_first_seg.push_back(static_cast<uint32_t>(total));
-        // task entries in place
+        // task entries in place; the messages that go on move to the front of `open`
         p.segs.resize(total);
         Seg *segs = p.segs.data();
         bool too_big = false;  // a unit index past 32 bits
-        for (uint64_t i = 0; i < n; ++i) {
-            if (nodes[i] == 0) continue;
-            const uint64_t base = out_base[i];
+        uint64_t kept = 0;
+        for (uint64_t j = 0; j < n_open; ++j) {
+            const Open m = open[j];
             bool sp = false;
-            for_each_group(nodes[i], pass == 0 ? 0 : in_base[i], node_shift, span_shift, lanes, may_split,
-                           pair_end[i] != 0, &sp,
+            for_each_group(m.nodes, m.in_base, node_shift, span_shift, lanes, may_split, m.pair_end, &sp,
                            [&](uint64_t first, uint64_t count, uint32_t b, uint64_t k, bool fin, bool pair) {
                                const uint64_t lane = lane_at[b];
                                lane_at[b] += 1ull << b;
                                too_big |= first >= (1ull << 32);
                                segs[seg_at[b]++] =
-                                   Seg{static_cast<uint32_t>(i), static_cast<uint32_t>(first),
-                                       fin ? 0u : static_cast<uint32_t>(base + k),
+                                   Seg{m.msg, static_cast<uint32_t>(first),
+                                       fin ? 0u : static_cast<uint32_t>(m.out_base + k),
                                        seg_info(static_cast<uint32_t>(lane & (lanes - 1)),
                                                 static_cast<uint32_t>(count), fin, pair)};
                            });
+            // next pass: a message's nodes are its groups (a split end counts once)
+            const uint64_t ngroups = (m.nodes + (1ull << span_shift) - 1) >> span_shift;
+            if (ngroups > 1) open[kept++] = Open{ngroups, m.out_base, 0, m.msg, m.split, false};
         }
         if (too_big) return kTooBig;
-        // next pass: a message's nodes are its groups (a split end counts once)
-        for (uint64_t i = 0; i < n; ++i) {
-            if (nodes[i] == 0) continue;
-            const uint64_t ngroups = (nodes[i] + (1ull << span_shift) - 1) >> span_shift;
-            nodes[i] = ngroups == 1 ? 0 : ngroups;
-        }
+        n_open = kept;
         out->passes.push_back(std::move(p));
-        in_base.swap(out_base);
-        pair_end.swap(split);
     }
     return kOk;
 }
