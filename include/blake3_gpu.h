@@ -18,7 +18,9 @@
  *    library never frees or retains them after the call returns.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). All work is
  *    enqueued on it; no entry point synchronises the host with the device. A digest is
- *    in dev_out once the stream reaches that point; read it after a stream sync.
+ *    in dev_out once the stream reaches that point; read it after a stream sync. The
+ *    stream and the dev_* buffers belong to the current device (hipSetDevice): scratch is
+ *    taken on the current device.
  *  - Scratch (chaining values of intermediate tree levels, the batch task table) is
  *    library-owned device memory. Up to 64 MiB per call comes from a few slots per device
  *    that the library allocates on first use, grows when needed and keeps for the life of
