@@ -4,8 +4,11 @@ The HIP path is called through the C ABI (via the thin binding); the oracle hash
 copy of the same device bytes. Cases: brute force over chunk counts and tail lengths
 (partial blocks, single-chunk roots, non-power-of-two trees, workgroup and level
 boundaries), the empty input, misaligned views, non-default streams, batches with gap
-bytes of 0xA5 between messages (an over-read changes the digest), and every workload at
-full size in the launch configuration the benchmark times.
+bytes of 0xA5 between messages (an over-read changes the digest), split message ends and
+seeded random batches, every workload at full size in the launch configuration the
+benchmark times, extended output and subtree CVs, and the library's scratch: a forced
+allocation failure, scratch of arbitrary prior contents, repeated runs, and calls shared
+between streams, host threads and a stream held behind long work.
 """
 import os
 
