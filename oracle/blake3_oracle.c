@@ -23,9 +23,11 @@
  * Python's hashlib.blake2s; the two tree-shape rules and the page's 13 = 8+4+1 example
  * ("Merkle tree reduction"); recursive form == stack-merge form == incremental form ==
  * multi-threaded form. The message permutation, flag values and the counter/length/flag
- * words of the state are fixed only by the specification text; where an independent
- * BLAKE3 is importable the tests cross-check the whole hash against it, otherwise those
- * parts are "parity unpinned" (stated in the test module header).
+ * words of the state are fixed by the keyed-hash cross-check against an independent
+ * BLAKE3 (the Xet client library's). The extended output (tests/test_oracle_xof.py) is
+ * tied to the digest, and each of its 64-byte blocks must invert, through the test's own
+ * inverse rounds, to the root node's input state with its block counter. Default mode's
+ * flag value 0 rests on the specification text alone: "parity unpinned".
  *
  * The form here follows the definitions literally: no SIMD, no blocking, no fusion.
  */
