@@ -556,8 +556,10 @@ __device__ __forceinline__ void compress_quad_lds(uint32_t &a, uint32_t &b, uint
 }
 
 // Output nodes per level up to which a level runs on quads (four lanes per node): at
-// most 32 nodes would fill half a wave or less at one lane per node.
-constexpr uint32_t kQuadLevelNodes = 32;
+// most 64 nodes would fill one wave or less at one lane per node, where on quads they
+// fill up to four waves (one per SIMD of a 256-lane workgroup) and each node's
+// compression has a quarter of the dependent chain.
+constexpr uint32_t kQuadLevelNodes = 64;
 
 // Levels l of a tree over `used` node positions with more than kQuadLevelNodes output
 // positions (these run one lane per node).
