@@ -57,6 +57,13 @@ def chunks_per_lane(request, monkeypatch):
 
 @pytest.mark.parametrize("lengths", LENGTH_SETS)
 def test_plan_invariants(lengths, chunks_per_lane):
+    splits = _check_plan(lengths, chunks_per_lane)
+    if lengths == LENGTH_SETS[-2]:
+        assert splits >= 1, "this set splits a message end at every chunks-per-lane setting"
+
+
+def _check_plan(lengths, chunks_per_lane):
+    """Asserts the plan's structural invariants; returns the number of split message ends."""
     plan = b3.debug_plan_batch(lengths)
     n = len(lengths)
     finals = [0] * n
@@ -132,8 +139,7 @@ def test_plan_invariants(lengths, chunks_per_lane):
         units = {msg: len(v) for msg, v in next_inputs.items()}
         inputs = next_inputs
     assert finals == [1] * n, "every message is finished exactly once"
-    if lengths == LENGTH_SETS[-2]:
-        assert splits >= 1, "this set splits a message end at every chunks-per-lane setting"
+    return splits
 
 
 def _pair_reduce(nodes, kw, mode, final):
@@ -238,3 +244,53 @@ def test_chunks_per_lane_choice(monkeypatch):
     assert all(k in (1, 2, 4) for k in ks)
     monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", "2")
     assert b3.debug_plan_batch([1 << 20])[0]["chunks_per_lane"] == 2
+
+
+# ---- property-based sweep: random mixes of lengths --------------------------------------
+#
+# Lengths near chunk and workgroup boundaries, small and large, in random mixes; seeded
+# (derandomized) so that every run checks the same cases, and with no example database
+# written to disk.
+
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+_NEAR = st.sampled_from([1024, 64 * 1024, 128 * 1024, 256 * 1024, 512 * 1024, 1024 * 1024])
+
+
+def _length(max_bytes):
+    return st.one_of(
+        st.integers(0, 4096),
+        st.builds(lambda b, k, d: max(0, min(max_bytes, b * k + d)), _NEAR, st.integers(1, 8),
+                  st.sampled_from([-1, 0, 1, 17])),
+        st.integers(0, max_bytes),
+    )
+
+
+_SWEEP = settings(max_examples=120, derandomize=True, database=None, deadline=None,
+                  suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+
+
+@_SWEEP
+@given(lengths=st.lists(_length(96 * 1024 * 1024), min_size=1, max_size=300),
+       k=st.sampled_from([1, 2, 4]))
+def test_plan_invariants_on_random_mixes(lengths, k, monkeypatch):
+    monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", str(k))
+    _check_plan(lengths, k)
+
+
+@settings(max_examples=25, derandomize=True, database=None, deadline=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+@given(lengths=st.lists(_length(1100 * 1024), min_size=1, max_size=12),
+       k=st.sampled_from([1, 2, 4]), keyed=st.booleans(), seed=st.integers(0, 2**32 - 1))
+def test_executed_plan_matches_oracle_on_random_mixes(lengths, k, keyed, seed, monkeypatch):
+    monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", str(k))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    offsets, pos = [], 0
+    for L in lengths:
+        offsets.append(pos)
+        pos += (L + 31) // 16 * 16
+    data = rng.bytes(pos)
+    keys = [rng.bytes(32) for _ in lengths] if keyed else None
+    got = _execute_plan(data, offsets, lengths, keys)
+    for i, (o, L) in enumerate(zip(offsets, lengths)):
+        assert got[i] == oracle.hash(data[o:o + L], keys[i] if keys else None), (i, L)
