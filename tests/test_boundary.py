@@ -166,3 +166,15 @@ def test_python_binding_rejects_host_tensors_and_bad_keys():
         b3._key_words(b"short")
     with pytest.raises(ValueError):
         b3.keyed_hash_batch(torch.zeros(16, dtype=torch.uint8), [0], [16])
+
+
+def test_missing_library_raises_and_nothing_falls_back(monkeypatch, tmp_path):
+    # the binding has no CPU path: with its library absent, every call that would reach the
+    # library raises ImportError rather than computing anything another way
+    monkeypatch.setattr(b3, "_LIB_PATH", str(tmp_path / "libblake3_gpu.so"))
+    monkeypatch.setattr(b3, "_lib", None)
+    calls = [lambda: b3.version(), lambda: b3.strerror(0), lambda: b3.leaf_group_chunks(1 << 20),
+             lambda: b3.debug_plan_batch([1024, 5])]
+    for call in calls:
+        with pytest.raises(ImportError, match="is not built"):
+            call()
