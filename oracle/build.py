@@ -1,6 +1,6 @@
 """Compile the CPU oracle (oracle/blake3_oracle.c) into oracle/_b3oracle.so with gcc.
 
-Test infrastructure only: the oracle is the checker, never part of the product path.
+Test infrastructure only: the oracle verifies results and is never part of the product path.
 """
 import os
 import subprocess
