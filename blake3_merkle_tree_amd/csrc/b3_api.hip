@@ -434,7 +434,10 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
 
     // case B: G = ceil(c / span) leaf workgroups per message
     const uint64_t g = (c + span - 1) / span;
-    const uint64_t per_launch = kMaxGrid / g;  // >= 1: g <= 2^32 / 256
+    // one message's workgroups go in one launch; at 2^42 bytes and 256 or more chunks per
+    // workgroup g is at most 2^24 - 2^16, but a quad leaf forced onto a huge input is not
+    if (g > kMaxGrid) return B3G_ETOOBIG;
+    const uint64_t per_launch = kMaxGrid / g;  // >= 1
     const uint64_t nb = n_msgs < per_launch ? n_msgs : per_launch;
     const uint64_t g1 = (g + kLevelLanes - 1) / kLevelLanes;
     StreamScratch scratch(s);

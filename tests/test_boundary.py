@@ -178,3 +178,14 @@ def test_missing_library_raises_and_nothing_falls_back(monkeypatch, tmp_path):
     for call in calls:
         with pytest.raises(ImportError, match="is not built"):
             call()
+
+
+def test_more_leaf_workgroups_than_one_grid_is_too_big(monkeypatch):
+    # a quad leaf (64 chunks per workgroup) forced onto 2^42 bytes would need 2^26 workgroups
+    # for one message, more than one launch holds: the call refuses before any HIP call
+    # (the pointers are never dereferenced)
+    monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", str(1 << 40))
+    lib = b3._load()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.blake3_gpu_hash(fake, 1 << 42, fake, None) == b3.ETOOBIG
+    monkeypatch.delenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS")
