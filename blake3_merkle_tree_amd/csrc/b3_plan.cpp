@@ -183,7 +183,8 @@ int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_
             lane_pos += bucket_n[b] << b;
         }
         const uint64_t workgroups = (lane_pos + lanes - 1) >> top;
-        if (workgroups >= (1ull << 31)) return kTooBig;
+        // one launch per pass, and a launch holds at most 2^32 - 1 work-items
+        if (workgroups > 0xFFFFFFFFull / lanes) return kTooBig;
         PassPlan p;
         p.lanes = static_cast<uint32_t>(lanes);
         p.chunks_per_lane = static_cast<uint32_t>(per_node);

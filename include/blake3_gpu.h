@@ -101,7 +101,9 @@ int blake3_gpu_keyed_hash(const void *dev_in, uint64_t len, const uint32_t key[8
  * stream order before the call returns. Both give the same digests.
  * Errors: EINVAL (NULL arrays with n > 0, NULL dev_out, NULL dev_base with a non-empty
  * message, offset + length overflowing 64 bits), EALIGN (misaligned dev_base, offset or
- * dev_keys), ETOOBIG, ENOMEM, EHIP.
+ * dev_keys), ETOOBIG (a length above 2^42, or a planned pass of more workgroups than one
+ * launch holds: 2^24 - 1 of 256 lanes, reached only by a table-planned batch of about
+ * 16 TiB of message bytes, overlapping messages counted each time), ENOMEM, EHIP.
  */
 int blake3_gpu_keyed_hash_batch(const void *dev_base, const uint64_t *host_offsets,
                                 const uint64_t *host_lengths, const uint32_t *dev_keys, void *dev_out,

@@ -294,3 +294,12 @@ def test_executed_plan_matches_oracle_on_random_mixes(lengths, k, keyed, seed, m
     got = _execute_plan(data, offsets, lengths, keys)
     for i, (o, L) in enumerate(zip(offsets, lengths)):
         assert got[i] == oracle.hash(data[o:o + L], keys[i] if keys else None), (i, L)
+
+
+def test_a_pass_beyond_one_launch_is_too_big(monkeypatch):
+    # five messages of 2^42 bytes at four chunks per lane: 5 * 2^22 leaf workgroups of 256
+    # lanes, more than the 2^32 - 1 work-items of one launch (refused before any table is built)
+    monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", "4")
+    with pytest.raises(b3.Blake3GpuError) as err:
+        b3.debug_plan_batch([1 << 42] * 5)
+    assert err.value.status == b3.ETOOBIG
