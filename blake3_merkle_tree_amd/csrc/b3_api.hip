@@ -657,7 +657,9 @@ int group_cvs(const void *in, uint64_t len, uint64_t chunk_base, const uint32_t 
     la.chunk_base = chunk_base;
     la.n_msgs = 1;
     la.lanes_per_msg = 0;
-    la.groups = static_cast<uint32_t>((n + group_chunks - 1) / group_chunks);
+    const uint64_t groups = (n + group_chunks - 1) / group_chunks;
+    if (groups > kMaxGrid) return B3G_ETOOBIG;  // one launch: at most 2^32 - 1 work-items
+    la.groups = static_cast<uint32_t>(groups);
     la.may_root = 0;
     la.keys = nullptr;
     if (key) memcpy(la.key, key, sizeof(la.key));

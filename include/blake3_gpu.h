@@ -175,7 +175,9 @@ int blake3_gpu_hash_xof_at(const void *dev_in, uint64_t len, const uint32_t key[
  *   dev_cvs      device pointer, 16-byte aligned, to ceil(ceil(len/1024)/group_chunks) * 32
  *                bytes; group g's CV (8 little-endian words) at byte 32*g.
  * Errors: EINVAL (NULL dev_in or dev_cvs, len == 0, other group_chunks, counter
- * overflow), EALIGN, ETOOBIG, EHIP. Needs no scratch.
+ * overflow), EALIGN, ETOOBIG (len above 2^42, or more groups than one launch holds:
+ * 2^24 - 1, reached only above 2^40 bytes at 64 chunks per group and at 2^42 bytes at
+ * 256), EHIP. Needs no scratch.
  */
 int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, const uint32_t key[8],
                          uint32_t group_chunks, void *dev_cvs, void *stream);

@@ -189,3 +189,15 @@ def test_more_leaf_workgroups_than_one_grid_is_too_big(monkeypatch):
     fake = ctypes.c_void_p(1 << 20)
     assert lib.blake3_gpu_hash(fake, 1 << 42, fake, None) == b3.ETOOBIG
     monkeypatch.delenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS")
+
+
+def test_group_cvs_refuses_more_groups_than_one_launch():
+    # 2^42 bytes in groups of 64 chunks is 2^26 workgroups, in groups of 256 chunks 2^24:
+    # both more than one launch's 2^32 - 1 work-items (256 per workgroup); 512 chunks fit.
+    # The call refuses before any HIP call (the pointers are never dereferenced).
+    lib = b3._load()
+    fake = ctypes.c_void_p(1 << 20)
+    key = (ctypes.c_uint32 * 8)()
+    for group in (64, 256):
+        assert lib.blake3_gpu_group_cvs(fake, 1 << 42, 0, key, group, fake, None) == b3.ETOOBIG, group
+    assert lib.blake3_gpu_group_cvs(fake, (1 << 42) + 1, 0, key, 1024, fake, None) == b3.ETOOBIG
