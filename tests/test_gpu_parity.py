@@ -115,15 +115,17 @@ def test_level_boundaries(b3, dev, monkeypatch, quad, fused):
     # 256-chunk leaf workgroups and 256-CV level workgroups: counts around 256 and 256^2;
     # with the quad leaf, 64-chunk workgroups: counts around 64, 64*256 and 64*256^2.
     # 200,000, 262,144 and 262,145 chunks leave 782, 1024 and 1025 leaf CVs: the first
-    # level pass ends with 4, 4 and 5 CVs.
+    # level pass ends with 4, 4 and 5 CVs. 25,600, 60,000 and 91,137 chunks give level groups
+    # of 100, 235, and 256 + 101 CVs (quad leaf: 256 + 144, 256 * 3 + 170, 256 * 5 + 145),
+    # so level trees whose widest level has 33-64 and 65-128 output positions.
     # fused: level passes run inside the leaf launch (last-arrival tickets), or as
     # separate level launches
     if quad != "default":
         monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", quad)
     monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", fused)
     from blake3_merkle_tree_amd import workloads
-    chunks = [63, 64, 65, 255, 256, 257, 511, 512, 513, 16383, 16384, 16385, 65535, 65536, 65537, 131073,
-              200000, 262144, 262145]
+    chunks = [63, 64, 65, 255, 256, 257, 511, 512, 513, 16383, 16384, 16385, 25600, 60000, 65535, 65536, 65537,
+              91137, 131073, 200000, 262144, 262145]
     buf = workloads.random_bytes(262145 * 1024, 23, dev)
     host = _host(buf)
     key = bytes(workloads.key_bytes(24)[0].tolist())
