@@ -6,7 +6,9 @@ copy of the same device bytes. Cases: brute force over chunk counts and tail len
 boundaries), the empty input, misaligned views, non-default streams, batches with gap
 bytes of 0xA5 between messages (an over-read changes the digest), split message ends and
 seeded random batches, every workload at full size in the launch configuration the
-benchmark times, extended output and subtree CVs, and the library's scratch: a forced
+benchmark times, extended output and subtree CVs (share roots of a 4 GiB and a 256 MiB
+input, hashed separately with their chunk bases, combine to the digest), and the library's
+scratch: a forced
 allocation failure, scratch of arbitrary prior contents, repeated runs, and calls shared
 between streams, host threads and a stream held behind long work.
 """
@@ -689,3 +691,44 @@ def test_subtree_cv_matches_oracle(b3, dev, keyed):
         _say("subtree cv", L, "bytes, chunk base", base, "keyed", keyed)
         got = b3.subtree_cv(buf[:L], key, chunk_base=base).cpu().numpy().view(np.uint32).tolist()
         assert got == oracle.subtree_cv(host[:L].tobytes(), base, key), (L, base)
+
+
+def _combine_share_roots(nodes, kw, mode, is_root):
+    # shares are complete subtrees of 2^s chunks but the last, so over the share roots the
+    # tree's left subtree is the largest power of two of shares below their count
+    if len(nodes) == 1:
+        return nodes[0]
+    k = 1
+    while 2 * k < len(nodes):
+        k *= 2
+    return oracle.parent_cv(kw, mode, _combine_share_roots(nodes[:k], kw, mode, False),
+                            _combine_share_roots(nodes[k:], kw, mode, False), is_root=is_root)
+
+
+@pytest.mark.parametrize("workload,share_chunks,cut", [("gib4", 1 << 20, None), ("fp32_8192", 1 << 15, None),
+                                                       ("fp32_8192", 1 << 16, 3 * (1 << 26) - 5)])
+def test_share_roots_combine_to_the_digest(b3, dev, workload, share_chunks, cut):
+    # the input cut into shares of 2^s chunks, each share's root from subtree_cv with its
+    # chunk base (what one GPU of several would compute), the share roots joined by parent
+    # compressions on the host: the digest of the whole input (gib4: 5 shares, the last one
+    # the 1000-byte tail chunk; fp32_8192: 8 shares, and 3 with a partial last share)
+    import struct
+    from blake3_merkle_tree_amd import workloads
+    t, key = workloads.single(workload, dev)
+    t = t.reshape(-1).view(torch.uint8)
+    if cut is not None:
+        t = t[:cut]
+    key = bytes(key.tolist())
+    n = t.numel()
+    share_bytes = share_chunks * 1024
+    p = (n + share_bytes - 1) // share_bytes
+    _say("share roots", workload, n, "bytes in", p, "shares of", share_chunks, "chunks")
+    roots = [b3.subtree_cv(t[g * share_bytes:min(n, (g + 1) * share_bytes)], key, chunk_base=g * share_chunks)
+             .cpu().numpy().view(np.uint32).tolist() for g in range(p)]
+    kw = list(struct.unpack("<8I", key))
+    digest = struct.pack("<8I", *_combine_share_roots(roots, kw, oracle.KEYED_HASH, True))
+    assert digest == bytes(b3.keyed_hash(t, key).cpu().tolist())
+    host = _host(t)
+    del t
+    torch.cuda.empty_cache()
+    assert digest == oracle.hash_mt(host, key, NTHREADS)
