@@ -8,9 +8,8 @@ bytes of 0xA5 between messages (an over-read changes the digest), split message 
 seeded random batches, every workload at full size in the launch configuration the
 benchmark times, extended output and subtree CVs (share roots of a 4 GiB and a 256 MiB
 input, hashed separately with their chunk bases, combine to the digest), and the library's
-scratch: a forced
-allocation failure, scratch of arbitrary prior contents, repeated runs, and calls shared
-between streams, host threads and a stream held behind long work.
+scratch: a forced allocation failure, scratch of arbitrary prior contents, repeated runs,
+and calls shared between streams, host threads and a stream held behind long work.
 """
 import os
 
