@@ -699,6 +699,17 @@ int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *length
         return hash_uniform(static_cast<const uint8_t *>(base) + offsets[0], stride, lengths[0], n, keys,
                             kIV, keys ? kKeyedHash : 0u, 0, kRoot, static_cast<uint8_t *>(out), s);
 
+    // The task table is read by the device from host memory that later calls reuse (or
+    // that is freed on return): a graph that recorded the upload would read another
+    // call's table when replayed. Such a batch is refused under capture.
+    // (A failed query means no capture: the calls below report what is wrong.)
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+        (void)hipGetLastError();
+        cap = hipStreamCaptureStatusNone;
+    }
+    if (cap != hipStreamCaptureStatusNone) return B3G_EINVAL;
+
     uint64_t total_chunks = 0;
     for (uint64_t i = 0; i < n; ++i) total_chunks += chunks_of(lengths[i]);
     BatchPlan plan;

@@ -30,6 +30,12 @@
  *    calls on a stream under graph capture allocate and free their scratch in stream order
  *    on `stream` from a memory pool the library keeps per device. Calls on different
  *    streams and host threads may overlap; entry points are thread-safe.
+ *  - Graph capture: on a stream being captured (hipStreamBeginCapture) an entry point
+ *    records its kernels and its scratch's stream-ordered allocation and release; a
+ *    replay hashes the input buffers' contents at replay time. Host key words are
+ *    captured by value. The exception is a batch planned into a task table (one that is
+ *    not uniform, below): its table is read from host memory that later calls reuse, so
+ *    under capture it returns B3G_EINVAL and enqueues nothing.
  *  - Errors are returned as negative b3g_status values. Arguments are checked before any
  *    HIP call, so an argument error (EINVAL, EALIGN, ETOOBIG) enqueues nothing. ENOMEM and
  *    EHIP can come after part of the work was enqueued; the output is then unspecified.

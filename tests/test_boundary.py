@@ -132,8 +132,9 @@ def test_batch_argument_checks():
 
 def test_forced_scratch_failure_returns_enomem_before_any_hip_call(monkeypatch):
     # BLAKE3_GPU_SCRATCH_LIMIT caps a call's scratch request: every call that needs
-    # scratch fails with ENOMEM before its first HIP call (no device here, so any HIP
-    # call would fail with EHIP instead), launching nothing
+    # scratch fails with ENOMEM before any allocation or launch (no device here, so either
+    # would fail with EHIP instead; the batch's graph-capture query, which enqueues
+    # nothing, reads a failed query as no capture), launching nothing
     lib = _lib()
     monkeypatch.setenv("BLAKE3_GPU_SCRATCH_LIMIT", "0")
     key = (ctypes.c_uint32 * 8)()

@@ -9,7 +9,8 @@ seeded random batches, every workload at full size in the launch configuration t
 benchmark times, extended output and subtree CVs (share roots of a 4 GiB and a 256 MiB
 input, hashed separately with their chunk bases, combine to the digest), and the library's
 scratch: a forced allocation failure, scratch of arbitrary prior contents, repeated runs,
-and calls shared between streams, host threads and a stream held behind long work.
+and calls shared between streams, host threads and a stream held behind long work; and graph
+capture (replays equal eager results; a table-planned batch is refused under capture).
 """
 import os
 
@@ -731,3 +732,88 @@ def test_share_roots_combine_to_the_digest(b3, dev, workload, share_chunks, cut)
     del t
     torch.cuda.empty_cache()
     assert digest == oracle.hash_mt(host, key, NTHREADS)
+
+
+def test_graph_capture_replays_match_eager(b3, dev):
+    # One graph holding a keyed hash (70 MiB + 7 B: a leaf and two level passes), an XOF read
+    # across a multiple of 2^32 blocks, a subtree CV with a chunk base above 2^32 and a
+    # uniform batch (no task table). Replayed four times, with the outputs cleared, eager
+    # hashing and synchronisations between replays: every replay gives the eager results.
+    # The replay reads the inputs as they are then: a changed byte changes its digest.
+    from blake3_merkle_tree_amd import workloads
+    buf = workloads.random_bytes(70 * 1024 * 1024 + 7, 81, dev)
+    key = bytes(workloads.key_bytes(82)[0].tolist())
+    bkeys = workloads.key_bytes(83, 64).to(dev)
+    boffs, blens = [4096 * i for i in range(64)], [3000] * 64
+    outs = {"hash": torch.empty(32, dtype=torch.uint8, device=dev),
+            "xof": torch.empty(200, dtype=torch.uint8, device=dev),
+            "subtree": torch.empty(32, dtype=torch.uint8, device=dev),
+            "batch": torch.empty((64, 32), dtype=torch.uint8, device=dev)}
+
+    def run():
+        b3.keyed_hash(buf, key, out=outs["hash"])
+        b3.hash_xof(buf[:5000], key, 200, out=outs["xof"], offset=(64 << 32) - 100)
+        b3.subtree_cv(buf[:1 << 20], key, chunk_base=1 << 33, out=outs["subtree"])
+        b3.keyed_hash_batch(buf, boffs, blens, bkeys, out=outs["batch"])
+
+    run()
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in outs.items()}
+    assert bytes(want["hash"].cpu().tolist()) == oracle.hash(_host(buf).tobytes(), key)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # a first run on a side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    _say("capturing a single hash, an XOF, a subtree CV and a uniform batch")
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        for v in outs.values():
+            v.zero_()
+        eager = b3.keyed_hash(buf[:12345 + rep], key)  # the library's eager path in between
+        torch.cuda.synchronize()
+        _say("replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k], want[k]), (rep, k)
+        assert bytes(eager.cpu().tolist()) == oracle.hash(_host(buf[:12345 + rep]).tobytes(), key)
+    buf[70 * 1024 * 1024] ^= 0x5A
+    changed = b3.keyed_hash(buf, key)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert not torch.equal(changed, want["hash"])
+    assert torch.equal(outs["hash"], changed)
+    del g
+
+
+def test_table_batch_under_capture_is_refused(b3, dev):
+    # a batch that needs a task table reads it from reused host memory: under capture the
+    # call returns EINVAL and records nothing (the capture itself stays valid)
+    from blake3_merkle_tree_amd import workloads
+    buf = workloads.random_bytes(1 << 20, 84, dev)
+    keys = workloads.key_bytes(85, 2).to(dev)
+    out = torch.zeros((2, 32), dtype=torch.uint8, device=dev)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.capture_begin()
+        try:
+            out.fill_(7)
+            with pytest.raises(b3.Blake3GpuError) as err:
+                b3.keyed_hash_batch(buf, [0, 4096], [3000, 100], keys, out=out)
+        finally:
+            g.capture_end()
+    assert err.value.status == b3.EINVAL
+    g.replay()
+    torch.cuda.synchronize()
+    assert (out == 7).all()
+    # the same batch outside capture is hashed as usual
+    b3.keyed_hash_batch(buf, [0, 4096], [3000, 100], keys, out=out)
+    host = _host(buf)
+    assert _digests_to_bytes(out) == oracle.hash_batch(host, [0, 4096], [3000, 100], keys.cpu().numpy().tobytes())
