@@ -200,7 +200,10 @@ def keyed_hash_batch(base: torch.Tensor, offsets, lengths, keys=None, out=None, 
     CPU tensors). keys: None (default mode) or a device tensor with 32 bytes per message,
     shape (n, 32) uint8 or (n, 8) int32. Returns (n, 32) uint8. Equal lengths at evenly
     spaced offsets take a faster path that needs no launch table. A base or keys tensor
-    that is not 16-byte aligned is copied first (on the call's stream)."""
+    that is not 16-byte aligned is copied first (on the call's stream). Under graph
+    capture only such uniform batches can be recorded: a batch that needs a launch table
+    raises Blake3GpuError (EINVAL) there. Offsets or lengths given as device tensors are
+    copied to the host, which waits for the device."""
     if not isinstance(base, torch.Tensor) or base.device.type != "cuda":
         raise ValueError("base must be a tensor on a HIP device")
     if not base.is_contiguous():
