@@ -21,7 +21,7 @@
 namespace b3g {
 namespace {
 
-constexpr int kAbiVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kAbiVersion = 1 * 10000 + 2 * 100 + 0;
 
 // Stream-ordered scratch comes from one memory pool per device, created on first use and
 // kept for the life of the process, with a release threshold of "never" so that freed
