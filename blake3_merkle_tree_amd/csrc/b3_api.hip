@@ -434,8 +434,9 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
 
     // case B: G = ceil(c / span) leaf workgroups per message
     const uint64_t g = (c + span - 1) / span;
-    // one message's workgroups go in one launch; at 2^42 bytes and 256 or more chunks per
-    // workgroup g is at most 2^24 - 2^16, but a quad leaf forced onto a huge input is not
+    // one message's workgroups go in one launch. From 2^21 chunks a workgroup covers 1024
+    // chunks, so at 2^42 bytes g is at most 2^22; only a leaf forced by a test hook onto a
+    // huge input (the quad leaf, or one chunk per lane at 2^42 bytes) needs more
     if (g > kMaxGrid) return B3G_ETOOBIG;
     const uint64_t per_launch = kMaxGrid / g;  // >= 1
     const uint64_t nb = n_msgs < per_launch ? n_msgs : per_launch;
