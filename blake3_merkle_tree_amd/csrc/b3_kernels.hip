@@ -1097,7 +1097,11 @@ __device__ __forceinline__ void quarter_uniform(uint32_t &a, uint32_t &b, uint32
 // enters column 0 (low word) and column 1 (high word, the same for the whole launch).
 // Columns 1..3 and the first sum of column 0 therefore read only wave-uniform words and
 // run once per wave on the scalar unit, which takes 37 of the block's 688 VALU
-// instructions off the vector unit. The stores keep to the requested byte range.
+// instructions off the vector unit. The stores keep to the requested byte range. A wave
+// whose 64 blocks are whole, in range and 16-byte aligned at the destination passes them
+// through LDS so that each of its four 16-byte stores writes 1 KiB contiguously (64 lanes
+// x 16 B) instead of 16 B every 64 B; the transposition stays inside the wave, whose LDS
+// accesses complete in order.
 __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
     const uint64_t i = static_cast<uint64_t>(blockIdx.x) * kXofLanes + threadIdx.x;
     if (i >= a.n_blocks) return;
@@ -1144,6 +1148,26 @@ __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
     }
     // stream bytes [s0, s0 + 64) of this block, clipped to [out_offset, end)
     const uint64_t s0 = kBlockBytes * t, end = a.out_offset + a.out_len;
+    // the wave path (the condition is the same for all lanes of the wave: a wave with
+    // lanes past n_blocks, which returned above, never takes it)
+    __shared__ uint4 xo[kXofLanes / 64][256];
+    const uint64_t w0 = static_cast<uint64_t>(blockIdx.x) * kXofLanes + (threadIdx.x & ~63u);
+    const uint64_t ws0 = kBlockBytes * (a.first_block + w0);
+    if (w0 + 64 <= a.n_blocks && ws0 >= a.out_offset && ws0 + 64 * kBlockBytes <= end &&
+        (reinterpret_cast<uintptr_t>(a.out) - a.out_offset) % 16 == 0) {
+        const uint32_t wv = threadIdx.x >> 6, ln = threadIdx.x & 63u;
+        uint4 *row = xo[wv];
+        row[4 * ln + 0] = make_uint4(o[0], o[1], o[2], o[3]);
+        row[4 * ln + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+        row[4 * ln + 2] = make_uint4(o[8], o[9], o[10], o[11]);
+        row[4 * ln + 3] = make_uint4(o[12], o[13], o[14], o[15]);
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+        uint4 *d = reinterpret_cast<uint4 *>(a.out + (ws0 - a.out_offset));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d[64 * q + ln] = row[64 * q + ln];
+        return;
+    }
     if (s0 >= a.out_offset && s0 + kBlockBytes <= end &&
         reinterpret_cast<uintptr_t>(a.out + (s0 - a.out_offset)) % 16 == 0) {
         uint4 *d = reinterpret_cast<uint4 *>(a.out + (s0 - a.out_offset));
