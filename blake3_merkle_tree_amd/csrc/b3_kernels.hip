@@ -1153,7 +1153,9 @@ __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
     __shared__ uint4 xo[kXofLanes / 64][256];
     const uint64_t w0 = static_cast<uint64_t>(blockIdx.x) * kXofLanes + (threadIdx.x & ~63u);
     const uint64_t ws0 = kBlockBytes * (a.first_block + w0);
-    if (w0 + 64 <= a.n_blocks && ws0 >= a.out_offset && ws0 + 64 * kBlockBytes <= end &&
+    // (every launched block starts before `end`, so end - s0 never wraps, where s0 + 64
+    // would for the last block of the 2^64-byte stream)
+    if (w0 + 64 <= a.n_blocks && ws0 >= a.out_offset && end - ws0 >= 64 * kBlockBytes &&
         (reinterpret_cast<uintptr_t>(a.out) - a.out_offset) % 16 == 0) {
         const uint32_t wv = threadIdx.x >> 6, ln = threadIdx.x & 63u;
         uint4 *row = xo[wv];
@@ -1168,7 +1170,7 @@ __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
         for (int q = 0; q < 4; ++q) d[64 * q + ln] = row[64 * q + ln];
         return;
     }
-    if (s0 >= a.out_offset && s0 + kBlockBytes <= end &&
+    if (s0 >= a.out_offset && end - s0 >= kBlockBytes &&
         reinterpret_cast<uintptr_t>(a.out + (s0 - a.out_offset)) % 16 == 0) {
         uint4 *d = reinterpret_cast<uint4 *>(a.out + (s0 - a.out_offset));
         d[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -1177,7 +1179,7 @@ __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
         d[3] = make_uint4(o[12], o[13], o[14], o[15]);
     } else {
         const uint64_t lo = s0 > a.out_offset ? s0 : a.out_offset;
-        const uint64_t hi = s0 + kBlockBytes < end ? s0 + kBlockBytes : end;
+        const uint64_t hi = end - s0 > kBlockBytes ? s0 + kBlockBytes : end;
         for (uint64_t x = lo; x < hi; ++x) {
             const uint32_t k = static_cast<uint32_t>(x - s0);
             a.out[x - a.out_offset] = static_cast<uint8_t>(o[k / 4] >> (8 * (k % 4)));
