@@ -84,6 +84,20 @@ struct DeviceSlots {
 };
 DeviceSlots g_slots[kMaxDevices];
 
+// Test hook: with BLAKE3_GPU_SCRATCH_FILL set, a call's scratch is filled with that byte
+// before its kernels run (by a kernel in stream order), so that tests can show that no
+// result depends on what the memory held before. Scratch requests are multiples of 4 bytes.
+int fill_scratch(void *p, size_t bytes, hipStream_t s) {
+    const int fill = scratch_fill_byte();
+    if (fill < 0) return B3G_OK;
+    const uint32_t word = 0x01010101u * static_cast<uint32_t>(fill);
+    if (launch_fill_words(static_cast<uint32_t *>(p), word, bytes / 4, s) != hipSuccess) {
+        (void)hipGetLastError();
+        return B3G_EHIP;
+    }
+    return B3G_OK;
+}
+
 // Scratch of one call: a slot (above), or, for large requests or when every slot is held,
 // a stream-ordered allocation released in stream order on the caller's stream.
 class StreamScratch {
@@ -113,12 +127,7 @@ class StreamScratch {
         int rc = bytes <= kSlotMaxBytes ? take_slot(bytes) : B3G_ENOMEM;
         if (rc != B3G_OK) rc = from_pool(bytes);
         if (rc != B3G_OK) return rc;
-        const int fill = scratch_fill_byte();  // test hook: scratch of known, arbitrary contents
-        if (fill >= 0 && hipMemsetAsync(p_, fill, bytes, s_) != hipSuccess) {
-            (void)hipGetLastError();
-            return B3G_EHIP;
-        }
-        return B3G_OK;
+        return fill_scratch(p_, bytes, s_);
     }
     uint8_t *get() const { return static_cast<uint8_t *>(p_); }
 

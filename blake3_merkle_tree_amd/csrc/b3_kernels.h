@@ -119,9 +119,12 @@ hipError_t launch_uniform_level(const UniformLevelArgs &a, uint32_t grid, hipStr
 constexpr uint32_t kQuadLeafChunks = 64;
 hipError_t launch_quad_leaf(const UniformLeafArgs &a, uint32_t grid, hipStream_t s);
 
-// Zeroes n words (the tickets of fused levels) with a kernel, in stream order.
 // n 16-byte words from src (device-visible pinned host memory, or device memory) to dst.
 hipError_t launch_copy_words16(const void *src, void *dst, uint64_t n, hipStream_t s);
+// Sets n 32-bit words to `value` with a kernel, in stream order (a kernel rather than
+// hipMemsetAsync, so that a graph that records it replays it as it ran).
+hipError_t launch_fill_words(uint32_t *p, uint32_t value, uint64_t n, hipStream_t s);
+// Zeroes n words (the tickets of fused levels): launch_fill_words with 0.
 hipError_t launch_zero_words(uint32_t *p, uint64_t n, hipStream_t s);
 // Extended output: output block t (64 bytes at out + 64*(t - first_block)) is the root
 // compression (cv, m, block_len, flags with ROOT) run with counter t; all 16 output words.

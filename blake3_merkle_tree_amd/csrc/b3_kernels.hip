@@ -1207,19 +1207,21 @@ hipError_t launch_copy_words16(const void *src, void *dst, uint64_t n, hipStream
     return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *p, uint64_t n) {
+__global__ __launch_bounds__(256) void fill_words_kernel(uint32_t *p, uint32_t value, uint64_t n) {
     for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
          i += static_cast<uint64_t>(gridDim.x) * 256)
-        p[i] = 0;
+        p[i] = value;
 }
 
-hipError_t launch_zero_words(uint32_t *p, uint64_t n, hipStream_t s) {
+hipError_t launch_fill_words(uint32_t *p, uint32_t value, uint64_t n, hipStream_t s) {
     if (n == 0) return hipSuccess;
     const uint64_t blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(zero_words_kernel, dim3(blocks < 1024 ? static_cast<uint32_t>(blocks) : 1024u), dim3(256), 0,
-                       s, p, n);
+    hipLaunchKernelGGL(fill_words_kernel, dim3(blocks < 1024 ? static_cast<uint32_t>(blocks) : 1024u), dim3(256), 0,
+                       s, p, value, n);
     return hipGetLastError();
 }
+
+hipError_t launch_zero_words(uint32_t *p, uint64_t n, hipStream_t s) { return launch_fill_words(p, 0, n, s); }
 
 hipError_t launch_xof_expand(const XofArgs &a, uint32_t grid, hipStream_t s) {
     hipLaunchKernelGGL(xof_expand_kernel, dim3(grid), dim3(kXofLanes), 0, s, a);
