@@ -4,19 +4,29 @@
                     [--workload gib4|gib16|fp32_8192|mib1|batch64k|ragged256|xof_gib8]
 
 A step is one full hash (leaf pass + level passes, ROOT) of the workload's bytes, which
-are already in HBM when the timed region starts. Prints ONE JSON line on stdout:
-  value         input bytes / 1e9 / seconds per step (GB/s), whole job, one GPU
+are already in HBM when the timed region starts. Before the W counted warm-up steps the
+step runs for --warmup-seconds of wall time (the GPU's clock and power settle only after
+~100 ms of this load). The K timed steps run back to back on one stream with a HIP event
+between consecutive steps. Prints ONE JSON line on stdout:
+  value         input bytes / 1e9 / median seconds per step (GB/s), whole job, one GPU
+  ms_per_step   the median step; ms_per_step_min and ms_per_step_mean beside it
   roofline      the dominant kernel (the leaf pass: chunk compression + fused in-workgroup
-                tree), timed alone with HIP events on the stream it runs on, against the
-                integer-VALU peak (it is ALU-bound; the HBM figure is reported beside it)
-  cpu_baseline  the CPU oracle on host threads over a bounded sample of the same bytes
+                tree), timed alone right after the chain with HIP events on the stream it
+                runs on (median launch), against the integer-VALU peak (it is ALU-bound;
+                the HBM figure is reported beside it)
+  gpu_state     gfx clock, temperatures and power read from the GPU's sysfs files while
+                the timed steps ran
+  cpu_baseline  the CPU oracle on the host's threads over the same bytes, plus one thread
+                on a bounded sample, with the CPU model
 Everything else goes to stderr.
 """
 import argparse
+import glob
 import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -43,6 +53,7 @@ PAGE_OPS_PER_BYTE = 336 / 64
 LEAF_LANES = 256
 BATCH_COUNT, BATCH_LEN = 65536, 65536  # the batch workload: 65,536 messages of 64 KiB
 CPU_SHARE = 16  # host threads of one GPU's share on the benchmark machines
+ONE_THREAD_SAMPLE = 1 << 30  # bytes the one-thread oracle leg hashes (about 3 s)
 
 
 def log(*a):
@@ -84,10 +95,14 @@ def kernel_source_digest(csrc=None):
     return h.hexdigest()[:16]
 
 
+def traffic_source(workload):
+    return os.path.join("profiles", f"leaf_{workload}_traffic.txt")
+
+
 def measured_traffic(workload):
-    """HBM bytes per leaf launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"leaf_{workload}_traffic.txt")
+    """HBM bytes per leaf launch from the committed rocprofv3 counter summary (taken in an
+    earlier run, not in this one), if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, traffic_source(workload))
     if not os.path.exists(path):
         return None
     fields = {}
@@ -104,6 +119,132 @@ def measured_traffic(workload):
         return None
 
 
+def host_cpu():
+    """Threads this process may run on (what `nproc` prints), the machine's CPU count and
+    the CPU model, from /proc/cpuinfo."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count() or 1
+    return {"nproc": nproc, "cpu_count": os.cpu_count(), "cpu_model": model}
+
+
+class GpuSensors:
+    """The benchmark GPU's gfx clock, temperatures and power, read from the amdgpu driver's
+    sysfs files of its PCI device (hwmon freq1_input / temp*_input / power1_*, and the
+    current pp_dpm_sclk level). Files only: no tool is started from this process."""
+
+    def __init__(self, torch, index):
+        self.dir = None
+        self.hwmon = []
+        try:
+            p = torch.cuda.get_device_properties(index)
+            d = f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+            if os.path.isdir(d):
+                self.dir = d
+                self.hwmon = sorted(glob.glob(os.path.join(d, "hwmon", "hwmon*")))
+        except Exception:  # noqa: BLE001 - sensors are optional
+            pass
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as f:
+                return f.read().strip()
+        except OSError:
+            return None
+
+    def sample(self):
+        s = {}
+        for h in self.hwmon:
+            for f in glob.glob(os.path.join(h, "freq*_input")):
+                label = self._read(f.replace("_input", "_label")) or os.path.basename(f)
+                v = self._read(f)
+                if v is not None and v.isdigit():
+                    s[f"{label}_mhz"] = int(v) / 1e6
+            for f in glob.glob(os.path.join(h, "temp*_input")):
+                label = self._read(f.replace("_input", "_label")) or os.path.basename(f)
+                v = self._read(f)
+                if v is not None and v.lstrip("-").isdigit():
+                    s[f"temp_{label}_c"] = int(v) / 1e3
+            for name in ("power1_average", "power1_input"):
+                v = self._read(os.path.join(h, name))
+                if v is not None and v.isdigit():
+                    s[f"{name}_w"] = int(v) / 1e6
+        if self.dir:
+            levels = self._read(os.path.join(self.dir, "pp_dpm_sclk"))
+            if levels:
+                cur = [ln for ln in levels.splitlines() if ln.rstrip().endswith("*")]
+                if cur:
+                    m = re.search(r"(\d+)\s*[Mm]hz", cur[0])
+                    if m:
+                        s["pp_dpm_sclk_mhz"] = int(m.group(1))
+        return s
+
+    def summary(self, samples):
+        """Median, minimum and maximum of every sampled quantity."""
+        if not samples:
+            return {"source": self.dir, "samples": 0}
+        out = {"source": self.dir, "samples": len(samples)}
+        for k in sorted({k for smp in samples for k in smp}):
+            v = [smp[k] for smp in samples if k in smp]
+            out[k] = {"median": round(statistics.median(v), 1), "min": round(min(v), 1), "max": round(max(v), 1)}
+        return out
+
+
+def warm_up(torch, step, seconds, count):
+    """Runs `step` for at least `seconds` of wall time (synchronising every few steps, so
+    that the time is the GPU's), then `count` more steps."""
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while True:
+        for _ in range(4):
+            step()
+        n += 4
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            break
+    for _ in range(count):
+        step()
+    torch.cuda.synchronize()
+    return n + count
+
+
+def timed_steps(torch, stream, step, k, sensors=None):
+    """Runs `step` k times back to back on `stream`, a HIP event recorded before the first
+    and after every step; while they run, samples the GPU's sensors. Returns the per-step
+    times (ms), the event time of all k steps (ms), the host wall time (s) and the samples."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(k):
+        step()
+        evs[i + 1].record(stream)
+    samples = []
+    if sensors is not None:
+        while not evs[k].query():
+            samples.append(sensors.sample())
+            time.sleep(0.002)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(k)]
+    return per, evs[0].elapsed_time(evs[k]), wall, samples
+
+
+def step_stats(per, total, k):
+    return {"median": statistics.median(per), "min": min(per), "mean": total / k}
+
+
 XOF_WORKLOAD = "xof_gib8"
 # An output block keeps all 16 words: the 8 xors of the fold plus 8 more for v[i+8] ^ cv[i].
 XOF_OPS_PER_BLOCK = 7 * 8 * 12 + 16
@@ -111,7 +252,13 @@ XOF_OUT_BYTES = 8 << 30
 XOF_CHECK_BYTES = 64 << 20
 
 
-def bench_xof(args, torch, b3, workloads, dev, stream):
+def oracle_threads(cpu):
+    """Threads of the multi-threaded oracle leg: every thread this process may run on, up
+    to one GPU's host share on the benchmark machines."""
+    return max(1, min(cpu["nproc"], CPU_SHARE))
+
+
+def bench_xof(args, torch, b3, workloads, dev, stream, sensors):
     """Extendable output: 8 GiB of keyed XOF output from the 1 MiB input. The step is the
     whole call (the input's two top subtrees, then the expansion kernel, one lane per
     64-byte block); the expansion is the dominant kernel, and its roofline is taken over
@@ -122,22 +269,15 @@ def bench_xof(args, torch, b3, workloads, dev, stream):
 
     def step():
         b3.hash_xof(data, key, XOF_OUT_BYTES, out=out)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    warm = warm_up(torch, step, args.warmup_seconds, args.warmup)
+    per, total, wall, samples = timed_steps(torch, stream, step, args.steps, sensors)
+    st = step_stats(per, total, args.steps)
+    ms = st["median"]
     value = XOF_OUT_BYTES / 1e9 / (ms / 1e3)
     ops = (XOF_OUT_BYTES // 64) * XOF_OPS_PER_BLOCK
     achieved = ops / (ms / 1e3) / 1e12
-    log(f"xof: {ms:.4f} ms/step ({value:.1f} GB/s of output), {achieved:.2f} Tops/s = "
-        f"{achieved / VALU_INT_PEAK_TOPS:.1%} of the int-VALU peak")
+    log(f"xof: {ms:.4f} ms/step median (min {st['min']:.4f}, mean {st['mean']:.4f}; {value:.1f} GB/s of "
+        f"output), {achieved:.2f} Tops/s = {achieved / VALU_INT_PEAK_TOPS:.1%} of the int-VALU peak")
     cpu = None
     digest_match = None
     if not args.no_check or not args.no_cpu:
@@ -149,14 +289,16 @@ def bench_xof(args, torch, b3, workloads, dev, stream):
         if not args.no_cpu:
             cpu = {"value": round(XOF_CHECK_BYTES / 1e9 / c_s, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                    "sample": f"the first {XOF_CHECK_BYTES} bytes of the same output stream, plain scalar C "
-                             f"oracle on one thread, {c_s:.2f} s wall"}
+                             f"oracle on one thread (its extended output has no multi-threaded form), "
+                             f"{c_s:.2f} s wall", **host_cpu()}
         if not args.no_check:
             digest_match = bytes(out[:XOF_CHECK_BYTES].cpu().numpy().tobytes()) == want
             log(f"first {XOF_CHECK_BYTES} output bytes match the oracle: {digest_match}")
     rec = {
         "metric": "GB/s of extended output, keyed BLAKE3 XOF",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": round(ms, 4), "ms_per_step_min": round(st["min"], 4), "ms_per_step_mean": round(st["mean"], 4),
+        "warmup_steps_run": warm, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "u32", "data": "synthetic",
         "config": {"workload": "8 GiB of keyed BLAKE3 extendable output of 1 MiB uniform random bytes "
                                "(seed 0, key seed 1)", "input_bytes": data.numel(), "output_bytes": XOF_OUT_BYTES},
@@ -165,21 +307,66 @@ def bench_xof(args, torch, b3, workloads, dev, stream):
                      "traffic": None, "kernel": "xof_expand_kernel (step time, input hash included)",
                      "kernel_ms": round(ms, 4), "ops_per_launch": ops,
                      "hbm_write_gbs": round(value, 1), "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
+        "gpu_state": sensors.summary(samples),
         "cpu_baseline": cpu,
         "digest_match": digest_match,
     }
     print(json.dumps(rec), flush=True)
 
 
+def cpu_legs(args, oracle, host, key, batch, cpu_info):
+    """The oracle on the host: every byte with oracle_threads() threads (its digests are
+    the check's expected values when it covers the whole input), and one thread on the
+    first ONE_THREAD_SAMPLE bytes. Returns (cpu_baseline dict, expected digest(s) or None)."""
+    threads = oracle_threads(cpu_info)
+    sample = len(host) if args.cpu_sample_gib is None else min(len(host), int(args.cpu_sample_gib * (1 << 30)))
+
+    def run(limit, nthreads):
+        c0 = time.perf_counter()
+        if batch is not None:
+            offs, lengths, keys_bytes = batch
+            # whole messages from the front of the batch, until the sample's bytes are used
+            cnt = 0
+            while cnt < len(lengths) and offs[cnt] + lengths[cnt] <= limit:
+                cnt += 1
+            end = offs[cnt - 1] + lengths[cnt - 1] if cnt else 0
+            got = oracle.hash_batch(host[:end], offs[:cnt], lengths[:cnt], keys_bytes[:32 * cnt], nthreads=nthreads)
+            nbytes = sum(lengths[:cnt])
+            whole = cnt == len(lengths)
+        else:
+            got = (oracle.hash_mt(host[:limit], key, nthreads) if nthreads > 1 else oracle.hash(host[:limit], key))
+            nbytes = limit
+            whole = limit == len(host)
+        return nbytes / 1e9 / (time.perf_counter() - c0), nbytes, (got if whole else None), time.perf_counter() - c0
+
+    rate, nbytes, want, secs = run(sample, threads)
+    what = "all" if want is not None else f"the first {nbytes}"
+    one_rate, one_bytes, one_want, one_secs = run(min(len(host), ONE_THREAD_SAMPLE), 1)
+    if want is None:
+        want = one_want
+    cpu = {"value": round(rate, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{what} bytes of the same {args.workload} input ({nbytes} B), plain scalar C oracle "
+                     f"(multi-threaded aligned-subtree form), {secs:.2f} s wall, {threads} threads",
+           "one_thread": {"value": round(one_rate, 3), "unit": "GB/s",
+                          "sample": f"the first {one_bytes} bytes of the same input, the oracle on one thread, "
+                                    f"{one_secs:.2f} s wall"},
+           **cpu_info}
+    log(f"cpu oracle: {cpu['value']} GB/s on {threads} threads ({nbytes} bytes); {cpu['one_thread']['value']} "
+        f"GB/s on one thread ({one_bytes} bytes); nproc {cpu_info['nproc']}, {cpu_info['cpu_model']}")
+    return cpu, want
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the GPU's clock settles only after ~100 ms of this load: warm up past that
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10, help="counted warm-up steps, after --warmup-seconds")
+    # the GPU's clock and power settle only after ~100 ms of this load: warm up past that
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="wall time of untimed steps before the counted warm-up")
     ap.add_argument("--workload", default="gib4")
     ap.add_argument("--cpu-sample-gib", type=float, default=None,
-                    help="time the CPU oracle on the first GIB GiB only (default: the whole input)")
+                    help="time the multi-threaded CPU oracle on the first GIB GiB only (default: the whole input)")
     ap.add_argument("--no-check", action="store_true", help="skip the full-digest oracle check")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--calibrate-copy", type=float, default=None, metavar="GIB",
@@ -209,8 +396,9 @@ def main():
         print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
                           "launches": args.steps}), flush=True)
         return
+    sensors = GpuSensors(torch, 0)
     if args.workload == XOF_WORKLOAD:
-        return bench_xof(args, torch, b3, workloads, dev, stream)
+        return bench_xof(args, torch, b3, workloads, dev, stream, sensors)
     batch = args.workload in ("batch64k", "ragged256")
     if batch:
         if args.workload == "batch64k":
@@ -237,21 +425,15 @@ def main():
     torch.cuda.synchronize()
     log(f"workload {args.workload}: {nbytes} bytes")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    warm = warm_up(torch, step, args.warmup_seconds, args.warmup)
+    per, total, wall, samples = timed_steps(torch, stream, step, args.steps, sensors)
+    st = step_stats(per, total, args.steps)
+    ms_per_step = st["median"]
     value = nbytes / 1e9 / (ms_per_step / 1e3)
-    log(f"chain: {ms_per_step:.4f} ms/step ({value:.1f} GB/s), wall {wall:.3f} s for {args.steps} steps")
+    log(f"chain: {ms_per_step:.4f} ms/step median, min {st['min']:.4f}, mean {st['mean']:.4f} ({value:.1f} GB/s); "
+        f"wall {wall:.3f} s for {args.steps} steps after {warm} warm-up steps")
+    gpu_state = sensors.summary(samples)
+    log(f"gpu state during the timed steps: {gpu_state}")
 
     # the dominant kernel alone: the leaf pass, launched on the same stream
     roofline = None
@@ -288,6 +470,7 @@ def main():
             "unit": "Tops/s (int32 VALU lane-ops)",
             "frac": round(achieved / VALU_INT_PEAK_TOPS, 4),
             "traffic": measured_traffic(args.workload),
+            "traffic_source": traffic_source(args.workload) + " (rocprofv3 counters of an earlier run)",
             "kernel": f"leaf_uniform_kernel<{k}> ({c} chunks per message, {per_wg} messages per workgroup)",
             "kernel_ms": round(ms_per_step, 4),
             "ops_per_launch": ops,
@@ -299,17 +482,15 @@ def main():
     else:
         group = b3.leaf_group_chunks(nbytes)  # the leaf configuration the chain uses
         cvs = torch.empty(((nbytes + 1023) // 1024 + group - 1) // group, 8, dtype=torch.int32, device=dev)
-        for _ in range(args.warmup):
+
+        def leaf_step():
             b3.group_cvs(data, key, group_chunks=group, out=cvs)
-        k0 = torch.cuda.Event(enable_timing=True)
-        k1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        k0.record(stream)
-        for _ in range(args.steps):
-            b3.group_cvs(data, key, group_chunks=group, out=cvs)
-        k1.record(stream)
-        torch.cuda.synchronize()
-        leaf_ms = k0.elapsed_time(k1) / args.steps
+        # right after the chain, in the same clock state: two untimed launches, then timed
+        leaf_step()
+        leaf_step()
+        kper, ktotal, _, _ = timed_steps(torch, stream, leaf_step, args.steps)
+        kst = step_stats(kper, ktotal, args.steps)
+        leaf_ms = kst["median"]
         ops = leaf_compressions(nbytes, group) * OPS_PER_COMPRESSION
         achieved = ops / (leaf_ms / 1e3) / 1e12
         roofline = {
@@ -319,55 +500,37 @@ def main():
             "unit": "Tops/s (int32 VALU lane-ops)",
             "frac": round(achieved / VALU_INT_PEAK_TOPS, 4),
             "traffic": measured_traffic(args.workload),
+            "traffic_source": traffic_source(args.workload) + " (rocprofv3 counters of an earlier run)",
             "kernel": "leaf_quad_kernel" if group < LEAF_LANES else f"leaf_uniform_kernel<{group // LEAF_LANES}>",
             "kernel_ms": round(leaf_ms, 4),
+            "kernel_ms_min": round(kst["min"], 4),
+            "kernel_ms_mean": round(kst["mean"], 4),
             "ops_per_launch": ops,
             "hbm_gbs": round(nbytes / 1e9 / (leaf_ms / 1e3), 1),
             "hbm_frac": round(nbytes / 1e9 / (leaf_ms / 1e3) / HBM_PEAK_GBS, 4),
         }
-        log(f"leaf kernel: {leaf_ms:.4f} ms, {achieved:.2f} Tops/s = {achieved / VALU_INT_PEAK_TOPS:.1%} "
-            f"of the int-VALU peak; {nbytes / 1e9 / (leaf_ms / 1e3):.0f} GB/s")
+        log(f"leaf kernel: {leaf_ms:.4f} ms median (min {kst['min']:.4f}), {achieved:.2f} Tops/s = "
+            f"{achieved / VALU_INT_PEAK_TOPS:.1%} of the int-VALU peak; {nbytes / 1e9 / (leaf_ms / 1e3):.0f} GB/s")
 
     digest_match = None
     cpu = None
     if not args.no_check or not args.no_cpu:
         import oracle
-        cores = min(CPU_SHARE, os.cpu_count() or 1)
+        cpu_info = host_cpu()
         host = data.contiguous().view(torch.uint8).reshape(-1).cpu().numpy()
+        bspec = (offs, lengths, keys_cpu.numpy().tobytes()) if batch else None
         want = None
         if not args.no_cpu:
-            # the oracle over the whole input (or the first --cpu-sample-gib GiB of it)
-            sample = len(host) if args.cpu_sample_gib is None else min(len(host), int(args.cpu_sample_gib * (1 << 30)))
-            c0 = time.perf_counter()
-            if batch:
-                # whole messages from the front of the batch, until the sample's bytes are used
-                cnt, end = 0, 0
-                while cnt < len(lengths) and offs[cnt] + lengths[cnt] <= sample:
-                    end = offs[cnt] + lengths[cnt]
-                    cnt += 1
-                got = oracle.hash_batch(host[:end], offs[:cnt], lengths[:cnt],
-                                        keys_cpu.numpy().tobytes()[:32 * cnt], nthreads=cores)
-                sample = sum(lengths[:cnt])
-                if cnt < len(lengths):
-                    got = None
-            else:
-                got = oracle.hash_mt(host[:sample], key, cores)
-            c_s = time.perf_counter() - c0
-            if got is not None and (batch or sample == len(host)):
-                want = got
-            what = "all" if want is not None else f"the first {sample}"
-            cpu = {"value": round(sample / 1e9 / c_s, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-                   "sample": f"{what} bytes of the same {args.workload} input ({sample} B), plain scalar C oracle "
-                             f"(multi-threaded aligned-subtree form), {c_s:.2f} s wall, {cores} threads"}
-            log(f"cpu oracle: {cpu['value']} GB/s on {cores} threads ({sample} bytes)")
+            cpu, want = cpu_legs(args, oracle, host, None if batch else key, bspec, cpu_info)
         if not args.no_check:
+            threads = oracle_threads(cpu_info)
             if batch:
                 if want is None:
-                    want = oracle.hash_batch(host, offs, lengths, keys_cpu.numpy().tobytes(), nthreads=cores)
+                    want = oracle.hash_batch(host, offs, lengths, bspec[2], nthreads=threads)
                 digest_match = [bytes(r) for r in out.cpu().numpy()] == want
             else:
                 if want is None:
-                    want = oracle.hash_mt(host, key, cores)
+                    want = oracle.hash_mt(host, key, threads)
                 digest_match = bytes(out.cpu().tolist()) == want
             log(f"digest matches the oracle: {digest_match}")
 
@@ -386,6 +549,7 @@ def main():
         "leaf_workgroup_chunks": b3.leaf_group_chunks(nbytes),
         "level_workgroup_cvs": 256,
     }
+    roof_page = min(HBM_PEAK_GBS, VALU_INT_PEAK_TOPS * 1e3 / PAGE_OPS_PER_BYTE)
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -394,6 +558,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_min": round(st["min"], 4),
+        "ms_per_step_mean": round(st["mean"], 4),
+        "warmup_steps_run": warm,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -401,13 +568,14 @@ def main():
         "data": "synthetic",
         "config": cfg,
         "roofline": roofline,
+        "gpu_state": gpu_state,
         "cpu_baseline": cpu,
         "digest_match": digest_match,
         "hbm_frac_chain": round(value / HBM_PEAK_GBS, 4),
         "roof_at_page_op_count": {
             "ops_per_byte": PAGE_OPS_PER_BYTE,
-            "roof_gbs": round(min(HBM_PEAK_GBS, VALU_INT_PEAK_TOPS * 1e3 / PAGE_OPS_PER_BYTE), 1),
-            "frac": round(value / min(HBM_PEAK_GBS, VALU_INT_PEAK_TOPS * 1e3 / PAGE_OPS_PER_BYTE), 4),
+            "roof_gbs": round(roof_page, 1),
+            "frac": round(value / roof_page, 4),
         },
     }
     print(json.dumps(rec), flush=True)
