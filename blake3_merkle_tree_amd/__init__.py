@@ -6,6 +6,8 @@ library's HIP kernels. The functions mirror the C entry points:
 
     hash(t)                              -> 32-byte digest tensor on t's device
     keyed_hash(t, key)                   -> 32-byte digest tensor (key: 32 bytes)
+    keyed_hash_noalloc(t, key, out)      -> keyed_hash (or hash, key None) that allocates
+                                         nothing, writing into out
     keyed_hash_batch(base, offsets, lengths, keys=None) -> (n, 32) digest tensor
     hash_xof(t, key=None, out_len=32, offset=0) -> bytes [offset, offset + out_len) of the
                                          extended output
@@ -30,14 +32,14 @@ import struct
 import numpy as np
 import torch
 
-__all__ = ["hash", "keyed_hash", "keyed_hash_batch", "hash_xof", "subtree_cv", "group_cvs", "leaf_group_chunks",
+__all__ = ["hash", "keyed_hash", "keyed_hash_noalloc", "keyed_hash_batch", "hash_xof", "subtree_cv", "group_cvs", "leaf_group_chunks",
            "strerror", "version", "Blake3GpuError", "library_path", "debug_plan_batch"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libblake3_gpu.so")
 _lib = None
 
-OK, EINVAL, EALIGN, ENOMEM, EHIP, ETOOBIG = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EALIGN, ENOMEM, EHIP, ETOOBIG, ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 
 
 class Blake3GpuError(RuntimeError):
@@ -61,6 +63,7 @@ def _load():
     vp, u64 = ctypes.c_void_p, ctypes.c_uint64
     lib.blake3_gpu_hash.argtypes = [vp, u64, vp, vp]
     lib.blake3_gpu_keyed_hash.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
+    lib.blake3_gpu_keyed_hash_noalloc.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
     lib.blake3_gpu_keyed_hash_batch.argtypes = [vp, vp, vp, vp, vp, u64, vp]
     lib.blake3_gpu_group_cvs.argtypes = [vp, u64, u64, ctypes.POINTER(ctypes.c_uint32), ctypes.c_uint32, vp, vp]
     lib.blake3_gpu_subtree_cv.argtypes = [vp, u64, u64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
@@ -74,7 +77,8 @@ def _load():
     lib.debug_plan = lib.blake3_gpu_debug_plan_batch
     lib.debug_plan.argtypes = [ctypes.POINTER(u64), u64, ctypes.POINTER(u64), u64]
     lib.debug_plan.restype = ctypes.c_int64
-    for f in ("blake3_gpu_hash", "blake3_gpu_keyed_hash", "blake3_gpu_keyed_hash_batch", "blake3_gpu_group_cvs",
+    for f in ("blake3_gpu_hash", "blake3_gpu_keyed_hash", "blake3_gpu_keyed_hash_noalloc",
+              "blake3_gpu_keyed_hash_batch", "blake3_gpu_group_cvs",
               "blake3_gpu_subtree_cv", "blake3_gpu_hash_xof", "blake3_gpu_hash_xof_at", "blake3_gpu_version"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
@@ -191,6 +195,28 @@ def keyed_hash(t: torch.Tensor, key, out=None, stream=None) -> torch.Tensor:
         rc = _load().blake3_gpu_keyed_hash(ctypes.c_void_p(t.data_ptr() if nbytes else 0), nbytes, kw,
                                            ctypes.c_void_p(out.data_ptr()), sh)
     _check(rc, "blake3_gpu_keyed_hash")
+    return out
+
+
+def keyed_hash_noalloc(t: torch.Tensor, key, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """keyed_hash (key: 32 bytes) or hash (key None) through the entry point that allocates
+    nothing: its scratch is a fixed 1 MiB device array per GPU, shared by every such call
+    on that GPU, so calls that overlap on one GPU race (calls ordered on one stream do
+    not). Neither the binding nor the library allocates: t must be a contiguous, 16-byte
+    aligned device tensor (it is not copied) and out a contiguous 32-byte uint8 tensor on
+    its device. Inputs above 31.875 GiB raise Blake3GpuError (ESCRATCH)."""
+    _check_tensor(t)
+    if not t.is_contiguous() or (t.numel() and t.data_ptr() % 16 != 0):
+        raise ValueError("keyed_hash_noalloc copies nothing: t must be contiguous and 16-byte aligned")
+    if out is None:
+        raise ValueError("keyed_hash_noalloc allocates nothing: pass out (32 bytes)")
+    kw = _key_words(key) if key is not None else None
+    with _on(t.device, stream) as sh:
+        out = _out(out, t.device, 32)
+        nbytes = t.numel() * t.element_size()
+        rc = _load().blake3_gpu_keyed_hash_noalloc(ctypes.c_void_p(t.data_ptr() if nbytes else 0), nbytes, kw,
+                                                   ctypes.c_void_p(out.data_ptr()), sh)
+    _check(rc, "blake3_gpu_keyed_hash_noalloc")
     return out
 
 

@@ -9,6 +9,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <memory>
 #include <mutex>
 #include <vector>
@@ -18,10 +19,17 @@
 #include "b3_kernels.h"
 #include "b3_plan.h"
 
+// Scratch of the entry point that allocates nothing (blake3_gpu_keyed_hash_noalloc): a fixed
+// array of device memory. Each GPU the library runs on holds its own copy until the process
+// ends, and every such call on that GPU uses it. In host code this name stands for a
+// host-side shadow, not for device memory: the calling device's address of the array is
+// looked up once per device (fixed_scratch_address) and only that address reaches kernels.
+static __device__ __align__(256) uint8_t scratch[BLAKE3_GPU_NOALLOC_SCRATCH_BYTES];
+
 namespace b3g {
 namespace {
 
-constexpr int kAbiVersion = 1 * 10000 + 2 * 100 + 0;
+constexpr int kAbiVersion = 1 * 10000 + 3 * 100 + 0;
 
 // Stream-ordered scratch comes from one memory pool per device, created on first use and
 // kept for the life of the process, with a release threshold of "never" so that freed
@@ -226,6 +234,62 @@ class StreamScratch {
     DeviceSlots *slots_ = nullptr;
 };
 
+// Device address of `scratch` per device, looked up on the device's first no-allocation
+// call (with that device current) and kept.
+std::mutex g_fixed_mu;
+std::atomic<uint8_t *> g_fixed_ptr[kMaxDevices];
+
+int fixed_scratch_address(uint8_t **p) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return B3G_EHIP;
+    }
+    uint8_t *q = g_fixed_ptr[dev].load(std::memory_order_acquire);
+    if (q == nullptr) {
+        std::lock_guard<std::mutex> lock(g_fixed_mu);
+        q = g_fixed_ptr[dev].load(std::memory_order_relaxed);
+        if (q == nullptr) {
+            void *addr = nullptr;
+            if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) {
+                (void)hipGetLastError();
+                return B3G_EHIP;
+            }
+            q = static_cast<uint8_t *>(addr);
+            g_fixed_ptr[dev].store(q, std::memory_order_release);
+        }
+    }
+    *p = q;
+    return B3G_OK;
+}
+
+// Scratch of one hash: a slot or the pool (StreamScratch), or, for the entry point that
+// allocates nothing, the calling device's copy of the fixed array. A request larger than
+// that array fails with B3G_ESCRATCH before any HIP call.
+class CallScratch {
+  public:
+    CallScratch(hipStream_t s, bool fixed) : s_(s), fixed_(fixed), pooled_(s) {}
+    int alloc(size_t bytes) {
+        if (!fixed_) {
+            const int rc = pooled_.alloc(bytes);
+            p_ = pooled_.get();
+            return rc;
+        }
+        if (bytes > BLAKE3_GPU_NOALLOC_SCRATCH_BYTES) return B3G_ESCRATCH;
+        if (bytes == 0) return B3G_OK;
+        const int rc = fixed_scratch_address(&p_);
+        if (rc != B3G_OK) return rc;
+        return fill_scratch(p_, bytes, s_);
+    }
+    uint8_t *get() const { return p_; }
+
+  private:
+    hipStream_t s_;
+    bool fixed_;
+    StreamScratch pooled_;  // unused (never allocates) when fixed_
+    uint8_t *p_ = nullptr;
+};
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 int launched(hipError_t e) {
@@ -393,10 +457,11 @@ constexpr uint64_t kMaxGrid = 0xFFFFFFFFull / kLeafLanes;
 // message of at most `span` chunks is finished by the leaf pass, span/R messages per
 // workgroup. A longer one spans G leaf workgroups, whose CVs the level passes reduce,
 // 256 to a workgroup, until at most 256 remain, which one last pass finishes. Pass
-// outputs ping-pong between two CV arrays.
+// outputs ping-pong between two CV arrays, in scratch from the slots or the pool, or, with
+// `fixed`, in the fixed array (nothing is allocated).
 int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_msgs, const uint32_t *keys,
                  const uint32_t key[8], uint32_t mode, uint64_t chunk_base, uint32_t root_flag, uint8_t *out,
-                 hipStream_t s) {
+                 hipStream_t s, bool fixed = false) {
     if (n_msgs == 0) return B3G_OK;
     const uint64_t c = chunks_of(len);
     const uint64_t total = c > UINT64_MAX / n_msgs ? UINT64_MAX : c * n_msgs;  // chunks, saturated
@@ -450,7 +515,7 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
     const uint64_t per_launch = kMaxGrid / g;  // >= 1
     const uint64_t nb = n_msgs < per_launch ? n_msgs : per_launch;
     const uint64_t g1 = (g + kLevelLanes - 1) / kLevelLanes;
-    StreamScratch scratch(s);
+    CallScratch scratch(s, fixed);
 
     if (fused) {
         // One launch: the leaf workgroups reduce the levels themselves (last arrival of
@@ -554,12 +619,13 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
     return B3G_OK;
 }
 
-int hash_single(const void *in, uint64_t len, const uint32_t key[8], uint32_t mode, void *out, void *stream) {
+int hash_single(const void *in, uint64_t len, const uint32_t key[8], uint32_t mode, void *out, void *stream,
+                bool fixed = false) {
     if (out == nullptr || (in == nullptr && len > 0)) return B3G_EINVAL;
     if (reinterpret_cast<uintptr_t>(in) % 16 != 0) return B3G_EALIGN;
     if (len > kMaxMessageBytes) return B3G_ETOOBIG;
     return hash_uniform(static_cast<const uint8_t *>(in), 0, len, 1, nullptr, key, mode, 0, kRoot,
-                        static_cast<uint8_t *>(out), static_cast<hipStream_t>(stream));
+                        static_cast<uint8_t *>(out), static_cast<hipStream_t>(stream), fixed);
 }
 
 // The CV (no ROOT) of the subtree over all chunks of in[0 .. len), chunk counters from
@@ -820,6 +886,12 @@ int blake3_gpu_keyed_hash(const void *dev_in, uint64_t len, const uint32_t key[8
     return b3g::hash_single(dev_in, len, key, b3g::kKeyedHash, dev_out32, stream);
 }
 
+int blake3_gpu_keyed_hash_noalloc(const void *dev_in, uint64_t len, const uint32_t key[8], void *dev_out32,
+                                  void *stream) {
+    return b3g::hash_single(dev_in, len, key ? key : b3g::kIV, key ? b3g::kKeyedHash : 0u, dev_out32, stream,
+                            true);
+}
+
 int blake3_gpu_keyed_hash_batch(const void *dev_base, const uint64_t *host_offsets,
                                 const uint64_t *host_lengths, const uint32_t *dev_keys, void *dev_out,
                                 uint64_t n, void *stream) {
@@ -860,6 +932,8 @@ const char *blake3_gpu_strerror(int status) {
         case B3G_ENOMEM: return "scratch allocation failed";
         case B3G_EHIP: return "HIP runtime call or kernel launch failed";
         case B3G_ETOOBIG: return "request exceeds the supported size";
+        case B3G_ESCRATCH:
+            return "the input needs more scratch than the fixed array of the no-allocation entry point holds";
         default: return "unknown status";
     }
 }

@@ -60,10 +60,14 @@ typedef enum {
     B3G_ENOMEM = -3,  /* scratch allocation failed */
     B3G_EHIP = -4,    /* a HIP runtime call or a kernel launch failed (incl. no device) */
     B3G_ETOOBIG = -5, /* the request exceeds what the planner represents (see below) */
+    B3G_ESCRATCH = -6, /* blake3_gpu_keyed_hash_noalloc: the input needs more scratch than
+                          its fixed array holds */
 } b3g_status;
 
 #define BLAKE3_GPU_KEY_WORDS 8
 #define BLAKE3_GPU_OUT_LEN 32
+/* Bytes of the fixed device array per GPU that blake3_gpu_keyed_hash_noalloc uses. */
+#define BLAKE3_GPU_NOALLOC_SCRATCH_BYTES (1u << 20)
 
 /*
  * Default-mode BLAKE3 of dev_in[0 .. len).
@@ -86,6 +90,30 @@ int blake3_gpu_hash(const void *dev_in, uint64_t len, void *dev_out32, void *str
  */
 int blake3_gpu_keyed_hash(const void *dev_in, uint64_t len, const uint32_t key[8], void *dev_out32,
                           void *stream);
+
+/*
+ * For callers that cannot allocate memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): blake3_gpu_keyed_hash (key != NULL) or blake3_gpu_hash
+ * (key == NULL, default mode) with the same kernels and the same digests, that allocates
+ * nothing. It calls no hipMalloc, hipFree, memory pool, event or pinned-buffer routine:
+ * the chaining values between its launches live in a fixed array of
+ * BLAKE3_GPU_NOALLOC_SCRATCH_BYTES (1 MiB) of device memory that the library holds on each
+ * GPU it runs on until the process ends, instead of the scratch slots and pool of the other
+ * entry points. The first call on a device looks up that device's address of the array
+ * (hipGetSymbolAddress).
+ *   Limit: the level CVs of the input must fit the array. In the default configuration
+ *   that is at most 32,640 leaf workgroups of 1024 chunks: len <= 34,225,520,640 bytes
+ *   (31.875 GiB). A larger input returns B3G_ESCRATCH before any HIP call.
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps the last call's
+ *   contents (no call depends on them: it writes every word it reads, and clears what must
+ *   start at zero). Calls ordered on one stream are safe; calls that overlap on one GPU
+ *   (unordered streams, host threads, or concurrently replayed graphs) race and may return
+ *   wrong digests.
+ * Arguments as blake3_gpu_keyed_hash, except that key may be NULL. Errors: EINVAL, EALIGN,
+ * ETOOBIG, ESCRATCH, EHIP (never ENOMEM).
+ */
+int blake3_gpu_keyed_hash_noalloc(const void *dev_in, uint64_t len, const uint32_t key[8], void *dev_out32,
+                                  void *stream);
 
 /*
  * Many independent messages in one call: message i is

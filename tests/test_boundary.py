@@ -151,8 +151,27 @@ def test_forced_scratch_failure_returns_enomem_before_any_hip_call(monkeypatch):
     assert lib.blake3_gpu_hash(MISALIGNED, 1 << 20, ALIGNED, None) == b3.EALIGN  # checks come first
 
 
+def test_noalloc_refuses_inputs_beyond_its_fixed_scratch_before_any_hip_call():
+    # the fixed array (1 MiB) holds the level CVs of at most 32,640 leaf workgroups of 1024
+    # chunks: one byte more is refused before any HIP call (the pointers are never
+    # dereferenced); at the limit the call goes on to the device (no device here: EHIP)
+    lib = b3._load()
+    fake = ctypes.c_void_p(1 << 20)
+    key = (ctypes.c_uint32 * 8)()
+    limit = 32640 * 1024 * 1024
+    assert lib.blake3_gpu_keyed_hash_noalloc(fake, limit + 1, key, fake, None) == b3.ESCRATCH
+    assert lib.blake3_gpu_keyed_hash_noalloc(fake, limit + 1, None, fake, None) == b3.ESCRATCH
+    assert lib.blake3_gpu_keyed_hash_noalloc(fake, 1 << 42, key, fake, None) == b3.ESCRATCH
+    assert lib.blake3_gpu_keyed_hash_noalloc(fake, (1 << 42) + 1, key, fake, None) == b3.ETOOBIG
+    if not torch.cuda.is_available():
+        assert lib.blake3_gpu_keyed_hash_noalloc(fake, limit, key, fake, None) == b3.EHIP
+    assert lib.blake3_gpu_keyed_hash_noalloc(None, 5, key, fake, None) == b3.EINVAL
+    assert lib.blake3_gpu_keyed_hash_noalloc(fake, 5, key, None, None) == b3.EINVAL
+    assert lib.blake3_gpu_keyed_hash_noalloc(ctypes.c_void_p(MISALIGNED), 5, key, fake, None) == b3.EALIGN
+
+
 def test_strerror_and_version():
-    for code in (b3.OK, b3.EINVAL, b3.EALIGN, b3.ENOMEM, b3.EHIP, b3.ETOOBIG):
+    for code in (b3.OK, b3.EINVAL, b3.EALIGN, b3.ENOMEM, b3.EHIP, b3.ETOOBIG, b3.ESCRATCH):
         assert b3.strerror(code) and b3.strerror(code) != "unknown status"
     assert b3.strerror(12345) == "unknown status"
     assert b3.version() >= 10000
