@@ -74,6 +74,8 @@ def _load():
     lib.blake3_gpu_strerror.argtypes = [ctypes.c_int]
     lib.blake3_gpu_strerror.restype = ctypes.c_char_p
     lib.blake3_gpu_version.argtypes = []
+    lib.blake3_gpu_debug_reload_env.argtypes = []
+    lib.blake3_gpu_debug_reload_env.restype = ctypes.c_int
     lib.debug_plan = lib.blake3_gpu_debug_plan_batch
     lib.debug_plan.argtypes = [ctypes.POINTER(u64), u64, ctypes.POINTER(u64), u64]
     lib.debug_plan.restype = ctypes.c_int64
@@ -161,6 +163,17 @@ def _u64_array(v, what):
         return np.asarray(v, dtype=np.uint64).reshape(-1)
     except OverflowError:
         raise ValueError(f"{what} must be non-negative 64-bit integers") from None
+
+
+_U64_LIMIT = 1 << 64
+
+
+def _u64(v, what):
+    """A non-negative integer below 2^64 (ctypes would silently reduce larger ones mod 2^64)."""
+    v = int(v)
+    if v < 0 or v >= _U64_LIMIT:
+        raise ValueError(f"{what} must be in [0, 2^64)")
+    return v
 
 
 def _out(out, device, n):
@@ -265,10 +278,10 @@ def hash_xof(t: torch.Tensor, key=None, out_len: int = 32, out=None, stream=None
     """Extendable output: bytes [offset, offset + out_len) of the root node's output stream
     for the tensor's bytes (key: 32 bytes for keyed mode, None for default mode); a uint8
     device tensor. Bytes 0..31 of the stream are the hash."""
+    out_len, offset = _u64(out_len, "out_len"), _u64(offset, "offset")
+    if offset + out_len > _U64_LIMIT:
+        raise ValueError("the output stream is 2^64 bytes: offset + out_len must not exceed 2^64")
     _check_tensor(t)
-    out_len, offset = int(out_len), int(offset)
-    if out_len < 0 or offset < 0:
-        raise ValueError("out_len and offset must be non-negative")
     kw = _key_words(key) if key is not None else None
     with _on(t.device, stream) as sh:
         t = _aligned(t)
@@ -283,6 +296,7 @@ def hash_xof(t: torch.Tensor, key=None, out_len: int = 32, out=None, stream=None
 def subtree_cv(t: torch.Tensor, key=None, chunk_base: int = 0, out=None, stream=None) -> torch.Tensor:
     """CV (no ROOT) of the subtree over all chunks of the tensor's bytes, chunk counters
     from chunk_base: an (8,) int32 device tensor of little-endian words."""
+    chunk_base = _u64(chunk_base, "chunk_base")
     _check_tensor(t)
     if out is not None and (out.device != t.device or out.numel() * out.element_size() != 32
                             or not out.is_contiguous()):
@@ -309,6 +323,7 @@ def group_cvs(t: torch.Tensor, key=None, chunk_base: int = 0, group_chunks: int 
     """CVs (no ROOT) of the aligned groups of group_chunks chunks (64: the small-input leaf
     with four lanes per chunk; 256, 512 or 1024) of the tensor's bytes, chunk counters
     starting at chunk_base: a (groups, 8) int32 device tensor of little-endian words."""
+    chunk_base = _u64(chunk_base, "chunk_base")
     _check_tensor(t)
     nbytes = t.numel() * t.element_size()
     if nbytes == 0:

@@ -89,6 +89,10 @@ struct ScratchSlot {
 struct DeviceSlots {
     std::mutex mu;
     ScratchSlot slot[kSlotsPerDevice];
+    // Memory of slots that outgrew it. It is never freed: hipFree waits for every stream of
+    // the device, and a call must not. A slot grows in powers of two up to kSlotMaxBytes,
+    // so what is kept this way stays below that per slot.
+    std::vector<void *> retired;
 };
 DeviceSlots g_slots[kMaxDevices];
 
@@ -187,11 +191,9 @@ class StreamScratch {
             return release_unused(ds, sl);
         }
         if (sl->bytes < bytes) {  // grow an idle slot (its last call's work has finished)
-            if (sl->p != nullptr && hipFree(sl->p) != hipSuccess) {
-                (void)hipGetLastError();
-                sl->p = nullptr;
-                sl->bytes = 0;
-                return release_unused(ds, sl);
+            if (sl->p != nullptr) {
+                std::lock_guard<std::mutex> lock(ds.mu);
+                ds.retired.push_back(sl->p);
             }
             sl->p = nullptr;
             sl->bytes = 0;
@@ -321,9 +323,11 @@ struct HostStage {
 };
 struct DeviceStages {
     std::mutex mu;
-    bool arena_tried = false;  // one pinned allocation for every buffer's first size: a pinned
-                               // allocation can wait for the device, so it is made once
+    bool arena_tried = false;  // one pinned allocation for every buffer's first size, made once
     HostStage stage[kStagesPerDevice];
+    // Buffers that were outgrown. Never freed: hipHostFree waits for every stream of the
+    // device, and a call must not.
+    std::vector<void *> retired;
 };
 DeviceStages g_stages[kMaxDevices];
 
@@ -359,7 +363,7 @@ class TableStage {
                     }
                 } else {
                     (void)hipGetLastError();
-                    if (a != nullptr) (void)hipHostFree(a);
+                    if (a != nullptr) ds.retired.push_back(a);  // unusable; freeing it would wait for the device
                 }
             }
             int best = -1;
@@ -391,7 +395,10 @@ class TableStage {
             return release();
         }
         if (st->bytes < bytes) {
-            if (st->own) (void)hipHostFree(st->p);  // idle: no upload reads it
+            if (st->own) {  // idle (no upload reads it), but freeing it would wait for the device
+                std::lock_guard<std::mutex> lock(ds.mu);
+                ds.retired.push_back(st->p);
+            }
             st->p = st->dev = nullptr;
             st->bytes = 0;
             st->own = false;
@@ -404,7 +411,8 @@ class TableStage {
             }
             if (hipHostGetDevicePointer(&dp, p, 0) != hipSuccess || dp == nullptr) {
                 (void)hipGetLastError();
-                (void)hipHostFree(p);
+                std::lock_guard<std::mutex> lock(ds.mu);
+                ds.retired.push_back(p);  // unusable, and freeing it would wait for the device
                 return release();
             }
             st->p = p;
@@ -649,7 +657,8 @@ int subtree_cv(const void *in, uint64_t len, uint64_t chunk_base, const uint32_t
 int hash_xof(const void *in, uint64_t len, const uint32_t *key, uint64_t out_offset, void *out, uint64_t out_len,
              void *stream) {
     if ((out == nullptr && out_len > 0) || (in == nullptr && len > 0)) return B3G_EINVAL;
-    if (out_offset + out_len < out_offset) return B3G_EINVAL;
+    // the stream is 2^64 bytes: the request may end at byte 2^64, not beyond
+    if (out_len > 0 && out_len - 1 > UINT64_MAX - out_offset) return B3G_EINVAL;
     if (reinterpret_cast<uintptr_t>(in) % 16 != 0) return B3G_EALIGN;
     if (len > kMaxMessageBytes || out_len > kMaxXofBytes) return B3G_ETOOBIG;
     if (out_len == 0) return B3G_OK;
@@ -939,6 +948,11 @@ const char *blake3_gpu_strerror(int status) {
 }
 
 int blake3_gpu_version(void) { return b3g::kAbiVersion; }
+
+int blake3_gpu_debug_reload_env(void) {
+    b3g::reload_options();
+    return B3G_OK;
+}
 
 int64_t blake3_gpu_debug_plan_batch(const uint64_t *host_lengths, uint64_t n, uint64_t *out,
                                     uint64_t out_words) {

@@ -1146,16 +1146,18 @@ __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
         o[w] = v[w] ^ v[w + 8];
         o[w + 8] = v[w + 8] ^ cv[w];
     }
-    // stream bytes [s0, s0 + 64) of this block, clipped to [out_offset, end)
-    const uint64_t s0 = kBlockBytes * t, end = a.out_offset + a.out_len;
+    // stream bytes [s0, s0 + 64) of this block, clipped to [out_offset, last], `last` being
+    // the request's last byte (out_len >= 1 and the request ends at byte 2^64 at the
+    // latest, so computing it does not wrap). Every launched block starts at or before
+    // `last`, so last - s0 never wraps, where s0 + 64 or the request's end would for the
+    // last block of the 2^64-byte stream.
+    const uint64_t s0 = kBlockBytes * t, last = a.out_offset + (a.out_len - 1);
     // the wave path (the condition is the same for all lanes of the wave: a wave with
     // lanes past n_blocks, which returned above, never takes it)
     __shared__ uint4 xo[kXofLanes / 64][256];
     const uint64_t w0 = static_cast<uint64_t>(blockIdx.x) * kXofLanes + (threadIdx.x & ~63u);
     const uint64_t ws0 = kBlockBytes * (a.first_block + w0);
-    // (every launched block starts before `end`, so end - s0 never wraps, where s0 + 64
-    // would for the last block of the 2^64-byte stream)
-    if (w0 + 64 <= a.n_blocks && ws0 >= a.out_offset && end - ws0 >= 64 * kBlockBytes &&
+    if (w0 + 64 <= a.n_blocks && ws0 >= a.out_offset && last - ws0 >= 64 * kBlockBytes - 1 &&
         (reinterpret_cast<uintptr_t>(a.out) - a.out_offset) % 16 == 0) {
         const uint32_t wv = threadIdx.x >> 6, ln = threadIdx.x & 63u;
         uint4 *row = xo[wv];
@@ -1170,7 +1172,7 @@ __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
         for (int q = 0; q < 4; ++q) d[64 * q + ln] = row[64 * q + ln];
         return;
     }
-    if (s0 >= a.out_offset && end - s0 >= kBlockBytes &&
+    if (s0 >= a.out_offset && last - s0 >= kBlockBytes - 1 &&
         reinterpret_cast<uintptr_t>(a.out + (s0 - a.out_offset)) % 16 == 0) {
         uint4 *d = reinterpret_cast<uint4 *>(a.out + (s0 - a.out_offset));
         d[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -1178,11 +1180,13 @@ __global__ __launch_bounds__(kXofLanes) void xof_expand_kernel(XofArgs a) {
         d[2] = make_uint4(o[8], o[9], o[10], o[11]);
         d[3] = make_uint4(o[12], o[13], o[14], o[15]);
     } else {
+        // stream bytes lo .. hi (inclusive) of this block: 1 to 64 of them
         const uint64_t lo = s0 > a.out_offset ? s0 : a.out_offset;
-        const uint64_t hi = end - s0 > kBlockBytes ? s0 + kBlockBytes : end;
-        for (uint64_t x = lo; x < hi; ++x) {
-            const uint32_t k = static_cast<uint32_t>(x - s0);
-            a.out[x - a.out_offset] = static_cast<uint8_t>(o[k / 4] >> (8 * (k % 4)));
+        const uint64_t hi = last - s0 > kBlockBytes - 1 ? s0 + (kBlockBytes - 1) : last;
+        const uint32_t count = static_cast<uint32_t>(hi - lo) + 1;
+        for (uint32_t i = 0; i < count; ++i) {
+            const uint32_t k = static_cast<uint32_t>(lo - s0) + i;
+            a.out[lo - a.out_offset + i] = static_cast<uint8_t>(o[k / 4] >> (8 * (k % 4)));
         }
     }
 }

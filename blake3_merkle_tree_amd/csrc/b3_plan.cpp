@@ -28,7 +28,9 @@
 #include "b3_plan.h"
 
 #include <stdlib.h>
+#include <string.h>
 
+#include <atomic>
 #include <memory>
 
 
@@ -70,13 +72,65 @@ inline void for_each_group(uint64_t nodes, uint64_t first0, uint32_t per_node_sh
 }
 }  // namespace
 
+// The BLAKE3_GPU_* test hooks, read from the environment once when the library is loaded
+// (and again on reload_options), so that no call reads the environment.
+namespace {
+struct Options {
+    std::atomic<uint32_t> chunks_per_lane{0};  // 0: chosen by input size
+    std::atomic<uint64_t> quad_leaf_max_chunks{kQuadLeafMaxChunksDefault};
+    std::atomic<uint64_t> scratch_limit{UINT64_MAX};
+    std::atomic<int> scratch_fill{-1};
+    std::atomic<bool> fused_levels{false};
+    std::atomic<bool> batch_table{false};
+    std::atomic<bool> lds_staging{false};
+};
+Options g_options;
+
+bool env_is(const char *name, const char *value) {
+    const char *e = getenv(name);
+    return e != nullptr && strcmp(e, value) == 0;
+}
+
+void read_options() {
+    Options &o = g_options;
+    uint32_t k = 0;
+    if (const char *e = getenv("BLAKE3_GPU_CHUNKS_PER_LANE")) {
+        const int v = atoi(e);
+        if (v == 1 || v == 2 || v == 4) k = static_cast<uint32_t>(v);
+    }
+    o.chunks_per_lane.store(k, std::memory_order_relaxed);
+    const char *q = getenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS");
+    o.quad_leaf_max_chunks.store(q ? strtoull(q, nullptr, 10) : kQuadLeafMaxChunksDefault, std::memory_order_relaxed);
+    const char *lim = getenv("BLAKE3_GPU_SCRATCH_LIMIT");
+    o.scratch_limit.store(lim == nullptr || lim[0] < '0' || lim[0] > '9' ? UINT64_MAX : strtoull(lim, nullptr, 10),
+                          std::memory_order_relaxed);
+    int fill = -1;
+    if (const char *f = getenv("BLAKE3_GPU_SCRATCH_FILL")) {
+        if (f[0] != 0) {
+            char *end = nullptr;
+            const long v = strtol(f, &end, 0);
+            if (*end == 0 && v >= 0 && v <= 255) fill = static_cast<int>(v);
+        }
+    }
+    o.scratch_fill.store(fill, std::memory_order_relaxed);
+    // Off by default: measured on MI355X, the fused form is slower than separate level
+    // launches on every input size.
+    o.fused_levels.store(env_is("BLAKE3_GPU_FUSED_LEVELS", "1"), std::memory_order_relaxed);
+    o.batch_table.store(env_is("BLAKE3_GPU_BATCH_TABLE", "1"), std::memory_order_relaxed);
+    o.lds_staging.store(env_is("BLAKE3_GPU_STAGING", "lds"), std::memory_order_relaxed);
+}
+
+struct ReadAtLoad {
+    ReadAtLoad() { read_options(); }
+} g_read_at_load;
+}  // namespace
+
+void reload_options() { read_options(); }
+
 uint64_t chunks_of(uint64_t len) { return len == 0 ? 1 : (len + 1023) / 1024; }
 
 uint32_t choose_chunks_per_lane(uint64_t total_chunks) {
-    if (const char *e = getenv("BLAKE3_GPU_CHUNKS_PER_LANE")) {
-        const int k = atoi(e);
-        if (k == 1 || k == 2 || k == 4) return static_cast<uint32_t>(k);
-    }
+    if (const uint32_t k = g_options.chunks_per_lane.load(std::memory_order_relaxed)) return k;
     // Four chunks per lane from 2 GiB of input: it cuts the lane-sparse top of each
     // workgroup tree and the fold work by 4x once the 1024-chunk workgroups are many rounds
     // of the chip. Measured on MI355X (ms at K = 1 / 2 / 4): 512 MiB 0.197 / 0.197 / 0.206,
@@ -86,42 +140,12 @@ uint32_t choose_chunks_per_lane(uint64_t total_chunks) {
     return 1;
 }
 
-uint64_t quad_leaf_max_chunks() {
-    if (const char *e = getenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS")) return strtoull(e, nullptr, 10);
-    return kQuadLeafMaxChunksDefault;
-}
-
-uint64_t scratch_limit() {
-    const char *e = getenv("BLAKE3_GPU_SCRATCH_LIMIT");
-    if (e == nullptr || e[0] < '0' || e[0] > '9') return UINT64_MAX;
-    return strtoull(e, nullptr, 10);
-}
-
-int scratch_fill_byte() {
-    const char *e = getenv("BLAKE3_GPU_SCRATCH_FILL");
-    if (e == nullptr || e[0] == 0) return -1;
-    char *end = nullptr;
-    const long v = strtol(e, &end, 0);
-    return (*end == 0 && v >= 0 && v <= 255) ? static_cast<int>(v) : -1;
-}
-
-bool fused_levels_enabled() {
-    // Off by default: measured on MI355X, the ticket zeroing launch and each workgroup's
-    // wait for its coherent stores and ticket cost more than the level launches they
-    // replace (4 GiB: 1.369 vs 1.351 ms; 1 MiB: 37.0 vs 31.6 us; 256 MiB: 122 vs 113 us).
-    const char *e = getenv("BLAKE3_GPU_FUSED_LEVELS");
-    return e != nullptr && e[0] == '1' && e[1] == 0;
-}
-
-bool uniform_batch_disabled() {
-    const char *e = getenv("BLAKE3_GPU_BATCH_TABLE");
-    return e != nullptr && e[0] == '1' && e[1] == 0;
-}
-
-bool use_lds_staging() {
-    const char *e = getenv("BLAKE3_GPU_STAGING");
-    return e != nullptr && e[0] == 'l' && e[1] == 'd' && e[2] == 's' && e[3] == 0;
-}
+uint64_t quad_leaf_max_chunks() { return g_options.quad_leaf_max_chunks.load(std::memory_order_relaxed); }
+uint64_t scratch_limit() { return g_options.scratch_limit.load(std::memory_order_relaxed); }
+int scratch_fill_byte() { return g_options.scratch_fill.load(std::memory_order_relaxed); }
+bool fused_levels_enabled() { return g_options.fused_levels.load(std::memory_order_relaxed); }
+bool uniform_batch_disabled() { return g_options.batch_table.load(std::memory_order_relaxed); }
+bool use_lds_staging() { return g_options.lds_staging.load(std::memory_order_relaxed); }
 
 uint32_t ceil_log2_host(uint64_t n) {
     return n <= 1 ? 0u : 64u - static_cast<uint32_t>(__builtin_clzll(n - 1));

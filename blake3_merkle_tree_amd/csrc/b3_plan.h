@@ -88,6 +88,10 @@ int scratch_fill_byte();    // -1 when unset
 // table like any other batch (for tests).
 bool uniform_batch_disabled();
 
+// The BLAKE3_GPU_* variables above are read from the environment once, when the library
+// is loaded; reload_options() reads them again (tests and tools change them between calls).
+void reload_options();
+
 // Builds the passes for messages of the given byte lengths. Pass 0 groups
 // leaf_lanes * chunks_per_lane chunks per workgroup (one node per lane); later passes
 // group level_lanes CVs. Returns 0 (B3G_OK) or a negative b3g_status (B3G_ETOOBIG when a

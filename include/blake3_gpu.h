@@ -24,9 +24,10 @@
  *  - Scratch (chaining values of intermediate tree levels, the batch task table) is
  *    library-owned device memory. Up to 64 MiB per call comes from a few slots per device
  *    that the library allocates on first use, grows when needed and keeps for the life of
- *    the process: a call makes `stream` wait (on the device, not the host) until the
- *    slot's previous call has finished with it, and records its own completion for the
- *    next. Larger requests, calls that find every slot in use by other host threads, and
+ *    the process (memory a slot outgrows is kept too, never freed: freeing device or
+ *    pinned memory would wait for every stream of the device): a call makes `stream` wait
+ *    (on the device, not the host) until the slot's previous call has finished with it,
+ *    and records its own completion for the next. Larger requests, calls that find every slot in use by other host threads, and
  *    calls on a stream under graph capture allocate and free their scratch in stream order
  *    on `stream` from a memory pool the library keeps per device. Calls on different
  *    streams and host threads may overlap; entry points are thread-safe.
@@ -70,7 +71,8 @@ typedef enum {
 #define BLAKE3_GPU_NOALLOC_SCRATCH_BYTES (1u << 20)
 
 /*
- * Default-mode BLAKE3 of dev_in[0 .. len).
+ * Default-mode BLAKE3 of dev_in[0 .. len) (page, section "BLAKE3": without a key every
+ * chunk and parent compression starts from the IV, and no mode flag is set).
  *   dev_in     device pointer, 16-byte aligned; may be NULL only when len == 0.
  *   len        byte count, 0 .. 2^42 (4 TiB; ETOOBIG above, so chunk indices fit 32 bits).
  *   dev_out32  device pointer to 32 writable bytes; receives the digest.
@@ -116,7 +118,8 @@ int blake3_gpu_keyed_hash_noalloc(const void *dev_in, uint64_t len, const uint32
                                   void *stream);
 
 /*
- * Many independent messages in one call: message i is
+ * Many independent messages in one call (page, introduction: hashing many messages at once
+ * is the common way to use a GPU; here each message gets its own tree): message i is
  * dev_base[host_offsets[i] .. host_offsets[i] + host_lengths[i]), hashed with its own key
  * and its own tree (counters restart at 0, each message gets its own ROOT).
  *   dev_base      device pointer, 16-byte aligned; may be NULL only if every length is 0.
@@ -183,9 +186,10 @@ int blake3_gpu_hash_xof(const void *dev_in, uint64_t len, const uint32_t key[8],
  * (BLAKE3 specification, extendable output: block t of the stream depends only on t, so no
  * earlier block is computed). blake3_gpu_hash_xof is the case out_offset == 0. Useful for
  * consumers that each take a slice of one long output stream.
- *   out_offset  any byte offset; out_offset + out_len must not exceed 2^64 - 1.
+ *   out_offset  any byte offset; out_offset + out_len must not exceed 2^64 (the stream's
+ *               last byte is byte 2^64 - 1).
  * Other arguments as blake3_gpu_hash_xof. Errors: as blake3_gpu_hash_xof, and EINVAL when
- * out_offset + out_len overflows 64 bits.
+ * out_offset + out_len exceeds 2^64.
  */
 int blake3_gpu_hash_xof_at(const void *dev_in, uint64_t len, const uint32_t key[8], uint64_t out_offset,
                            void *dev_out, uint64_t out_len, void *stream);
@@ -235,13 +239,24 @@ int blake3_gpu_version(void);
  * as uint64 words:
  *   [passes] then per pass [lanes, chunks per lane K, workgroups W, segments S, in_cvs,
  *   out_cvs, W+1 first-segment indices, W level counts, S x (msg, first, dst, info)].
- * Segment info packs bits 0..11 lane start, 12..23 node count - 1, 31 final. In pass 0 a
- * node is a lane's run of K chunks and `first` a chunk index; later nodes are CVs.
+ * Segment info packs bits 0..11 lane start, 12..23 node count - 1, 30 pair, 31 final. In
+ * pass 0 a node is a lane's run of K chunks and `first` a chunk index; later nodes are
+ * CVs. Pair: the segment's last node is the parent of input CVs first + count - 1 and
+ * first + count (the two halves of a message end that pass 0 split in two subtrees).
  * Returns the number of words the plan needs (nothing is written if out_words is
  * smaller), or a negative b3g_status (EINVAL for NULL lengths with n > 0, ETOOBIG).
  */
 int64_t blake3_gpu_debug_plan_batch(const uint64_t *host_lengths, uint64_t n, uint64_t *out,
                                     uint64_t out_words);
+
+/*
+ * Test hooks. The library reads its BLAKE3_GPU_* environment variables (leaf and input-path
+ * overrides, forced scratch failure and fill, and the like) once, when it is loaded, so no
+ * call reads the environment. This reads them again, for tests and tools that change them
+ * between calls; it must not run while another call of the library is running. No GPU
+ * work, no HIP call. Returns B3G_OK.
+ */
+int blake3_gpu_debug_reload_env(void);
 
 #ifdef __cplusplus
 }

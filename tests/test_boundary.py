@@ -79,6 +79,11 @@ def test_subtree_and_xof_argument_checks():
     assert lib.blake3_gpu_hash_xof_at(MISALIGNED, 5, None, 7, ALIGNED, 10, None) == b3.EALIGN
     assert lib.blake3_gpu_hash_xof_at(ALIGNED, 5, None, 7, ALIGNED, (1 << 42) + 1, None) == b3.ETOOBIG
     assert lib.blake3_gpu_hash_xof_at(ALIGNED, 5, None, (1 << 64) - 1, None, 0, None) == b3.OK
+    # a request may end at byte 2^64 (the stream's last byte is 2^64 - 1), not one past it
+    assert lib.blake3_gpu_hash_xof_at(ALIGNED, 5, None, (1 << 64) - 10, ALIGNED, 11, None) == b3.EINVAL
+    assert lib.blake3_gpu_hash_xof_at(ALIGNED, 5, None, (1 << 64) - 1, ALIGNED, 2, None) == b3.EINVAL
+    for off, n in (((1 << 64) - 10, 10), ((1 << 64) - 1, 1)):
+        assert lib.blake3_gpu_hash_xof_at(MISALIGNED, 5, None, off, ALIGNED, n, None) == b3.EALIGN  # range ok
 
 
 def test_group_cvs_argument_checks_and_leaf_group_size(monkeypatch):
@@ -170,11 +175,51 @@ def test_noalloc_refuses_inputs_beyond_its_fixed_scratch_before_any_hip_call():
     assert lib.blake3_gpu_keyed_hash_noalloc(ctypes.c_void_p(MISALIGNED), 5, key, fake, None) == b3.EALIGN
 
 
+def test_environment_hooks_are_read_at_load_and_on_reload():
+    # no call reads the environment: a change takes effect only when the library is asked
+    # to read it again (plain os.environ here, not the test suite's reloading monkeypatch)
+    lib = b3._load()
+    name = "BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS"
+    saved = os.environ.pop(name, None)
+    lib.blake3_gpu_debug_reload_env()
+    try:
+        assert lib.blake3_gpu_leaf_group_chunks(1 << 20) == 64
+        os.environ[name] = "0"
+        assert lib.blake3_gpu_leaf_group_chunks(1 << 20) == 64  # still what was read before
+        assert lib.blake3_gpu_debug_reload_env() == b3.OK
+        assert lib.blake3_gpu_leaf_group_chunks(1 << 20) == 256
+    finally:
+        os.environ.pop(name, None)
+        if saved is not None:
+            os.environ[name] = saved
+        lib.blake3_gpu_debug_reload_env()
+
+
 def test_strerror_and_version():
     for code in (b3.OK, b3.EINVAL, b3.EALIGN, b3.ENOMEM, b3.EHIP, b3.ETOOBIG, b3.ESCRATCH):
         assert b3.strerror(code) and b3.strerror(code) != "unknown status"
     assert b3.strerror(12345) == "unknown status"
     assert b3.version() >= 10000
+
+
+def test_python_binding_range_checks_64_bit_arguments():
+    # ctypes reduces Python ints mod 2^64 without complaint: the binding refuses values a
+    # uint64 cannot hold, before it looks at the tensor
+    t = torch.zeros(16, dtype=torch.uint8)
+    for call in (lambda: b3._u64(1 << 64, "x"), lambda: b3._u64(-1, "x")):
+        with pytest.raises(ValueError):
+            call()
+    assert b3._u64((1 << 64) - 1, "x") == (1 << 64) - 1
+    with pytest.raises(ValueError, match="2\\^64"):
+        b3.hash_xof(t, None, 32, offset=(1 << 64) + 5)
+    with pytest.raises(ValueError, match="2\\^64"):
+        b3.hash_xof(t, None, 11, offset=(1 << 64) - 10)
+    with pytest.raises(ValueError, match="2\\^64"):
+        b3.subtree_cv(t, None, chunk_base=1 << 64)
+    with pytest.raises(ValueError, match="2\\^64"):
+        b3.group_cvs(t, None, chunk_base=(1 << 64) + 7)
+    with pytest.raises(ValueError, match="HIP device"):  # in range: on to the tensor check
+        b3.hash_xof(t, None, 10, offset=(1 << 64) - 10)
 
 
 def test_python_binding_rejects_host_tensors_and_bad_keys():

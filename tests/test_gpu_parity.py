@@ -672,13 +672,16 @@ def test_xof_from_an_offset_matches_oracle(b3, dev, keyed):
         _say("xof at", off, "length", n, "input", L, "keyed", keyed)
         got = bytes(b3.hash_xof(buf[:L], key, n, offset=off).cpu().numpy().tobytes())
         assert got == oracle.hash_xof(host[:L].tobytes(), key, n, offset=off), (L, off, n)
-    # the end of the 2^64-byte stream, where a block's start + 64 wraps: a request ends at
-    # byte 2^64 - 2 at most, so the last block is never whole; nothing is written past the
-    # requested bytes (a guard of 64 bytes after them), and a whole wave just below the top
-    # goes through the wave-wide stores
+    # the end of the 2^64-byte stream, where a block's start + 64 wraps: requests that stop
+    # short of the end and requests that reach it; nothing is written past the requested
+    # bytes (a guard of 64 bytes after them), and a whole wave just below the top goes
+    # through the wave-wide stores
     top = 1 << 64
     for off, n in ((top - 4096, 4095), (top - 8192, 8191), (top - 65, 64), (top - 64, 63),
-                   (top - 64 * 300 - 5, 64 * 300 + 4), (top - 2, 1)):
+                   (top - 64 * 300 - 5, 64 * 300 + 4), (top - 2, 1),
+                   # requests that end exactly at byte 2^64, the stream's end: its last byte
+                   # is written, by the per-byte, the whole-block and the wave-wide stores
+                   (top - 1, 1), (top - 5, 5), (top - 64, 64), (top - 4096, 4096), (top - 64 * 300 - 5, 64 * 300 + 5)):
         _say("xof at the top of the stream", off, "length", n, "keyed", keyed)
         guard = torch.full((n + 64,), 7, dtype=torch.uint8, device=dev)
         b3.hash_xof(buf[:5123], key, n, out=guard[:n], offset=off)
