@@ -9,11 +9,13 @@ step runs for --warmup-seconds of wall time (the GPU's clock and power settle on
 ~100 ms of this load). The K timed steps run back to back on one stream with a HIP event
 between consecutive steps. Prints ONE JSON line on stdout:
   value         input bytes / 1e9 / median seconds per step (GB/s), whole job, one GPU
-  ms_per_step   the median step; ms_per_step_min and ms_per_step_mean beside it
+  ms_per_step   the median step; ms_per_step_min and ms_per_step_mean beside it, and
+                ms_per_step_back_to_back: K more steps with no event between them
   roofline      the dominant kernel (the leaf pass: chunk compression + fused in-workgroup
-                tree), timed alone right after the chain with HIP events on the stream it
-                runs on (median launch), against the integer-VALU peak (it is ALU-bound;
-                the HBM figure is reported beside it)
+                tree), timed alone with HIP events on the stream it runs on, each launch
+                alternating with a whole step so that it runs in the chain's clock and
+                power state (median launch), against the integer-VALU peak (it is
+                ALU-bound; the HBM figure is reported beside it)
   gpu_state     gfx clock, temperatures and power read from the GPU's sysfs files while
                 the timed steps ran
   cpu_baseline  the CPU oracle on the host's threads over the same bytes, plus one thread
@@ -241,6 +243,32 @@ def timed_steps(torch, stream, step, k, sensors=None):
     return per, evs[0].elapsed_time(evs[k]), wall, samples
 
 
+def timed_pairs(torch, stream, a, b, k):
+    """k pairs (a, b) back to back on `stream`, HIP events around every `a`: the times of
+    the a's (ms), each run in the clock and power state that alternating with b sets."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * k)]
+    torch.cuda.synchronize()
+    for i in range(k):
+        evs[2 * i].record(stream)
+        a()
+        evs[2 * i + 1].record(stream)
+        b()
+    torch.cuda.synchronize()
+    return [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(k)]
+
+
+def back_to_back(torch, stream, step, k):
+    """Mean time (ms) of k steps with no event between them."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(k):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / k
+
+
 def step_stats(per, total, k):
     return {"median": statistics.median(per), "min": min(per), "mean": total / k}
 
@@ -434,6 +462,8 @@ def main():
         f"wall {wall:.3f} s for {args.steps} steps after {warm} warm-up steps")
     gpu_state = sensors.summary(samples)
     log(f"gpu state during the timed steps: {gpu_state}")
+    b2b = back_to_back(torch, stream, step, args.steps)
+    log(f"the same steps with no event between them: {b2b:.4f} ms/step")
 
     # the dominant kernel alone: the leaf pass, launched on the same stream
     roofline = None
@@ -485,11 +515,11 @@ def main():
 
         def leaf_step():
             b3.group_cvs(data, key, group_chunks=group, out=cvs)
-        # right after the chain, in the same clock state: two untimed launches, then timed
+        # each leaf launch alternates with a whole step, so that it runs in the clock and
+        # power state of the chain
         leaf_step()
-        leaf_step()
-        kper, ktotal, _, _ = timed_steps(torch, stream, leaf_step, args.steps)
-        kst = step_stats(kper, ktotal, args.steps)
+        kper = timed_pairs(torch, stream, leaf_step, step, args.steps)
+        kst = step_stats(kper, sum(kper), args.steps)
         leaf_ms = kst["median"]
         ops = leaf_compressions(nbytes, group) * OPS_PER_COMPRESSION
         achieved = ops / (leaf_ms / 1e3) / 1e12
@@ -560,6 +590,7 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_min": round(st["min"], 4),
         "ms_per_step_mean": round(st["mean"], 4),
+        "ms_per_step_back_to_back": round(b2b, 4),
         "warmup_steps_run": warm,
         "higher_is_better": True,
         "scaling": "weak",
