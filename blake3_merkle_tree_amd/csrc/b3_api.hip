@@ -77,10 +77,14 @@ hipMemPool_t device_pool() {
 // reuse the block the same stream freed until the device has passed the free.
 constexpr int kSlotsPerDevice = 4;
 constexpr size_t kSlotMaxBytes = size_t(64) << 20;  // larger requests use the pool
+// Each slot also holds the tickets of fused level passes: zeroed once, when the slot's
+// memory is allocated, and left at zero by every launch that uses them.
+constexpr size_t kSlotTicketWords = 16384;
 
 struct ScratchSlot {
     void *p = nullptr;
     size_t bytes = 0;
+    uint32_t *tickets = nullptr;     // kSlotTicketWords words after the slot's `bytes`
     hipEvent_t done = nullptr;       // recorded after the work of the slot's last call
     hipStream_t last = nullptr;      // that call's stream (a preference only: every reuse waits on done)
     bool used = false;               // done has been recorded
@@ -142,6 +146,11 @@ class StreamScratch {
         return fill_scratch(p_, bytes, s_);
     }
     uint8_t *get() const { return static_cast<uint8_t *>(p_); }
+    // Zeroed tickets of the slot this call holds (left at zero by every launch that uses
+    // them), or nullptr: scratch from the pool, or more tickets than a slot holds.
+    uint32_t *zeroed_tickets(size_t words) const {
+        return slot_ != nullptr && words <= kSlotTicketWords ? slot_->tickets : nullptr;
+    }
 
   private:
     int take_slot(size_t bytes) {
@@ -199,10 +208,22 @@ class StreamScratch {
             sl->bytes = 0;
             size_t grown = size_t(1) << 20;
             while (grown < bytes) grown <<= 1;
-            if (hipMalloc(&sl->p, grown) != hipSuccess) {
+            if (hipMalloc(&sl->p, grown + kSlotTicketWords * 4) != hipSuccess) {
                 (void)hipGetLastError();
                 sl->p = nullptr;
                 return release_unused(ds, sl);
+            }
+            sl->tickets = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(sl->p) + grown);
+            // zero the tickets in stream order, before this call's kernels (a slot that is
+            // grown is idle: no launch still uses its old memory)
+            if (launch_fill_words(sl->tickets, 0, kSlotTicketWords, s_) != hipSuccess) {
+                (void)hipGetLastError();
+                std::lock_guard<std::mutex> lock(ds.mu);
+                ds.retired.push_back(sl->p);
+                sl->p = nullptr;
+                sl->tickets = nullptr;
+                sl->held = false;
+                return B3G_ENOMEM;
             }
             sl->bytes = grown;
         } else if (wait && hipStreamWaitEvent(s_, sl->done, 0) != hipSuccess) {  // after its last call
@@ -284,6 +305,7 @@ class CallScratch {
         return fill_scratch(p_, bytes, s_);
     }
     uint8_t *get() const { return p_; }
+    uint32_t *zeroed_tickets(size_t words) const { return fixed_ ? nullptr : pooled_.zeroed_tickets(words); }
 
   private:
     hipStream_t s_;
@@ -536,29 +558,36 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
             lg[levels + 1] = (lg[levels] + kLevelLanes - 1) / kLevelLanes;
             ++levels;
         }
-        size_t cv_at[kMaxLevels], ctr_at[kMaxLevels], at = 0;
+        size_t cv_at[kMaxLevels], ctr_at[kMaxLevels], at = 0, ctr_words = 0;
         for (uint32_t L = 0; L < levels; ++L) {
             cv_at[L] = at;
             at += align256(nb * lg[L] * 32);
         }
-        const size_t ctr_begin = at;
         for (uint32_t L = 0; L < levels; ++L) {
-            ctr_at[L] = at;
-            at += align256(nb * lg[L + 1] * 4);
+            ctr_at[L] = ctr_words;
+            ctr_words += nb * lg[L + 1];
         }
-        int rc = scratch.alloc(at);
+        // tickets: the slot's (zero, and left at zero by every launch), else zeroed by a
+        // fill kernel before each launch, after the CVs in this call's scratch
+        const size_t cv_bytes = at;
+        int rc = scratch.alloc(cv_bytes + align256(ctr_words * 4));
         if (rc != B3G_OK) return rc;
         uint8_t *d = scratch.get();
+        uint32_t *tickets = scratch.zeroed_tickets(ctr_words);
+        const bool fill_tickets = tickets == nullptr;
+        if (fill_tickets) tickets = reinterpret_cast<uint32_t *>(d + cv_bytes);
         la.levels = levels;
         for (uint32_t L = 0; L < levels; ++L) {
             la.lvl_cv[L] = reinterpret_cast<uint32_t *>(d + cv_at[L]);
-            la.lvl_ctr[L] = reinterpret_cast<uint32_t *>(d + ctr_at[L]);
+            la.lvl_ctr[L] = tickets + ctr_at[L];
         }
         for (uint32_t L = 0; L <= levels; ++L) la.lvl_g[L] = lg[L];
         for (uint64_t m0 = 0; m0 < n_msgs; m0 += nb) {
             const uint64_t nm = n_msgs - m0 < nb ? n_msgs - m0 : nb;
-            rc = launched(launch_zero_words(reinterpret_cast<uint32_t *>(d + ctr_begin), (at - ctr_begin) / 4, s));
-            if (rc != B3G_OK) return rc;
+            if (fill_tickets) {
+                rc = launched(launch_zero_words(tickets, ctr_words, s));
+                if (rc != B3G_OK) return rc;
+            }
             la.base = base + m0 * stride;
             la.n_msgs = static_cast<uint32_t>(nm);
             la.lanes_per_msg = 0;

@@ -58,7 +58,7 @@ struct UniformLeafArgs {
     // fused levels (case B only; levels == 0: the leaf's CVs are the result)
     uint32_t levels;                     // level steps after the leaf
     uint32_t *lvl_cv[kMaxLevels];        // [0] == cv_out; [L]: n_msgs * lvl_g[L] CVs, message-major
-    uint32_t *lvl_ctr[kMaxLevels];       // [L]: n_msgs * lvl_g[L + 1] tickets, zero on entry
+    uint32_t *lvl_ctr[kMaxLevels];       // [L]: n_msgs * lvl_g[L + 1] tickets, zero on entry and exit
     uint64_t lvl_g[kMaxLevels + 1];      // nodes per message: [0] = groups, [L + 1] = ceil([L] / 256)
 };
 

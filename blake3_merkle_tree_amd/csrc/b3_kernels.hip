@@ -704,16 +704,18 @@ __device__ __forceinline__ void uniform_common(UniformSegs &sg, const Args &a) {
 // Fused level passes (UniformLeafArgs::levels): called by the whole workgroup after its
 // leaf tree has written group CV blockIdx.x with device-coherent stores. Each wave waits
 // for its stores to complete, a barrier, then one agent-scope atomic ticket per
-// workgroup; the last arrival of a group reads the group's CVs with device-coherent loads
-// and reduces them with the tree of the level kernel.
-// Ordering: the CV words are only ever accessed as agent-scope atomics, which on gfx950
-// write through to, and read from, the point of coherence shared by all XCDs. A writer's
-// ticket is issued only after vmcnt(0) has seen its CV stores acknowledged there, and the
-// last arrival issues its CV loads only after its ticket has returned (the outcome reaches
-// the other waves through LDS and a barrier), so those loads find every CV of the group.
-// This relies on the hardware's in-order completion rather than on release/acquire
-// ordering: an agent-scope release fence per workgroup would also write back the XCD's
-// whole L2, and measured 43% slower at 4 GiB.
+// workgroup; the last arrival of a group reads the group's CVs with device-coherent loads,
+// sets the ticket back to zero (so tickets need no clearing between launches: every
+// launch leaves them as it found them) and reduces the CVs with the tree of the level
+// kernel, on quads up to the group's own size.
+// Ordering: the CV words are only ever accessed as agent-scope atomics, which gfx950
+// performs at the point of coherence shared by the XCDs (the compiler emits them as sc1
+// stores and loads). A writer's ticket is issued only after vmcnt(0) has seen its CV
+// stores complete there, and the last arrival issues its CV loads only after its ticket
+// has returned (the outcome reaches the other waves through LDS and a barrier), so those
+// loads find every CV of the group. The release/acquire form (an acquire-release ticket,
+// which adds an L2 write-back before it and an invalidation after it) gives the same
+// digests and measured 0.5-27% slower.
 __device__ void fused_levels(const UniformLeafArgs &a, uint32_t *lds) {
     const uint32_t lane = threadIdx.x;
     auto buf = reinterpret_cast<uint32_t(*)[8][kLevelLanes]>(lds);
@@ -725,7 +727,12 @@ __device__ void fused_levels(const UniformLeafArgs &a, uint32_t *lds) {
         const uint32_t count = g_in - first < kLevelLanes ? static_cast<uint32_t>(g_in - first) : kLevelLanes;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's CV stores have completed
         __syncthreads();  // ... in every wave; the tree is done with the LDS: word 0 carries the outcome
-        if (lane == 0) lds[0] = atomicAdd(a.lvl_ctr[L] + msg * g_out + group, 1u) + 1u == count ? 1u : 0u;
+        if (lane == 0) {
+            uint32_t *ticket = a.lvl_ctr[L] + msg * g_out + group;
+            const bool last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == count;
+            if (last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            lds[0] = last ? 1u : 0u;
+        }
         __syncthreads();
         const bool last = lds[0] != 0;
         __syncthreads();  // everyone has read it before the tree writes over it
@@ -738,7 +745,7 @@ __device__ void fused_levels(const UniformLeafArgs &a, uint32_t *lds) {
         }
         UniformSegs sg{};
         uniform_common(sg, a);
-        sg.lanes_log2 = 8;
+        sg.lanes_log2 = ceil_log2(count);  // the group's nodes at positions 0 .. count - 1
         sg.nodes = count;
         sg.segs = 1;
         sg.first_msg = msg;
