@@ -362,7 +362,7 @@ def cpu_legs(args, oracle, host, key, batch, cpu_info):
             nbytes = sum(lengths[:cnt])
             whole = cnt == len(lengths)
         else:
-            got = (oracle.hash_mt(host[:limit], key, nthreads) if nthreads > 1 else oracle.hash(host[:limit], key))
+            got = oracle.hash_mt(host[:limit], key, nthreads)  # one thread too: the same aligned-subtree form
             nbytes = limit
             whole = limit == len(host)
         return nbytes / 1e9 / (time.perf_counter() - c0), nbytes, (got if whole else None), time.perf_counter() - c0
@@ -376,8 +376,8 @@ def cpu_legs(args, oracle, host, key, batch, cpu_info):
            "sample": f"{what} bytes of the same {args.workload} input ({nbytes} B), plain scalar C oracle "
                      f"(multi-threaded aligned-subtree form), {secs:.2f} s wall, {threads} threads",
            "one_thread": {"value": round(one_rate, 3), "unit": "GB/s",
-                          "sample": f"the first {one_bytes} bytes of the same input, the oracle on one thread, "
-                                    f"{one_secs:.2f} s wall"},
+                          "sample": f"the first {one_bytes} bytes of the same input, the same oracle form on one "
+                                    f"thread, {one_secs:.2f} s wall"},
            **cpu_info}
     log(f"cpu oracle: {cpu['value']} GB/s on {threads} threads ({nbytes} bytes); {cpu['one_thread']['value']} "
         f"GB/s on one thread ({one_bytes} bytes); nproc {cpu_info['nproc']}, {cpu_info['cpu_model']}")
