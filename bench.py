@@ -478,7 +478,7 @@ def main():
             "unit": "Tops/s (int32 VALU lane-ops)",
             "frac": round(achieved / VALU_INT_PEAK_TOPS, 4),
             "traffic": None,
-            "kernel": "whole step (leaf_batch_kernel + level_batch_kernel launches, task table upload)",
+            "kernel": "whole step (task-table upload, batch leaf and level passes)",
             "kernel_ms": round(ms_per_step, 4),
             "ops_per_launch": ops,
             "hbm_gbs": round(value, 1),

@@ -502,7 +502,7 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
     if (quad) k = 1;
     const uint64_t span = quad ? kQuadLeafChunks : static_cast<uint64_t>(kLeafLanes) * k;
     const uint32_t wg_slots = quad ? kQuadLeafChunks : kLeafLanes;  // nodes per leaf workgroup
-    const bool fused = fused_levels_enabled();
+    const bool fused = fuse_uniform_levels();
     const bool staged = use_lds_staging() && !fused;  // the fused leaf loads directly
     auto leaf = [&](const UniformLeafArgs &args, uint32_t grid) {
         return quad ? launch_quad_leaf(args, grid, s) : launch_uniform_leaf(args, k, staged, grid, s);
@@ -852,6 +852,16 @@ int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *length
         lay[p].levels = at;
         at += align256(pp.wg_levels.size());
     }
+    // Fused first level pass (the leaf launch reduces it, last arrival of each level
+    // segment): the table also maps each leaf output CV to its level segment, and the
+    // level segments' tickets come from the scratch slot (zero, and left at zero).
+    const bool fuse = fuse_batch_first_level(plan) && !use_lds_staging() &&
+                      plan.passes[1].segs.size() <= kSlotTicketWords;
+    size_t up_at = 0;
+    if (fuse) {
+        up_at = at;
+        at += align256(plan.passes[1].up.size() * sizeof(uint32_t));
+    }
     const size_t table_bytes = at;
     for (size_t p = 0; p < plan.passes.size(); ++p) {
         lay[p].cv_out = at;
@@ -861,6 +871,7 @@ int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *length
     rc = scratch.alloc(at);
     if (rc != B3G_OK) return rc;
     uint8_t *d = scratch.get();
+    uint32_t *tickets = fuse ? scratch.zeroed_tickets(plan.passes[1].segs.size()) : nullptr;
 
     // the table image (the alignment padding between its parts is never read and left as
     // it is): in a pinned buffer, uploaded by a copy kernel, when one is free; else in
@@ -880,6 +891,7 @@ int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *length
         copy_bytes(img, lay[p].first, plan.passes[p].wg_first_seg);
         copy_bytes(img, lay[p].levels, plan.passes[p].wg_levels);
     }
+    if (fuse) copy_bytes(img, up_at, plan.passes[1].up);
     if (pinned) {
         rc = stage.upload(d, table_bytes, s);
         if (rc != B3G_OK) return rc;
@@ -897,8 +909,17 @@ int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *length
             BatchLeafArgs a{static_cast<const uint8_t *>(base),
                             reinterpret_cast<const uint64_t *>(d + msg_off_at),
                             reinterpret_cast<const uint64_t *>(d + msg_len_at),
-                            keys, first, levels, segs, cv_out, static_cast<uint8_t *>(out)};
-            rc = launched(launch_batch_leaf(a, pp.chunks_per_lane, use_lds_staging(), pp.workgroups(), s));
+                            keys, first, levels, segs, cv_out, static_cast<uint8_t *>(out),
+                            nullptr, nullptr, nullptr, nullptr};
+            const bool fused = tickets != nullptr;
+            if (fused) {
+                a.up = reinterpret_cast<const uint32_t *>(d + up_at);
+                a.lvl_segs = reinterpret_cast<const Seg *>(d + lay[1].segs);
+                a.lvl_ctr = tickets;
+                a.lvl_cv_out = reinterpret_cast<uint32_t *>(d + lay[1].cv_out);
+            }
+            rc = launched(launch_batch_leaf(a, pp.chunks_per_lane, use_lds_staging(), fused, pp.workgroups(), s));
+            if (fused) ++p;  // the first level pass ran in the leaf launch
         } else {
             const auto *cv_in = reinterpret_cast<const uint32_t *>(d + lay[p - 1].cv_out);
             BatchLevelArgs a{cv_in, keys, first, levels, segs, cv_out, static_cast<uint8_t *>(out)};

@@ -95,6 +95,12 @@ struct BatchLeafArgs {
     const Seg *segs;
     uint32_t *cv_out;             // next level array
     uint8_t *digests;             // out + 32*msg for final segments
+    // fused first level pass (leaf_batch_kernel<..., Fused>): the last workgroup to deliver
+    // a level segment's CVs reduces it in this launch
+    const uint32_t *up;           // level segment that takes each CV of cv_out
+    const Seg *lvl_segs;          // the first level pass's segments
+    uint32_t *lvl_ctr;            // one ticket per level segment, zero on entry and exit
+    uint32_t *lvl_cv_out;         // the first level pass's output CVs (for the passes after it)
 };
 
 struct BatchLevelArgs {
@@ -156,7 +162,8 @@ struct ChunkRootArgs {
 };
 hipError_t launch_xof_chunk_root(const ChunkRootArgs &a, hipStream_t s);
 
-hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
+// fused: a.up etc. are set and the first level pass runs in this launch (direct loads only).
+hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t chunks_per_lane, bool staged, bool fused, uint32_t grid,
                              hipStream_t s);
 hipError_t launch_batch_level(const BatchLevelArgs &a, uint32_t grid, hipStream_t s);
 

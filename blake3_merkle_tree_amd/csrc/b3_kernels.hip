@@ -474,6 +474,7 @@ struct BatchSegs {
     const uint32_t *keys;  // global, nullptr for default mode
     uint32_t *cv_out;
     uint8_t *digests;
+    bool coherent;         // CVs are read by another workgroup of this launch: device-coherent stores
 
     __device__ uint32_t used_positions() const { return kLanes; }
     __device__ uint32_t root_bit() const { return kRoot; }
@@ -491,12 +492,24 @@ struct BatchSegs {
         }
     }
     __device__ void emit(int s, const uint32_t (&cv)[8]) const {
-        if (final(s)) store_digest(digests + 32ull * seg[s].msg, cv);
-        else store_cv(cv_out + 8ull * seg[s].dst, cv);
+        if (final(s)) {
+            store_digest(digests + 32ull * seg[s].msg, cv);
+        } else if (coherent) {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) store_word_coherent(cv_out + 8ull * seg[s].dst + w, cv[w]);
+        } else {
+            store_cv(cv_out + 8ull * seg[s].dst, cv);
+        }
     }
     __device__ void emit_pair(int s, uint32_t j, uint32_t lo, uint32_t hi) const {
-        if (final(s)) store_digest_pair(digests + 32ull * seg[s].msg, j, lo, hi);
-        else store_cv_pair(cv_out + 8ull * seg[s].dst, j, lo, hi);
+        if (final(s)) {
+            store_digest_pair(digests + 32ull * seg[s].msg, j, lo, hi);
+        } else if (coherent) {
+            store_word_coherent(cv_out + 8ull * seg[s].dst + j, lo);
+            store_word_coherent(cv_out + 8ull * seg[s].dst + 4 + j, hi);
+        } else {
+            store_cv_pair(cv_out + 8ull * seg[s].dst, j, lo, hi);
+        }
     }
 };
 
@@ -969,15 +982,132 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a
     if (Fused) fused_levels(a, lds);
 }
 
-template <uint32_t K, bool Staged>
+// Level segments that one workgroup reduces together (fused_batch_level): n of them, in
+// slots of 2^lanes_log2 lanes (64, four to a workgroup, or one of 256), read from LDS.
+struct LevelSlots {
+    const Seg *seg;        // LDS, n entries
+    uint32_t n;
+    uint32_t lanes_log2;
+    const uint32_t *keys;  // global, nullptr for default mode
+    uint32_t *cv_out;
+    uint8_t *digests;
+
+    __device__ uint32_t used_positions() const { return n << lanes_log2; }
+    __device__ uint32_t root_bit() const { return kRoot; }
+    __device__ int seg_of(uint32_t pos) const {
+        const uint32_t s = pos >> lanes_log2;
+        return s < n && pos - (s << lanes_log2) < seg_count(seg[s].info) ? static_cast<int>(s) : -1;
+    }
+    __device__ uint32_t start(int s) const { return static_cast<uint32_t>(s) << lanes_log2; }
+    __device__ uint32_t count(int s) const { return seg_count(seg[s].info); }
+    __device__ bool final(int s) const { return seg_final(seg[s].info); }
+    __device__ uint32_t mode() const { return keys ? kKeyedHash : 0u; }
+    __device__ void key_words(int s, uint32_t (&kw)[8]) const {
+        if (keys) {
+            load_cv(kw, keys + 8ull * seg[s].msg);
+        } else {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) kw[w] = kIV[w];
+        }
+    }
+    __device__ void emit(int s, const uint32_t (&cv)[8]) const {
+        if (final(s)) store_digest(digests + 32ull * seg[s].msg, cv);
+        else store_cv(cv_out + 8ull * seg[s].dst, cv);
+    }
+    __device__ void emit_pair(int s, uint32_t j, uint32_t lo, uint32_t hi) const {
+        if (final(s)) store_digest_pair(digests + 32ull * seg[s].msg, j, lo, hi);
+        else store_cv_pair(cv_out + 8ull * seg[s].dst, j, lo, hi);
+    }
+};
+
+// Fused first level pass of a batch (BatchLeafArgs::up), called by the whole workgroup after
+// its leaf tree has written the CVs of its segments that are not whole messages, with
+// device-coherent stores. Each such CV belongs to one segment of the first level pass; its
+// segment here takes that level segment's ticket, and the last of them to arrive sets the
+// ticket back to zero and reduces the level segment in this workgroup: it loads the level
+// segment's CVs with device-coherent loads (the last node the parent of two CVs when a
+// message end was split), runs the level tree, and writes the message's digest when the
+// level finishes it, else a CV for the next level pass. A workgroup that holds the ends of
+// several messages is often the last arrival for several level segments: up to four of at
+// most 64 CVs are reduced together, one to a wave's worth of lanes. The ordering is that of
+// fused_levels. `own` (256 words of LDS, free once the leaf tree is done) lists the level
+// segments this workgroup took last; `slots` holds a round's four segments.
+__device__ void fused_batch_level(const BatchLeafArgs &a, const Seg *s_seg, uint32_t nseg, uint32_t *lds,
+                                  uint32_t *own, uint32_t *own_n, Seg *slots) {
+    const uint32_t lane = threadIdx.x;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's CV stores have completed
+    if (lane == 0) *own_n = 0;
+    __syncthreads();  // ... in every wave, and the leaf tree is done with the LDS
+    if (lane < nseg) {
+        const Seg g = s_seg[lane];
+        if (!seg_final(g.info)) {
+            const uint32_t j = a.up[g.dst];
+            const uint32_t info = a.lvl_segs[j].info;
+            const uint32_t inputs = seg_count(info) + (seg_pair(info) ? 1u : 0u);
+            uint32_t *ticket = a.lvl_ctr + j;
+            if (__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == inputs) {
+                __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                own[atomicAdd(own_n, 1u)] = j;
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t owned = *own_n;
+    auto buf = reinterpret_cast<uint32_t(*)[8][kLevelLanes]>(lds);
+    constexpr uint32_t kSlotLanes = kLevelLanes / 4;
+    for (uint32_t o = 0; o < owned;) {
+        // this round: one segment of more than 64 CVs, or up to four of at most 64
+        __syncthreads();  // the previous round is done with `slots` and the LDS
+        const bool big = seg_count(a.lvl_segs[own[o]].info) > kSlotLanes;
+        uint32_t r = 1;
+        while (!big && r < 4 && o + r < owned && seg_count(a.lvl_segs[own[o + r]].info) <= kSlotLanes) ++r;
+        if (lane < r) slots[lane] = a.lvl_segs[own[o + lane]];
+        __syncthreads();
+        LevelSlots sg{slots, r, big ? 8u : 6u, a.keys, a.lvl_cv_out, a.digests};
+        const uint32_t s = lane >> sg.lanes_log2, x = lane - (s << sg.lanes_log2);
+        uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        uint32_t levels = 0;
+        for (uint32_t k = 0; k < r; ++k) {
+            const uint32_t lv = ceil_log2(seg_count(slots[k].info));
+            levels = lv > levels ? lv : levels;
+        }
+        if (s < r) {
+            const Seg g = slots[s];
+            const uint32_t cnt = seg_count(g.info);
+            if (x < cnt) {
+                const uint32_t *src = a.cv_out + 8ull * (g.first + x);
+#pragma unroll
+                for (int w = 0; w < 8; ++w) cv[w] = load_word_coherent(src + w);
+                if (seg_pair(g.info) && x + 1 == cnt) {  // the two halves of a split message end
+                    uint32_t left[8], key[8];
+#pragma unroll
+                    for (int w = 0; w < 8; ++w) {
+                        left[w] = cv[w];
+                        cv[w] = load_word_coherent(src + 8 + w);
+                    }
+                    sg.key_words(static_cast<int>(s), key);
+                    parent_left(cv, left, key, sg.mode(), false);
+                }
+            }
+        }
+        tree_reduce<kLevelLanes, LevelSlots, true>(cv, sg, levels, buf);
+        o += r;
+    }
+}
+
+// Fused: the first level pass runs in this launch (fused_batch_level); a separate
+// instantiation, so that its registers do not weigh on the default leaf.
+template <uint32_t K, bool Staged, bool Fused>
 __global__ __launch_bounds__(kLeafLanes) void leaf_batch_kernel(BatchLeafArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t lds[leaf_lds_words<K, Staged>()];
     __shared__ Seg s_seg[kLanes];
     __shared__ int s_seg_of[kLanes];
+    __shared__ uint32_t s_own_n;
+    __shared__ Seg s_slots[Fused ? 4 : 1];
     stage_segments<kLanes>(a.wg_first_seg, a.segs, s_seg, s_seg_of);
     const uint32_t lane = threadIdx.x;
     const int s = s_seg_of[lane];
-    BatchSegs sg{s_seg, s_seg_of, a.keys, a.cv_out, a.digests};
+    BatchSegs sg{s_seg, s_seg_of, a.keys, a.cv_out, a.digests, Fused};
     uint32_t key[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const uint8_t *ptr = a.base;
@@ -1023,6 +1153,9 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_batch_kernel(BatchLeafArgs a)
     }
     __syncthreads();  // every wave is done with its stage buffer before the tree reuses it
     tree_reduce<kLanes>(cv, sg, a.wg_levels[blockIdx.x], reinterpret_cast<uint32_t(*)[8][kLanes]>(lds));
+    if (Fused)
+        fused_batch_level(a, s_seg, a.wg_first_seg[blockIdx.x + 1] - a.wg_first_seg[blockIdx.x], lds,
+                          reinterpret_cast<uint32_t *>(s_seg_of), &s_own_n, s_slots);
 }
 
 __global__ __launch_bounds__(kLevelLanes) void level_batch_kernel(BatchLevelArgs a) {
@@ -1033,7 +1166,7 @@ __global__ __launch_bounds__(kLevelLanes) void level_batch_kernel(BatchLevelArgs
     const uint32_t lane = threadIdx.x;
     const int s = s_seg_of[lane];
     uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    BatchSegs sg{s_seg, s_seg_of, a.keys, a.cv_out, a.digests};
+    BatchSegs sg{s_seg, s_seg_of, a.keys, a.cv_out, a.digests, false};
     if (s >= 0) {
         const Seg g = s_seg[s];
         const uint32_t x = lane - seg_lane(g.info);
@@ -1281,16 +1414,25 @@ hipError_t launch_uniform_level(const UniformLevelArgs &a, uint32_t grid, hipStr
     return hipGetLastError();
 }
 
-hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t chunks_per_lane, bool staged, uint32_t grid,
+hipError_t launch_batch_leaf(const BatchLeafArgs &a, uint32_t chunks_per_lane, bool staged, bool fused, uint32_t grid,
                              hipStream_t s) {
     const dim3 g(grid), b(kLeafLanes);
+    if (fused) {  // direct loads only
+        switch (staged ? 0 : chunks_per_lane) {
+            case 1: hipLaunchKernelGGL((leaf_batch_kernel<1, false, true>), g, b, 0, s, a); break;
+            case 2: hipLaunchKernelGGL((leaf_batch_kernel<2, false, true>), g, b, 0, s, a); break;
+            case 4: hipLaunchKernelGGL((leaf_batch_kernel<4, false, true>), g, b, 0, s, a); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (chunks_per_lane * 2 + (staged ? 1 : 0)) {
-        case 2: hipLaunchKernelGGL((leaf_batch_kernel<1, false>), g, b, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((leaf_batch_kernel<1, true>), g, b, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((leaf_batch_kernel<2, false>), g, b, 0, s, a); break;
-        case 5: hipLaunchKernelGGL((leaf_batch_kernel<2, true>), g, b, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((leaf_batch_kernel<4, false>), g, b, 0, s, a); break;
-        case 9: hipLaunchKernelGGL((leaf_batch_kernel<4, true>), g, b, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((leaf_batch_kernel<1, false, false>), g, b, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((leaf_batch_kernel<1, true, false>), g, b, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((leaf_batch_kernel<2, false, false>), g, b, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((leaf_batch_kernel<2, true, false>), g, b, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((leaf_batch_kernel<4, false, false>), g, b, 0, s, a); break;
+        case 9: hipLaunchKernelGGL((leaf_batch_kernel<4, true, false>), g, b, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

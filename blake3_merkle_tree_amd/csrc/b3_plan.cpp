@@ -80,7 +80,7 @@ struct Options {
     std::atomic<uint64_t> quad_leaf_max_chunks{kQuadLeafMaxChunksDefault};
     std::atomic<uint64_t> scratch_limit{UINT64_MAX};
     std::atomic<int> scratch_fill{-1};
-    std::atomic<bool> fused_levels{false};
+    std::atomic<int> fused_levels{-1};  // -1 the default choice, 0 never, 1 wherever the form exists
     std::atomic<bool> batch_table{false};
     std::atomic<bool> lds_staging{false};
 };
@@ -113,9 +113,8 @@ void read_options() {
         }
     }
     o.scratch_fill.store(fill, std::memory_order_relaxed);
-    // Off by default: measured on MI355X, the fused form is slower than separate level
-    // launches on every input size.
-    o.fused_levels.store(env_is("BLAKE3_GPU_FUSED_LEVELS", "1"), std::memory_order_relaxed);
+    o.fused_levels.store(env_is("BLAKE3_GPU_FUSED_LEVELS", "1") ? 1 : env_is("BLAKE3_GPU_FUSED_LEVELS", "0") ? 0 : -1,
+                         std::memory_order_relaxed);
     o.batch_table.store(env_is("BLAKE3_GPU_BATCH_TABLE", "1"), std::memory_order_relaxed);
     o.lds_staging.store(env_is("BLAKE3_GPU_STAGING", "lds"), std::memory_order_relaxed);
 }
@@ -143,7 +142,27 @@ uint32_t choose_chunks_per_lane(uint64_t total_chunks) {
 uint64_t quad_leaf_max_chunks() { return g_options.quad_leaf_max_chunks.load(std::memory_order_relaxed); }
 uint64_t scratch_limit() { return g_options.scratch_limit.load(std::memory_order_relaxed); }
 int scratch_fill_byte() { return g_options.scratch_fill.load(std::memory_order_relaxed); }
-bool fused_levels_enabled() { return g_options.fused_levels.load(std::memory_order_relaxed); }
+int fused_levels_setting() { return g_options.fused_levels.load(std::memory_order_relaxed); }
+
+bool fuse_uniform_levels() { return fused_levels_setting() == 1; }
+
+bool fuse_batch_first_level(const BatchPlan &plan) {
+    if (plan.passes.size() < 2) return false;
+    const int setting = fused_levels_setting();
+    if (setting >= 0) return setting == 1;
+    // Measured on MI355X: fused where the first level pass finishes every message and its
+    // segments are small (the workgroups holding message ends, last to finish, each reduce
+    // a few short level segments together: 256 ragged messages of 0 B-1 MiB 80.7 -> 77.8 us);
+    // a level segment of more CVs makes the grid's end wait for its tree (a 300 MiB message
+    // in a batch: 150.3 -> 154.3 us).
+    // Only over one round of leaf workgroups: over many, every workgroup's wait for its
+    // stores and ticket costs more than the launch saves (1024 messages of ~1 MiB: 390.1 ->
+    // 391.3 us).
+    if (plan.passes.size() != 2 || plan.passes[0].workgroups() > 1024) return false;
+    for (const Seg &g : plan.passes[1].segs)
+        if (((g.info >> 12) & 0xFFFu) + 1u + ((g.info & kSegPair) ? 1u : 0u) > 64) return false;
+    return true;
+}
 bool uniform_batch_disabled() { return g_options.batch_table.load(std::memory_order_relaxed); }
 bool use_lds_staging() { return g_options.lds_staging.load(std::memory_order_relaxed); }
 
@@ -251,6 +270,14 @@ int plan_batch(const uint64_t *lengths, uint64_t n, uint32_t leaf_lanes, uint32_
         }
         if (too_big) return kTooBig;
         n_open = kept;
+        if (pass > 0) {  // which segment takes each input CV (a pair node's segment takes two)
+            p.up.assign(p.in_cvs, 0);
+            for (uint64_t j = 0; j < total; ++j) {
+                const uint32_t info = segs[j].info;
+                const uint64_t first = segs[j].first, n_in = ((info >> 12) & 0xFFFu) + 1u + ((info & kSegPair) ? 1u : 0u);
+                for (uint64_t c = first; c < first + n_in && c < p.in_cvs; ++c) p.up[c] = static_cast<uint32_t>(j);
+            }
+        }
         out->passes.push_back(std::move(p));
     }
     return kOk;

@@ -43,6 +43,7 @@ struct PassPlan {
     std::vector<uint8_t> wg_levels;      // W entries: ceil(log2(largest segment))
     uint64_t in_cvs = 0;                 // size of the input CV array (passes > 0)
     uint64_t out_cvs = 0;                // size of the output CV array
+    std::vector<uint32_t> up;            // passes > 0: the segment of this pass that takes input CV c
     uint32_t workgroups() const { return static_cast<uint32_t>(wg_levels.size()); }
 };
 
@@ -70,10 +71,13 @@ bool use_lds_staging();
 constexpr uint64_t kQuadLeafMaxChunksDefault = 16384;
 uint64_t quad_leaf_max_chunks();
 
-// Whether a message spanning several leaf workgroups has its level passes fused into the
-// leaf launch (last-arrival tickets) rather than run as separate level launches (the
-// default). BLAKE3_GPU_FUSED_LEVELS=1 in the environment selects the fused form.
-bool fused_levels_enabled();
+// Fused level passes: the leaf launch reduces the levels itself (last-arrival tickets)
+// instead of separate level launches. Single messages and uniform batches: only with
+// BLAKE3_GPU_FUSED_LEVELS=1 (measured slower). Batches planned into a task table: the first
+// level pass, by default where that pass finishes every message with segments of at most 64
+// CVs (measured faster there); BLAKE3_GPU_FUSED_LEVELS=1 or 0 forces it on or off.
+bool fuse_uniform_levels();
+bool fuse_batch_first_level(const BatchPlan &plan);
 
 // Test hooks for the scratch of a call (stream-ordered device memory). A request of more
 // than BLAKE3_GPU_SCRATCH_LIMIT bytes fails with B3G_ENOMEM before any HIP call, as an

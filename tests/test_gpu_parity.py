@@ -193,10 +193,13 @@ def test_batch_mixed_lengths_with_gaps(b3, dev):
     assert singles == _digests_to_bytes(b3.keyed_hash_batch(base, offs, lengths, keys.to(dev)))
 
 
-def test_random_batches_match_oracle(b3, dev, monkeypatch):
+@pytest.mark.parametrize("fused", ["0", "1"])
+def test_random_batches_match_oracle(b3, dev, monkeypatch, fused):
     # seeded random batches through the task table: lengths mixing empty, sub-block,
     # chunk-boundary, multi-workgroup and split-end messages, random 16-byte gaps, keyed
-    # and default mode, at one, two and four chunks per lane
+    # and default mode, at one, two and four chunks per lane; the first level pass as its
+    # own launch and fused into the leaf launch (last arrival of each level segment)
+    monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", fused)
     from blake3_merkle_tree_amd import workloads
     rng = np.random.Generator(np.random.PCG64(2024))
 
@@ -230,19 +233,22 @@ def test_random_batches_match_oracle(b3, dev, monkeypatch):
         host = _host(base)
         keyed = trial % 2 == 0
         keys = workloads.key_bytes(90 + trial, n)
-        _say("random batch", trial, "messages", n, "bytes", sum(lengths), "keyed", keyed)
+        _say("random batch", trial, "messages", n, "bytes", sum(lengths), "keyed", keyed, "fused", fused)
         out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev) if keyed else None)
         want = oracle.hash_batch(host, offs, lengths, keys.numpy().tobytes() if keyed else None, nthreads=NTHREADS)
         assert _digests_to_bytes(out) == want, (trial, n)
 
 
+@pytest.mark.parametrize("fused", ["0", "1"])
 @pytest.mark.parametrize("chunks_per_lane", ["1", "2", "4"])
-def test_batch_split_message_ends(b3, dev, monkeypatch, chunks_per_lane):
+def test_batch_split_message_ends(b3, dev, monkeypatch, chunks_per_lane, fused):
     # a message's last group of more than half a workgroup that is not a power of two is
     # split in the leaf pass into its left subtree and the rest, whose parent the level
     # pass computes: 456 chunks split at one chunk per lane, 813 at two, 1725 at one and
-    # four; 70,100 chunks put the pair node in a level pass that is not the last
+    # four; 70,100 chunks put the pair node in a level pass that is not the last. Fused:
+    # the first level pass (pair nodes included) runs in the leaf launch, a second one after
     monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", chunks_per_lane)
+    monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", fused)
     from blake3_merkle_tree_amd import workloads
     lengths = [456 * 1024 + 7, 813 * 1024, 1725 * 1024 + 11, 3000, 70100 * 1024 - 100, 1, 200 * 1024 + 5]
     plan = b3.debug_plan_batch(lengths)
@@ -254,7 +260,7 @@ def test_batch_split_message_ends(b3, dev, monkeypatch, chunks_per_lane):
         base[o:o + L] = data[o:o + L]
     host = _host(base)
     keys = workloads.key_bytes(37, len(lengths))
-    _say("batch split message ends, chunks per lane", chunks_per_lane)
+    _say("batch split message ends, chunks per lane", chunks_per_lane, "fused", fused)
     out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))
     want = oracle.hash_batch(host, offs, lengths, keys.numpy().tobytes(), nthreads=NTHREADS)
     assert _digests_to_bytes(out) == want
@@ -319,12 +325,17 @@ def test_workload_gib16(b3, dev):
     _single_workload(b3, dev, "gib16")
 
 
-def test_workload_ragged256(b3, dev):
+def test_workload_ragged256(b3, dev, monkeypatch):
+    # the default plan fuses the first level pass into the leaf launch here; the separate
+    # level launch gives the same digests
     from blake3_merkle_tree_amd import workloads
     base, offs, lengths, keys = workloads.ragged_batch(dev)
+    assert b3.debug_plan_batch(lengths)[1]["segs"], "the ragged batch has a level pass"
     out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))
     want = oracle.hash_batch(_host(base), offs, lengths, keys.numpy().tobytes(), nthreads=NTHREADS)
     assert _digests_to_bytes(out) == want
+    monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", "0")
+    assert _digests_to_bytes(b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))) == want
 
 
 def test_workload_batch64k(b3, dev, monkeypatch):
@@ -532,11 +543,13 @@ def test_results_do_not_depend_on_scratch_contents(b3, dev, monkeypatch, fill):
             monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", fused)
             _say("scratch fill", fill, "length", L, "fused", fused)
             assert bytes(b3.keyed_hash(buf[:L], key).cpu().tolist()) == oracle.hash(host[:L].tobytes(), key)
-    monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", "0")
     lengths = [456 * 1024 + 7, 813 * 1024, 1725 * 1024 + 11, 3000, 1, 200 * 1024 + 5]
     offs, total = workloads.pack_messages(lengths)
-    out = b3.keyed_hash_batch(buf[:total], offs, lengths, None)
-    assert _digests_to_bytes(out) == oracle.hash_batch(host[:total], offs, lengths, None, nthreads=NTHREADS)
+    for fused in ("0", "1"):  # the batch's first level pass as its own launch, and fused
+        monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", fused)
+        out = b3.keyed_hash_batch(buf[:total], offs, lengths, None)
+        assert _digests_to_bytes(out) == oracle.hash_batch(host[:total], offs, lengths, None, nthreads=NTHREADS)
+    monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", "0")
     xof = b3.hash_xof(buf[:1 << 20], key, out_len=4096 + 17)
     assert bytes(xof.cpu().tolist()) == oracle.hash_xof(host[:1 << 20].tobytes(), key, out_len=4096 + 17)
 
