@@ -229,11 +229,13 @@ constexpr QuadWords make_quad_words() {
 }
 constexpr QuadWords kQuadWord = make_quad_words();
 
-// Lane j of the quad takes x from lane (j + k) mod 4 (DPP quad_perm, k = 1, 2, 3).
+// Lane j of the quad takes x from lane (j + k) mod 4 (DPP quad_perm, k = 1, 2, 3). The
+// source lane is always in the quad, so no lane keeps an old value: with bound_ctrl and
+// no old operand the move needs no initialised destination.
 template <int K>
 __device__ __forceinline__ uint32_t quad_take(uint32_t x) {
     constexpr int ctrl = ((0 + K) & 3) | (((1 + K) & 3) << 2) | (((2 + K) & 3) << 4) | (((3 + K) & 3) << 6);
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), ctrl, 0xF, 0xF, false));
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), ctrl, 0xF, 0xF, true));
 }
 
 template <int R>
