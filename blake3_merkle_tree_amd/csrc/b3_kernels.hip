@@ -102,8 +102,7 @@ __device__ __forceinline__ void hash_full_chunk(uint32_t (&cv)[8], const uint8_t
 // registers; it is used where waves have few neighbours on their SIMD to hide a load
 // behind (single messages and uniform batches: 64 MiB 44.4 -> 42.5 us, 1 GiB 360 -> 355
 // us, 4 GiB + 1000 B 1.370 -> 1.360 ms, measured on MI355X), not for the batches planned
-// into a task table, whose messages sit at 16-byte-aligned offsets (256 ragged messages
-// 77.5 -> 79.0 us).
+// into a task table, where it measured slower (256 ragged messages 77.5 -> 79.0 us).
 __device__ __forceinline__ void hash_full_chunk_line_ahead(uint32_t (&cv)[8], const uint8_t *chunk, uint32_t ctr_lo,
                                                            uint32_t ctr_hi, uint32_t mode, uint32_t end_flags) {
     const uint4 *p = reinterpret_cast<const uint4 *>(chunk);
