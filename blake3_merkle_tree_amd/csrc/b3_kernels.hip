@@ -26,6 +26,7 @@
 // at least as large as the right one. Several independent segments (batch mode) share
 // one workgroup by sitting at lane offsets aligned to the next power of two of their
 // size, so that the same pairing never mixes two segments.
+#include <utility>
 #include "b3_device.h"
 #include "b3_kernels.h"
 
@@ -938,15 +939,19 @@ __global__ __launch_bounds__(kLevelLanes) void level_uniform_kernel(UniformLevel
 // With a few thousand chunks the lane-per-chunk leaf cannot fill the chip, and its time
 // is the latency of 16 sequential compressions on one lane plus the tree. Here a quad
 // hashes each chunk (compress_quad, a third of the latency): a workgroup of 256 lanes
-// takes kQuadLeafChunks = 64 chunks, stages them whole in LDS (16-byte loads, zero past
-// the end of a short chunk), runs their blocks, and reduces the chunk CVs on quads.
+// takes kQuadLeafChunks = 64 chunks, loads them whole (16-byte loads, zero past the end of
+// a short chunk) and stages each block in LDS as its compression comes, runs their blocks,
+// and reduces the chunk CVs on quads.
 
-// Bytes [off, off + 16) of a chunk holding len valid bytes; bytes at or past len read as
-// zero and are not loaded.
-__device__ __forceinline__ uint4 load_piece_bounded(const uint8_t *chunk, uint32_t off, uint32_t len) {
-    if (off + 16 <= len) return *reinterpret_cast<const uint4 *>(chunk + off);
-    return make_uint4(load_word_bounded(chunk, off, len), load_word_bounded(chunk, off + 4, len),
-                      load_word_bounded(chunk, off + 8, len), load_word_bounded(chunk, off + 12, len));
+// f(std::integral_constant<uint32_t, b>) for the blocks b = 0..15 of a chunk, in order: one
+// copy of f's body per block, each with its block index a compile-time constant.
+template <class F, uint32_t... Bs>
+__device__ __forceinline__ void for_each_block_of(F &&f, std::integer_sequence<uint32_t, Bs...>) {
+    (f(std::integral_constant<uint32_t, Bs>{}), ...);
+}
+template <class F>
+__device__ __forceinline__ void for_each_block(F &&f) {
+    for_each_block_of(f, std::make_integer_sequence<uint32_t, kBlocksPerChunk>{});
 }
 
 // Words per staged chunk row in LDS: 256 data words plus 4 of padding. Rows 256 words apart
@@ -985,46 +990,64 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a
     uint32_t *mine = lds + q * kQuadRowWords;
     uint32_t lo = 0, hi = 0;  // this lane's CV words j and 4 + j
     uint32_t clen = 0;
+    uint4 piece[kBlocksPerChunk];  // lane j's 16-byte piece j of every block of the quad's chunk
+    uint4 tail = make_uint4(0, 0, 0, 0);
+    uint32_t tail_at = kChunkBytes;  // byte offset of the chunk's partly valid piece, if any
+    uint32_t kw[8];
     if (active) {
+        // the key first: loads complete in issue order, so waiting for a per-message key
+        // loaded after the chunk would wait for the whole chunk
+        sg.key_words(static_cast<int>(s), kw);
         const uint64_t ci = first_chunk + x;
         const uint8_t *chunk = a.base + static_cast<uint64_t>(sg.first_msg + s) * a.stride + ci * kChunkBytes;
         const uint64_t rem = a.len - ci * kChunkBytes;
         clen = a.len == 0 ? 0u : (rem < kChunkBytes ? static_cast<uint32_t>(rem) : kChunkBytes);
-        // lane j stages the 16-byte pieces j, j + 4, ... of the quad's chunk
+        // all sixteen loads are issued here, one 16-byte load each with no branch (a piece not
+        // wholly inside the chunk's bytes comes from the zero piece), so that the wait before
+        // block b is for the loads of blocks 0..b only (loads complete in issue order); each
+        // block's pieces go to LDS just before the quad compresses that block
 #pragma unroll
-        for (uint32_t i = 0; i < 16; ++i) {
-            const uint32_t off = 64 * i + 16 * j;
-            reinterpret_cast<uint4 *>(mine)[4 * i + j] = load_piece_bounded(chunk, off, clen);
+        for (uint32_t i = 0; i < kBlocksPerChunk; ++i) piece[i] = load_piece_or_zero(chunk, 64 * i + 16 * j, clen);
+        if (clen & 15u) {  // the piece holding the last byte, read byte by byte by its lane
+            tail_at = clen & ~15u;
+            if (((tail_at >> 4) & 3u) == j) tail = load_tail_piece(chunk, clen);
         }
     }
-    // the quad reads what its own lanes wrote (same wave, LDS in order): keep the
-    // compiler from moving the reads above the writes
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
     if (active) {
         uint32_t moff[28];  // block word offsets of this lane's 28 message words
 #pragma unroll
         for (int r = 0; r < 7; ++r)
 #pragma unroll
             for (int t = 0; t < 4; ++t) moff[4 * r + t] = (static_cast<uint32_t>(kQuadWord.at[r][t]) >> (4 * j)) & 15u;
-        uint32_t kw[8];
-        sg.key_words(static_cast<int>(s), kw);
         lo = pick4(kw[0], kw[1], kw[2], kw[3], j);
         hi = pick4(kw[4], kw[5], kw[6], kw[7], j);
         const uint64_t ctr = a.chunk_base + first_chunk + x;
         const uint32_t nb = clen == 0 ? 1u : (clen + kBlockBytes - 1) / kBlockBytes;
         const uint32_t end_flags = kChunkEnd | (sg.whole && sg.nodes == 1 ? sg.top_flag : 0u);
         const uint32_t iv_j = pick4(kIV[0], kIV[1], kIV[2], kIV[3], j);
-        for (uint32_t b = 0; b < nb; ++b) {
-            const uint32_t last = b + 1 == nb;
-            const uint32_t flags = sg.mode() | (b == 0 ? kChunkStart : 0u) | (last ? end_flags : 0u);
-            const uint32_t blen = last ? clen - kBlockBytes * b : kBlockBytes;
-            uint32_t va = lo, vb = hi, vc = iv_j;
-            uint32_t vd = pick4(static_cast<uint32_t>(ctr), static_cast<uint32_t>(ctr >> 32), blen, flags, j);
-            compress_quad_lds(va, vb, vc, vd, mine + 16 * b, moff);
-            lo = va ^ vc;
-            hi = vb ^ vd;
-        }
+        // one copy per block (a compile-time block index): the pieces stay in registers and
+        // every message read has a constant offset from the lane's precomputed addresses
+        for_each_block([&](auto bc) __attribute__((always_inline)) {
+            constexpr uint32_t b = decltype(bc)::value;
+            if (b < nb) {  // nb is the same for the quad's four lanes
+                // the partly valid piece replaces the zeros loaded for it (a second store by the
+                // same lane, so that the array is only ever indexed by constants)
+                reinterpret_cast<uint4 *>(mine)[4 * b + j] = piece[b];
+                if (tail_at == 64 * b + 16 * j) reinterpret_cast<uint4 *>(mine)[4 * b + j] = tail;
+                // the quad reads what its own lanes wrote (same wave, LDS in order): keep
+                // the compiler from moving the reads above the writes
+                __builtin_amdgcn_wave_barrier();
+                asm volatile("" ::: "memory");
+                const uint32_t last = b + 1 == nb;
+                const uint32_t flags = sg.mode() | (b == 0 ? kChunkStart : 0u) | (last ? end_flags : 0u);
+                const uint32_t blen = last ? clen - kBlockBytes * b : kBlockBytes;
+                uint32_t va = lo, vb = hi, vc = iv_j;
+                uint32_t vd = pick4(static_cast<uint32_t>(ctr), static_cast<uint32_t>(ctr >> 32), blen, flags, j);
+                compress_quad_lds(va, vb, vc, vd, mine + 16 * b, moff);
+                lo = va ^ vc;
+                hi = vb ^ vd;
+            }
+        });
     }
     __syncthreads();  // every quad is done with its staged chunk: the tree reuses the LDS
     auto buf = reinterpret_cast<uint32_t(*)[8][kQuadLeafChunks]>(lds);
