@@ -1061,7 +1061,9 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a
 }
 
 // Level segments that one workgroup reduces together (fused_batch_level): n of them, in
-// slots of 2^lanes_log2 lanes (64, four to a workgroup, or one of 256), read from LDS.
+// slots of 2^lanes_log2 lanes (from kMinSlotLanes to the whole workgroup), read from LDS.
+constexpr uint32_t kMinSlotLanes = 4;
+constexpr uint32_t kMaxSlots = kLevelLanes / kMinSlotLanes;
 struct LevelSlots {
     const Seg *seg;        // LDS, n entries
     uint32_t n;
@@ -1106,10 +1108,12 @@ struct LevelSlots {
 // segment's CVs with device-coherent loads (the last node the parent of two CVs when a
 // message end was split), runs the level tree, and writes the message's digest when the
 // level finishes it, else a CV for the next level pass. A workgroup that holds the ends of
-// several messages is often the last arrival for several level segments: up to four of at
-// most 64 CVs are reduced together, one to a wave's worth of lanes. The ordering is that of
-// fused_levels. `own` (256 words of LDS, free once the leaf tree is done) lists the level
-// segments this workgroup took last; `slots` holds a round's four segments.
+// several messages is often the last arrival for several level segments: they are reduced
+// together, as many per round as fit in the workgroup's 256 lanes in slots sized to the
+// round's largest segment (a ragged batch's level segments hold a few CVs each). The
+// ordering is that of fused_levels. `own` (256 words of LDS, free once the leaf tree is
+// done) lists the level segments this workgroup took last; `slots` (kMaxSlots entries)
+// holds a round's segments.
 __device__ void fused_batch_level(const BatchLeafArgs &a, const Seg *s_seg, uint32_t nseg, uint32_t *lds,
                                   uint32_t *own, uint32_t *own_n, Seg *slots) {
     const uint32_t lane = threadIdx.x;
@@ -1132,16 +1136,22 @@ __device__ void fused_batch_level(const BatchLeafArgs &a, const Seg *s_seg, uint
     __syncthreads();
     const uint32_t owned = *own_n;
     auto buf = reinterpret_cast<uint32_t(*)[8][kLevelLanes]>(lds);
-    constexpr uint32_t kSlotLanes = kLevelLanes / 4;
     for (uint32_t o = 0; o < owned;) {
-        // this round: one segment of more than 64 CVs, or up to four of at most 64
+        // this round: as many of the next segments as fit in the workgroup in slots of equal
+        // power-of-two width, the smallest that holds the largest of them (at least
+        // kMinSlotLanes lanes, so at most kMaxSlots segments)
         __syncthreads();  // the previous round is done with `slots` and the LDS
-        const bool big = seg_count(a.lvl_segs[own[o]].info) > kSlotLanes;
-        uint32_t r = 1;
-        while (!big && r < 4 && o + r < owned && seg_count(a.lvl_segs[own[o + r]].info) <= kSlotLanes) ++r;
+        uint32_t r = 0, width_log2 = ceil_log2(kMinSlotLanes);
+        while (o + r < owned) {
+            const uint32_t need = ceil_log2(seg_count(a.lvl_segs[own[o + r]].info));
+            const uint32_t w = need > width_log2 ? need : width_log2;
+            if ((r + 1) << w > kLevelLanes) break;
+            width_log2 = w;
+            ++r;
+        }
         if (lane < r) slots[lane] = a.lvl_segs[own[o + lane]];
         __syncthreads();
-        LevelSlots sg{slots, r, big ? 8u : 6u, a.keys, a.lvl_cv_out, a.digests};
+        LevelSlots sg{slots, r, width_log2, a.keys, a.lvl_cv_out, a.digests};
         const uint32_t s = lane >> sg.lanes_log2, x = lane - (s << sg.lanes_log2);
         uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         uint32_t levels = 0;
@@ -1181,7 +1191,7 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_batch_kernel(BatchLeafArgs a)
     __shared__ Seg s_seg[kLanes];
     __shared__ int s_seg_of[kLanes];
     __shared__ uint32_t s_own_n;
-    __shared__ Seg s_slots[Fused ? 4 : 1];
+    __shared__ Seg s_slots[Fused ? kMaxSlots : 1];
     stage_segments<kLanes>(a.wg_first_seg, a.segs, s_seg, s_seg_of);
     const uint32_t lane = threadIdx.x;
     const int s = s_seg_of[lane];

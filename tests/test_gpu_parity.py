@@ -269,6 +269,31 @@ def test_batch_split_message_ends(b3, dev, monkeypatch, chunks_per_lane, fused):
     assert _digests_to_bytes(out) == want
 
 
+@pytest.mark.parametrize("fused", ["0", "1"])
+def test_batch_many_level_segments_per_workgroup(b3, dev, monkeypatch, fused):
+    # 600 messages of one full 256-chunk group plus an end of 1-7 chunks: the ends pack into
+    # a few workgroups dispatched after the 600 full ones, so with the first level pass fused
+    # a workgroup is often the last arrival for many two-CV level segments, which it reduces
+    # in rounds of up to 64 (slots sized to the largest segment)
+    monkeypatch.setenv("BLAKE3_GPU_CHUNKS_PER_LANE", "1")
+    monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", fused)
+    from blake3_merkle_tree_amd import workloads
+    lengths = [(256 + 1 + i % 7) * 1024 - (i * 37) % 1000 for i in range(600)]
+    plan = b3.debug_plan_batch(lengths)
+    assert len(plan) == 2 and len(plan[1]["segs"]) == 600
+    offs, total = workloads.pack_messages(lengths)
+    base = workloads.random_bytes(total, 38, dev)
+    host = _host(base)
+    keys = workloads.key_bytes(39, len(lengths))
+    _say("batch of 600 two-group messages, fused", fused)
+    out = b3.keyed_hash_batch(base, offs, lengths, keys.to(dev))
+    want = oracle.hash_batch(host, offs, lengths, keys.numpy().tobytes(), nthreads=NTHREADS)
+    assert _digests_to_bytes(out) == want
+    out = b3.keyed_hash_batch(base, offs, lengths, None)
+    want = oracle.hash_batch(host, offs, lengths, None, nthreads=NTHREADS)
+    assert _digests_to_bytes(out) == want
+
+
 def test_batch_deep_messages(b3, dev):
     # messages with more than 256^2 chunks need a second level pass inside the batch
     from blake3_merkle_tree_amd import workloads
