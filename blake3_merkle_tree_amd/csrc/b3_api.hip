@@ -497,7 +497,7 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
     const uint64_t total = c > UINT64_MAX / n_msgs ? UINT64_MAX : c * n_msgs;  // chunks, saturated
     // small inputs: a quad per chunk, kQuadLeafChunks chunk slots per workgroup
     const bool quad = total <= quad_leaf_max_chunks();
-    uint32_t k = choose_chunks_per_lane(total);
+    uint32_t k = n_msgs == 1 ? choose_single_chunks_per_lane(total) : choose_chunks_per_lane(total);
     while (k > 1 && k > c) k >>= 1;  // a lane's run of chunks does not outgrow the message
     if (quad) k = 1;
     const uint64_t span = quad ? kQuadLeafChunks : static_cast<uint64_t>(kLeafLanes) * k;
@@ -980,7 +980,7 @@ int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, 
 uint32_t blake3_gpu_leaf_group_chunks(uint64_t len) {
     const uint64_t c = b3g::chunks_of(len);
     if (c <= b3g::quad_leaf_max_chunks()) return b3g::kQuadLeafChunks;
-    return b3g::kLeafLanes * b3g::choose_chunks_per_lane(c);
+    return b3g::kLeafLanes * b3g::choose_single_chunks_per_lane(c);
 }
 
 const char *blake3_gpu_strerror(int status) {

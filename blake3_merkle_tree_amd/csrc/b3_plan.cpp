@@ -139,6 +139,17 @@ uint32_t choose_chunks_per_lane(uint64_t total_chunks) {
     return 1;
 }
 
+uint32_t choose_single_chunks_per_lane(uint64_t chunks) {
+    if (const uint32_t k = g_options.chunks_per_lane.load(std::memory_order_relaxed)) return k;
+    // From 2^16 to 2^17 chunks (64-128 MiB) one chunk per lane puts a second leaf workgroup
+    // on some of the 256 CUs and two keep one per CU. Measured on MI355X (us at K = 1 / 2):
+    // 65 MiB 65.3 / 62.5, 96 MiB 67.0 / 63.4, 128 MiB 67.8 / 64.1; 192 MiB 88.1 / 106.1.
+    // Not for batches: 1000 messages of 100,000 bytes 55.1 / 65.4 (every wave holds message
+    // ends), 256 ragged messages of 122 MiB in all 76.7 / 116.0.
+    if (chunks > (1ull << 16) && chunks <= (1ull << 17)) return 2;
+    return choose_chunks_per_lane(chunks);
+}
+
 uint64_t quad_leaf_max_chunks() { return g_options.quad_leaf_max_chunks.load(std::memory_order_relaxed); }
 uint64_t scratch_limit() { return g_options.scratch_limit.load(std::memory_order_relaxed); }
 int scratch_fill_byte() { return g_options.scratch_fill.load(std::memory_order_relaxed); }
