@@ -203,9 +203,12 @@ class GpuSensors:
         return out
 
 
-def warm_up(torch, step, seconds, count):
+def warm_up(torch, step, seconds, count, depth=0):
     """Runs `step` for at least `seconds` of wall time (synchronising every few steps, so
-    that the time is the GPU's), then `count` more steps."""
+    that the time is the GPU's), then `count` more steps. Those go back to back without a
+    synchronisation, at least `depth` of them (the timed loop's length): calls queued that
+    deep make the library grow its per-call resources (scratch from the stream-ordered pool,
+    pinned table buffers) once, and that growth belongs to the warm-up, not to a timed step."""
     t_end = time.perf_counter() + seconds
     n = 0
     while True:
@@ -215,6 +218,7 @@ def warm_up(torch, step, seconds, count):
         torch.cuda.synchronize()
         if time.perf_counter() >= t_end:
             break
+    count = max(count, depth)
     for _ in range(count):
         step()
     torch.cuda.synchronize()
@@ -297,7 +301,7 @@ def bench_xof(args, torch, b3, workloads, dev, stream, sensors):
 
     def step():
         b3.hash_xof(data, key, XOF_OUT_BYTES, out=out)
-    warm = warm_up(torch, step, args.warmup_seconds, args.warmup)
+    warm = warm_up(torch, step, args.warmup_seconds, args.warmup, args.steps)
     per, total, wall, samples = timed_steps(torch, stream, step, args.steps, sensors)
     st = step_stats(per, total, args.steps)
     ms = st["median"]
@@ -453,7 +457,7 @@ def main():
     torch.cuda.synchronize()
     log(f"workload {args.workload}: {nbytes} bytes")
 
-    warm = warm_up(torch, step, args.warmup_seconds, args.warmup)
+    warm = warm_up(torch, step, args.warmup_seconds, args.warmup, args.steps)
     per, total, wall, samples = timed_steps(torch, stream, step, args.steps, sensors)
     st = step_stats(per, total, args.steps)
     ms_per_step = st["median"]
