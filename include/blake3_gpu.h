@@ -221,7 +221,7 @@ int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, 
                          uint32_t group_chunks, void *dev_cvs, void *stream);
 
 /* Chunks per leaf workgroup that the hash entry points use for an input of len bytes: 64
- * for inputs of at most 16384 chunks (four lanes per chunk; the environment variable
+ * for inputs of at most 32768 chunks (four lanes per chunk; the environment variable
  * BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS moves that bound), else 256, 512 or 1024 (larger
  * inputs fold more chunks per lane before the workgroup tree). */
 uint32_t blake3_gpu_leaf_group_chunks(uint64_t len);

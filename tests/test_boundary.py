@@ -99,12 +99,12 @@ def test_group_cvs_argument_checks_and_leaf_group_size(monkeypatch):
         assert lib.blake3_gpu_group_cvs(None, 5000, 0, None, g, ALIGNED, None) == b3.EINVAL
         assert lib.blake3_gpu_group_cvs(ALIGNED, 5000, 0, None, g, None, None) == b3.EINVAL
         assert lib.blake3_gpu_group_cvs(MISALIGNED, 5000, 0, None, g, ALIGNED, None) == b3.EALIGN
-    # what the hash entry points use: the quad leaf up to 16384 chunks, then 256 * K (K = 2
+    # what the hash entry points use: the quad leaf up to 32768 chunks, then 256 * K (K = 2
     # above 64 MiB up to 128 MiB, 4 from 2 GiB)
     monkeypatch.delenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", raising=False)
     monkeypatch.delenv("BLAKE3_GPU_CHUNKS_PER_LANE", raising=False)
     assert [lib.blake3_gpu_leaf_group_chunks(n) for n in
-            (0, 1 << 20, 16384 * 1024, 16384 * 1024 + 1, 64 << 20, (64 << 20) + 1, 128 << 20, (128 << 20) + 1,
+            (0, 1 << 20, 32768 * 1024, 32768 * 1024 + 1, 64 << 20, (64 << 20) + 1, 128 << 20, (128 << 20) + 1,
              256 << 20, 2 << 30, (4 << 30) + 1000)] == \
         [64, 64, 64, 256, 256, 512, 512, 256, 256, 1024, 1024]
     monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", "0")

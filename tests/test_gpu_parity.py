@@ -126,7 +126,8 @@ def test_level_boundaries(b3, dev, monkeypatch, quad, fused):
         monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", quad)
     monkeypatch.setenv("BLAKE3_GPU_FUSED_LEVELS", fused)
     from blake3_merkle_tree_amd import workloads
-    chunks = [63, 64, 65, 255, 256, 257, 511, 512, 513, 16383, 16384, 16385, 25600, 60000, 65535, 65536, 65537,
+    chunks = [63, 64, 65, 255, 256, 257, 511, 512, 513, 16383, 16384, 16385, 25600, 32767, 32768, 32769, 60000,
+              65535, 65536, 65537,
               91137, 131073, 200000, 262144, 262145]
     buf = workloads.random_bytes(262145 * 1024, 23, dev)
     host = _host(buf)
@@ -666,7 +667,7 @@ def test_repeated_runs_give_identical_digests(b3, dev):
 # ---- extendable output and subtree CVs ----------------------------------------------------
 
 XOF_LENGTHS = [0, 1, 63, 64, 65, 1023, 1024, 1025, 2048, 2049, 5 * 1024 + 7, 64 * 1024, 300 * 1024 + 9,
-               16384 * 1024 + 1, 20000 * 1024 + 3]
+               16384 * 1024 + 1, 20000 * 1024 + 3, 32768 * 1024 + 1]
 XOF_OUT = [0, 1, 31, 32, 33, 64, 65, 200, 4096 + 17]
 
 
@@ -740,7 +741,8 @@ def test_subtree_cv_matches_oracle(b3, dev, keyed):
     host = _host(buf)
     key = bytes(workloads.key_bytes(73)[0].tolist()) if keyed else None
     cases = [(0, 0), (1, 0), (1024, 5), (1025, 2), (64 * 1024, 64), (300 * 1024 + 9, 512),
-             (16384 * 1024 + 1, 1 << 15), (70000 * 1024, 1 << 17), (5000, (1 << 40) + 8)]
+             (16384 * 1024 + 1, 1 << 15), (32768 * 1024 + 1, 1 << 16), (70000 * 1024, 1 << 17),
+             (5000, (1 << 40) + 8)]
     for L, base in cases:
         _say("subtree cv", L, "bytes, chunk base", base, "keyed", keyed)
         got = b3.subtree_cv(buf[:L], key, chunk_base=base).cpu().numpy().view(np.uint32).tolist()
