@@ -791,13 +791,14 @@ def test_share_roots_combine_to_the_digest(b3, dev, workload, share_chunks, cut)
 
 
 def test_graph_capture_replays_match_eager(b3, dev):
-    # One graph holding a keyed hash (70 MiB + 7 B: a leaf and two level passes), an XOF read
+    # One graph holding a keyed hash (130 MiB + 7 B: a leaf at one chunk per lane and two level
+    # passes; from 64 to 128 MiB a single message runs two chunks per lane and one pass), an XOF read
     # across a multiple of 2^32 blocks, a subtree CV with a chunk base above 2^32 and a
     # uniform batch (no task table). Replayed four times, with the outputs cleared, eager
     # hashing and synchronisations between replays: every replay gives the eager results.
     # The replay reads the inputs as they are then: a changed byte changes its digest.
     from blake3_merkle_tree_amd import workloads
-    buf = workloads.random_bytes(70 * 1024 * 1024 + 7, 81, dev)
+    buf = workloads.random_bytes(130 * 1024 * 1024 + 7, 81, dev)
     key = bytes(workloads.key_bytes(82)[0].tolist())
     bkeys = workloads.key_bytes(83, 64).to(dev)
     boffs, blens = [4096 * i for i in range(64)], [3000] * 64
@@ -837,7 +838,7 @@ def test_graph_capture_replays_match_eager(b3, dev):
         for k in outs:
             assert torch.equal(outs[k], want[k]), (rep, k)
         assert bytes(eager.cpu().tolist()) == oracle.hash(_host(buf[:12345 + rep]).tobytes(), key)
-    buf[70 * 1024 * 1024] ^= 0x5A
+    buf[130 * 1024 * 1024] ^= 0x5A
     changed = b3.keyed_hash(buf, key)
     torch.cuda.synchronize()
     g.replay()

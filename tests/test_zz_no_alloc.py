@@ -54,10 +54,11 @@ def _compare(sizes, seed0, check_oracle_up_to=4 << 20):
 
 
 def test_noalloc_equals_keyed_hash_on_consecutive_shrinking_calls():
-    # 64 MiB + 777 B: 257 leaf workgroups and two level passes (both CV arrays of the fixed
-    # scratch); then smaller inputs: the quad leaf and one level pass, a message that one
+    # 128 MiB + 777 B: 513 leaf workgroups and two level passes (both CV arrays of the fixed
+    # scratch); then smaller inputs: 64 MiB + 777 B (two chunks per lane, 129 leaf
+    # workgroups and one level pass), the quad leaf and one level pass, a message that one
     # leaf workgroup finishes (no scratch), a short chunk, the empty input
-    _compare([(64 << 20) + 777, (300 << 10) + 5, 40 * 1024, 5000, 0], 700)
+    _compare([(128 << 20) + 777, (64 << 20) + 777, (300 << 10) + 5, 40 * 1024, 5000, 0], 700)
 
 
 def test_noalloc_equals_keyed_hash_at_the_headline_size_then_smaller():
