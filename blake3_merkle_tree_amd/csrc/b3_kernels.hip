@@ -104,23 +104,28 @@ __device__ __forceinline__ void hash_full_chunk(uint32_t (&cv)[8], const uint8_t
 // behind (single messages and uniform batches: 64 MiB 44.4 -> 42.5 us, 1 GiB 360 -> 355
 // us, 4 GiB + 1000 B 1.370 -> 1.360 ms, measured on MI355X), not for the batches planned
 // into a task table, where it measured slower (256 ragged messages 77.5 -> 79.0 us).
+// ea, oa: on entry blocks 0 and 1 of this chunk (loaded by the caller); on exit blocks 0
+// and 1 at `next`, loaded during the chunk's last blocks, so that a lane folding several
+// chunks never waits at a chunk boundary (`next` is the lane's next chunk, or any readable
+// 128 bytes).
 __device__ __forceinline__ void hash_full_chunk_line_ahead(uint32_t (&cv)[8], const uint8_t *chunk, uint32_t ctr_lo,
-                                                           uint32_t ctr_hi, uint32_t mode, uint32_t end_flags) {
+                                                           uint32_t ctr_hi, uint32_t mode, uint32_t end_flags,
+                                                           Block &ea, Block &oa, const uint8_t *next) {
     const uint4 *p = reinterpret_cast<const uint4 *>(chunk);
+    const uint4 *pn = reinterpret_cast<const uint4 *>(next);
     uint32_t st[16], su[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) st[i] = cv[i], st[i + 8] = 0;
-    Block ea = load_block(p), oa = load_block(p + 4);  // blocks 0 and 1
     for (uint32_t b = 0; b < kBlocksPerChunk; b += 4) {
         const Block eb = load_block(p + 4 * (b + 2)), ob = load_block(p + 4 * (b + 3));
         __builtin_amdgcn_sched_barrier(0);
         compress_block_chained(st, ea, ctr_lo, ctr_hi, mode | (b == 0 ? kChunkStart : 0u), su);
         compress_block_chained(su, oa, ctr_lo, ctr_hi, mode, st);
-        // blocks b + 4 and b + 5; the last iteration re-reads blocks 14 and 15 (in cache),
-        // so that the loop carries no conditional register values
-        const uint32_t nx = b + 4 < kBlocksPerChunk ? b + 4 : kBlocksPerChunk - 2;
-        ea = load_block(p + 4 * nx);
-        oa = load_block(p + 4 * (nx + 1));
+        // blocks b + 4 and b + 5; in the last iteration blocks 0 and 1 at `next` (a select
+        // of the address, so that the loop carries no conditional register values)
+        const uint4 *q = b + 4 < kBlocksPerChunk ? p + 4 * (b + 4) : pn;
+        ea = load_block(q);
+        oa = load_block(q + 4);
         __builtin_amdgcn_sched_barrier(0);
         compress_block_chained(st, eb, ctr_lo, ctr_hi, mode, su);
         compress_block_chained(su, ob, ctr_lo, ctr_hi, mode | (b + 4 == kBlocksPerChunk ? end_flags : 0u), st);
@@ -299,14 +304,23 @@ __device__ __forceinline__ void direct_subtree(uint32_t (&c)[8], const uint8_t *
                                                const uint32_t (&key)[8], uint32_t mode, uint32_t root_flag,
                                                uint32_t *slots) {
     const uint32_t rot = threadIdx.x % K;
+    Block ea, oa;  // blocks 0 and 1 of the next chunk (line-ahead form)
+    if (LineAhead) {
+        const uint4 *p0 = reinterpret_cast<const uint4 *>(ptr + static_cast<uint64_t>(rot) * kChunkBytes);
+        ea = load_block(p0);
+        oa = load_block(p0 + 4);
+    }
     for (uint32_t step = 0; step < K; ++step) {
         const uint32_t k = (step + rot) % K;
 #pragma unroll
         for (int w = 0; w < 8; ++w) c[w] = key[w];
         const uint64_t ctr = ctr0 + k;
-        if (LineAhead)
-            hash_full_chunk_line_ahead(c, ptr + static_cast<uint64_t>(k) * kChunkBytes, static_cast<uint32_t>(ctr),
-                                       static_cast<uint32_t>(ctr >> 32), mode, kChunkEnd | (K == 1 ? root_flag : 0u));
+        const uint8_t *chunk = ptr + static_cast<uint64_t>(k) * kChunkBytes;
+        if (LineAhead)  // the last chunk prefetches its own blocks 14 and 15 again (in cache)
+            hash_full_chunk_line_ahead(c, chunk, static_cast<uint32_t>(ctr), static_cast<uint32_t>(ctr >> 32), mode,
+                                       kChunkEnd | (K == 1 ? root_flag : 0u), ea, oa,
+                                       step + 1 < K ? ptr + static_cast<uint64_t>((k + 1) % K) * kChunkBytes
+                                                    : chunk + (kBlocksPerChunk - 2) * kBlockBytes);
         else
             hash_full_chunk(c, ptr + static_cast<uint64_t>(k) * kChunkBytes, static_cast<uint32_t>(ctr),
                             static_cast<uint32_t>(ctr >> 32), mode, kChunkEnd | (K == 1 ? root_flag : 0u));

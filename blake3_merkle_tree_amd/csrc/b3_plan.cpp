@@ -141,13 +141,34 @@ uint32_t choose_chunks_per_lane(uint64_t total_chunks) {
 
 uint32_t choose_single_chunks_per_lane(uint64_t chunks) {
     if (const uint32_t k = g_options.chunks_per_lane.load(std::memory_order_relaxed)) return k;
-    // From 2^16 to 2^17 chunks (64-128 MiB) one chunk per lane puts a second leaf workgroup
-    // on some of the 256 CUs and two keep one per CU. Measured on MI355X (us at K = 1 / 2):
-    // 65 MiB 65.3 / 62.5, 96 MiB 67.0 / 63.4, 128 MiB 67.8 / 64.1; 192 MiB 88.1 / 106.1.
-    // Not for batches: 1000 messages of 100,000 bytes 55.1 / 65.4 (every wave holds message
-    // ends), 256 ragged messages of 122 MiB in all 76.7 / 116.0.
-    if (chunks > (1ull << 16) && chunks <= (1ull << 17)) return 2;
-    return choose_chunks_per_lane(chunks);
+    // A single message's leaf takes about as long as its busiest CU: with the workgroups
+    // placed in turn on the 256 CUs, the CU that holds the most of them, each worth K chunks
+    // per lane (the last, partial one only as many as its lanes hold: min(K, its chunks)).
+    // K is the one that minimises that, the largest among equals (fewer workgroups, trees and
+    // level CVs). Measured on MI355X (us at K = 1 / 2 / 4), the choice in brackets: 64 MiB
+    // 43.4 / 60.0 / 101.8 [1], 128 MiB 67.8 / 64.1 / - [2], 192 MiB 89.1 / 105.2 / 104.0 [1],
+    // 256 MiB 109.0 / 106.6 / 104.3 [4], 320 MiB 131.1 / 147.2 / 185.1 [1], 384 MiB 153.5 /
+    // 150.6 / 186.9 [2], 448 MiB 173.1 / 187.0 / 188.0 [1], 512 MiB 193.2 / 188.4 / 190.1 [4],
+    // 640 MiB 236.5 / 229.3 / 266.1 [2], 1 GiB 357.2 / 349.9 / 350.4 [4], 2 GiB 690.2 / 673.7 /
+    // 671.8 [4]. From 2^21 chunks (2 GiB) K is 4, as for batches: the rounds are many there,
+    // the level CVs fewest, and the fixed scratch of the entry point that allocates nothing
+    // is sized for it.
+    if (chunks >= (1ull << 21)) return 4;
+    constexpr uint64_t kCUs = 256, kWgLanes = 256;
+    uint64_t best_work = UINT64_MAX;
+    uint32_t best = 1;
+    for (uint32_t k = 1; k <= 4; k *= 2) {
+        const uint64_t span = kWgLanes * k;
+        const uint64_t wgs = (chunks + span - 1) / span;
+        const uint64_t last = chunks - (wgs - 1) * span;  // chunks of the last workgroup
+        const uint64_t q = (wgs - 1) / kCUs, rem = (wgs - 1) % kCUs;  // the last one's round and CU
+        const uint64_t work = rem > 0 ? (q + 1) * k : q * k + (last < k ? last : k);
+        if (work <= best_work) {
+            best_work = work;
+            best = k;
+        }
+    }
+    return best;
 }
 
 uint64_t quad_leaf_max_chunks() { return g_options.quad_leaf_max_chunks.load(std::memory_order_relaxed); }

@@ -59,8 +59,9 @@ uint32_t ceil_log2_host(uint64_t n);     // 0 for n <= 1
 // BLAKE3_GPU_CHUNKS_PER_LANE (1, 2 or 4) in the environment overrides the choice (for
 // tests and benchmarks).
 uint32_t choose_chunks_per_lane(uint64_t total_chunks);
-// The same for a single message of `chunks` chunks: two chunks per lane from 2^16 to 2^17
-// chunks, where it keeps the leaf at one workgroup per CU.
+// The same for a single message of `chunks` chunks: 4 from 2^21 chunks, below that the K that
+// gives the busiest CU the fewest chunks per lane (workgroups placed in turn on the 256 CUs),
+// the largest among equals.
 uint32_t choose_single_chunks_per_lane(uint64_t chunks);
 
 // Input path of full leaf waves: per-lane loads (default) or staged through LDS with
