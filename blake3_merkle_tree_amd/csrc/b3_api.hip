@@ -82,9 +82,9 @@ constexpr size_t kSlotMaxBytes = size_t(64) << 20;  // larger requests use the p
 // tests it before it reuses the memory, and other streams wait on it on the device. None of
 // that needs the system-scope cache write-back and invalidation that a recorded event
 // otherwise performs. Single messages and uniform batches record an event without it
-// (MI355X, back to back, one box: 1 MiB 26.1 -> 24.1 us, 64 MiB 42.6 -> 40.2 us, 256 MiB
-// 105.1 -> 102.9 us); batches planned into a task table keep the fenced event, which measured
-// faster there (256 ragged messages 75.8 against 77.3 us, one process per build).
+// (MI355X, back to back, one process per build: 1 MiB 26.0 -> 23.9 us, 64 MiB 42.8 -> 40.5
+// us, 256 MiB 105.2 -> 103.1 us); batches planned into a task table keep the fenced event,
+// which measured faster there (256 ragged messages 75.8 against 77.3 us).
 constexpr unsigned kUnfencedEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
 // Each slot also holds the tickets of fused level passes: zeroed once, when the slot's
 // memory is allocated, and left at zero by every launch that uses them.

@@ -152,7 +152,9 @@ uint32_t choose_single_chunks_per_lane(uint64_t chunks) {
     // 640 MiB 236.5 / 229.3 / 266.1 [2], 1 GiB 357.2 / 349.9 / 350.4 [4], 2 GiB 690.2 / 673.7 /
     // 671.8 [4]. From 2^21 chunks (2 GiB) K is 4, as for batches: the rounds are many there,
     // the level CVs fewest, and the fixed scratch of the entry point that allocates nothing
-    // is sized for it.
+    // is sized for it. Batches do not use this rule: with K > 1 most of their waves hold
+    // message ends (1000 messages of 100,000 bytes 55.1 / 65.4 us at K = 1 / 2, 256 ragged
+    // messages of 122 MiB in all 76.7 / 116.0).
     if (chunks >= (1ull << 21)) return 4;
     constexpr uint64_t kCUs = 256, kWgLanes = 256;
     uint64_t best_work = UINT64_MAX;
