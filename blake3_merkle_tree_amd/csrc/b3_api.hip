@@ -504,6 +504,55 @@ uint32_t next_pow2_u32(uint64_t x) {
 // Largest grid of one launch: HIP caps a grid at 2^32 - 1 work-items.
 constexpr uint64_t kMaxGrid = 0xFFFFFFFFull / kLeafLanes;
 
+// One message of len bytes whose chunk count is a little above T0 = 2^16 * k (see
+// split_tail_chunks_per_lane): its first T0 chunks as 256 leaf workgroups of 256 * k chunks
+// and the rest on quad workgroups, in one launch (leaf_split_kernel), then both subtrees and
+// their parent in one workgroup (level_split_root_kernel). out receives the root digest, or
+// with root_flag 0 the message's CV.
+int hash_split(const uint8_t *base, uint64_t len, const uint32_t key[8], uint32_t mode, uint64_t chunk_base,
+               uint32_t root_flag, uint8_t *out, uint32_t k, hipStream_t s, bool fixed) {
+    const uint64_t t0 = (1ull << 16) * k;
+    const uint64_t tail_chunks = chunks_of(len) - t0;
+    const uint32_t tail_wgs = static_cast<uint32_t>((tail_chunks + kQuadLeafChunks - 1) / kQuadLeafChunks);
+    CallScratch scratch(s, fixed);
+    int rc = scratch.alloc(static_cast<size_t>(kLevelLanes + tail_wgs) * 32);
+    if (rc != B3G_OK) return rc;
+    auto *cvs = reinterpret_cast<uint32_t *>(scratch.get());
+
+    SplitLeafArgs a{};
+    UniformLeafArgs &m = a.main;  // case B: 256 groups of 256 * k whole chunks
+    m.base = base;
+    m.len = t0 * kChunkBytes;
+    m.n_chunks = t0;
+    m.chunk_base = chunk_base;
+    m.n_msgs = 1;
+    m.groups = kLevelLanes;
+    memcpy(m.key, key, sizeof(m.key));
+    m.mode = mode;
+    m.cv_out = cvs;
+    UniformLeafArgs &t = a.tail;  // case B on quads: tail_wgs groups of 64 chunks
+    t = m;
+    t.base = base + t0 * kChunkBytes;
+    t.len = len - t0 * kChunkBytes;
+    t.n_chunks = tail_chunks;
+    t.chunk_base = chunk_base + t0;
+    t.groups = tail_wgs;
+    t.cv_out = cvs + 8ull * kLevelLanes;
+    a.tail_wgs = tail_wgs;
+    rc = launched(launch_split_leaf(a, k, s));
+    if (rc != B3G_OK) return rc;
+
+    SplitRootArgs r{};
+    r.main_cv = cvs;
+    r.tail_cv = cvs + 8ull * kLevelLanes;
+    r.tail_n = tail_wgs;
+    memcpy(r.key, key, sizeof(r.key));
+    r.mode = mode;
+    r.root_flag = root_flag;
+    r.out = out;
+    return launched(launch_split_root(r, s));
+}
+
 // n_msgs messages of len bytes each, message m at base + m * stride (wrapping 64-bit
 // arithmetic), keyed by keys + 8*m (device) or all by `key` (host words). A leaf
 // workgroup covers `span` chunks (256*K, or 64 with the quad leaf for small inputs). A
@@ -517,6 +566,10 @@ int hash_uniform(const uint8_t *base, uint64_t stride, uint64_t len, uint64_t n_
                  hipStream_t s, bool fixed = false) {
     if (n_msgs == 0) return B3G_OK;
     const uint64_t c = chunks_of(len);
+    if (n_msgs == 1 && keys == nullptr && !fuse_uniform_levels() && !use_lds_staging()) {
+        if (const uint32_t ks = split_tail_chunks_per_lane(c))
+            return hash_split(base, len, key, mode, chunk_base, root_flag, out, ks, s, fixed);
+    }
     const uint64_t total = c > UINT64_MAX / n_msgs ? UINT64_MAX : c * n_msgs;  // chunks, saturated
     // small inputs: a quad per chunk, kQuadLeafChunks chunk slots per workgroup
     const bool quad = total <= quad_leaf_max_chunks();
@@ -1003,6 +1056,7 @@ int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, 
 uint32_t blake3_gpu_leaf_group_chunks(uint64_t len) {
     const uint64_t c = b3g::chunks_of(len);
     if (c <= b3g::quad_leaf_max_chunks()) return b3g::kQuadLeafChunks;
+    if (const uint32_t ks = b3g::split_tail_chunks_per_lane(c)) return b3g::kLeafLanes * ks;
     return b3g::kLeafLanes * b3g::choose_single_chunks_per_lane(c);
 }
 

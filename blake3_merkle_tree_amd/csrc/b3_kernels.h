@@ -125,6 +125,31 @@ hipError_t launch_uniform_level(const UniformLevelArgs &a, uint32_t grid, hipStr
 constexpr uint32_t kQuadLeafChunks = 64;
 hipError_t launch_quad_leaf(const UniformLeafArgs &a, uint32_t grid, hipStream_t s);
 
+// One message a little longer than a power of two T0 = 2^16 * K chunks (K = 1, 2 or 4): the
+// leaf groups of the first T0 chunks (256 workgroups of 256 * K chunks, one round on the 256
+// CUs) and the tail past T0 on quads (quad leaf groups of kQuadLeafChunks chunks) in one
+// launch, the tail's tail_wgs workgroups first. main and tail describe the two parts as
+// case-B uniform leaves (may_root = 0: group CVs to their cv_out).
+struct SplitLeafArgs {
+    UniformLeafArgs main;
+    UniformLeafArgs tail;
+    uint32_t tail_wgs;
+};
+hipError_t launch_split_leaf(const SplitLeafArgs &a, uint32_t chunks_per_lane, hipStream_t s);
+// Its levels and root in one workgroup: the 256 main group CVs reduce to the left subtree's
+// CV and the tail_n tail group CVs (1 .. 256) to the right one's, side by side; their parent,
+// with root_flag (ROOT, or 0 for a subtree CV), is written to out (32 bytes).
+struct SplitRootArgs {
+    const uint32_t *main_cv;
+    const uint32_t *tail_cv;
+    uint32_t tail_n;
+    uint32_t key[8];
+    uint32_t mode;
+    uint32_t root_flag;
+    uint8_t *out;
+};
+hipError_t launch_split_root(const SplitRootArgs &a, hipStream_t s);
+
 // n 16-byte words from src (device-visible pinned host memory, or device memory) to dst.
 hipError_t launch_copy_words16(const void *src, void *dst, uint64_t n, hipStream_t s);
 // Sets n 32-bit words to `value` with a kernel, in stream order (a kernel rather than

@@ -772,14 +772,14 @@ constexpr uint32_t leaf_lds_words() {
 
 // Sets the fields of a UniformSegs that do not depend on the pass.
 template <typename Args>
-__device__ __forceinline__ void uniform_common(UniformSegs &sg, const Args &a) {
+__device__ __forceinline__ void uniform_common(UniformSegs &sg, const Args &a, uint32_t block) {
     sg.top_flag = a.root_flag;
     sg.keys = a.keys;
 #pragma unroll
     for (int w = 0; w < 8; ++w) sg.key[w] = a.key[w];
     sg.mode_flag = a.mode;
     sg.cv_out = a.cv_out;
-    sg.cv_slot = blockIdx.x;
+    sg.cv_slot = block;
     sg.coherent = false;
     sg.digests = a.digests;
 }
@@ -827,7 +827,7 @@ __device__ void fused_levels(const UniformLeafArgs &a, uint32_t *lds) {
             for (int w = 0; w < 8; ++w) cv[w] = load_word_coherent(src + w);
         }
         UniformSegs sg{};
-        uniform_common(sg, a);
+        uniform_common(sg, a, blockIdx.x);
         sg.lanes_log2 = ceil_log2(count);  // the group's nodes at positions 0 .. count - 1
         sg.nodes = count;
         sg.segs = 1;
@@ -843,36 +843,38 @@ __device__ void fused_levels(const UniformLeafArgs &a, uint32_t *lds) {
 
 // Case A groups: `per_wg` messages per workgroup, R = 1 << lanes_log2 lanes each.
 __device__ __forceinline__ void uniform_case_a(UniformSegs &sg, uint32_t lanes_per_msg, uint32_t n_msgs,
-                                               uint32_t wg_lanes) {
+                                               uint32_t wg_lanes, uint32_t block) {
     sg.lanes_log2 = static_cast<uint32_t>(__builtin_ctz(lanes_per_msg));
     const uint32_t per_wg = wg_lanes >> sg.lanes_log2;
-    sg.first_msg = blockIdx.x * per_wg;
+    sg.first_msg = block * per_wg;
     sg.segs = n_msgs - sg.first_msg < per_wg ? n_msgs - sg.first_msg : per_wg;
 }
 
-// Fused: the level passes run in this launch (fused_levels); a separate instantiation, so
-// that the registers the level tree needs do not weigh on the default leaf.
+// One workgroup of the lane-per-chunk leaf: workgroup `block` of the grid that `a`
+// describes, with leaf_lds_words<K, Staged>() words of LDS at `lds`. Fused: the level
+// passes run in this launch (fused_levels, and `block` is then the launch's own workgroup
+// index); a separate instantiation, so that the registers the level tree needs do not
+// weigh on the default leaf.
 template <uint32_t K, bool Staged, bool Fused>
-__global__ __launch_bounds__(kLeafLanes) void leaf_uniform_kernel(UniformLeafArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t lds[leaf_lds_words<K, Staged>()];
+__device__ __forceinline__ void leaf_uniform_wg(const UniformLeafArgs &a, uint32_t block, uint32_t *lds) {
     const uint32_t lane = threadIdx.x;
     constexpr uint64_t kWgChunks = static_cast<uint64_t>(kLanes) * K;
     UniformSegs sg{};
     uint64_t first_chunk = 0;
     if (a.lanes_per_msg != 0) {  // case A: whole messages, several per workgroup
-        uniform_case_a(sg, a.lanes_per_msg, a.n_msgs, kLanes);
+        uniform_case_a(sg, a.lanes_per_msg, a.n_msgs, kLanes, block);
         sg.nodes = static_cast<uint32_t>((a.n_chunks + K - 1) / K);
         sg.whole = a.may_root != 0;
     } else {  // case B: one group of one message
         sg.lanes_log2 = 8;
-        sg.first_msg = blockIdx.x / a.groups;
+        sg.first_msg = block / a.groups;
         sg.segs = 1;
-        first_chunk = static_cast<uint64_t>(blockIdx.x - sg.first_msg * a.groups) * kWgChunks;
+        first_chunk = static_cast<uint64_t>(block - sg.first_msg * a.groups) * kWgChunks;
         const uint64_t left = a.n_chunks - first_chunk;
         sg.nodes = left >= kWgChunks ? kLanes : static_cast<uint32_t>((left + K - 1) / K);
         sg.whole = a.may_root != 0 && a.groups == 1;
     }
-    uniform_common(sg, a);
+    uniform_common(sg, a, block);
     sg.coherent = Fused;  // group CVs are read by the fused levels
 
     const uint32_t s = lane >> sg.lanes_log2, x = lane - (s << sg.lanes_log2);
@@ -923,13 +925,19 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_uniform_kernel(UniformLeafArg
     if (Fused) fused_levels(a, lds);
 }
 
+template <uint32_t K, bool Staged, bool Fused>
+__global__ __launch_bounds__(kLeafLanes) void leaf_uniform_kernel(UniformLeafArgs a) {
+    __shared__ __attribute__((aligned(16))) uint32_t lds[leaf_lds_words<K, Staged>()];
+    leaf_uniform_wg<K, Staged, Fused>(a, blockIdx.x, lds);
+}
+
 __global__ __launch_bounds__(kLevelLanes) void level_uniform_kernel(UniformLevelArgs a) {
     __shared__ uint32_t buf[2][8][kLevelLanes];
     const uint32_t lane = threadIdx.x;
     UniformSegs sg{};
     uint64_t first_cv = 0;
     if (a.lanes_per_msg != 0) {  // case A: the last g_in CVs of several messages, finished here
-        uniform_case_a(sg, a.lanes_per_msg, a.n_msgs, kLevelLanes);
+        uniform_case_a(sg, a.lanes_per_msg, a.n_msgs, kLevelLanes, blockIdx.x);
         sg.nodes = static_cast<uint32_t>(a.g_in);
         sg.whole = true;
     } else {  // case B: 256 CVs (or the rest) of one message
@@ -941,7 +949,7 @@ __global__ __launch_bounds__(kLevelLanes) void level_uniform_kernel(UniformLevel
         sg.nodes = left < kLevelLanes ? static_cast<uint32_t>(left) : kLevelLanes;
         sg.whole = false;
     }
-    uniform_common(sg, a);
+    uniform_common(sg, a, blockIdx.x);
     const uint32_t s = lane >> sg.lanes_log2, x = lane - (s << sg.lanes_log2);
     uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (s < sg.segs && x < sg.nodes)
@@ -975,27 +983,30 @@ __device__ __forceinline__ void for_each_block(F &&f) {
 // of a wave spread over the 32 banks.
 constexpr uint32_t kQuadRowWords = kChunkBytes / 4 + 4;
 
+// LDS of the quad leaf: the staged chunks (65 KiB); afterwards the tree's level buffers.
+constexpr uint32_t kQuadLeafLdsWords = kQuadLeafChunks * kQuadRowWords;
+
+// One workgroup of the quad leaf: workgroup `block` of the grid that `a` describes, with
+// kQuadLeafLdsWords words of LDS at `lds` (Fused: `block` is the launch's own workgroup index).
 template <bool Fused>
-__global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a) {
-    // the staged chunks (65 KiB); afterwards the tree's level buffers
-    __shared__ __attribute__((aligned(16))) uint32_t lds[kQuadLeafChunks * kQuadRowWords];
+__device__ __forceinline__ void leaf_quad_wg(const UniformLeafArgs &a, uint32_t block, uint32_t *lds) {
     const uint32_t lane = threadIdx.x, q = lane >> 2, j = lane & 3u;
     UniformSegs sg{};
     uint64_t first_chunk = 0;
     if (a.lanes_per_msg != 0) {  // case A: whole messages, R chunk slots each
-        uniform_case_a(sg, a.lanes_per_msg, a.n_msgs, kQuadLeafChunks);
+        uniform_case_a(sg, a.lanes_per_msg, a.n_msgs, kQuadLeafChunks, block);
         sg.nodes = static_cast<uint32_t>(a.n_chunks);
         sg.whole = a.may_root != 0;
     } else {  // case B: 64 chunks (or the rest) of one message
         sg.lanes_log2 = 6;
-        sg.first_msg = blockIdx.x / a.groups;
+        sg.first_msg = block / a.groups;
         sg.segs = 1;
-        first_chunk = static_cast<uint64_t>(blockIdx.x - sg.first_msg * a.groups) * kQuadLeafChunks;
+        first_chunk = static_cast<uint64_t>(block - sg.first_msg * a.groups) * kQuadLeafChunks;
         const uint64_t left = a.n_chunks - first_chunk;
         sg.nodes = left >= kQuadLeafChunks ? kQuadLeafChunks : static_cast<uint32_t>(left);
         sg.whole = a.may_root != 0 && a.groups == 1;
     }
-    uniform_common(sg, a);
+    uniform_common(sg, a, block);
     sg.coherent = Fused;  // group CVs are read by the fused levels
 
     // chunk slot q of the workgroup: chunk x of segment s
@@ -1072,6 +1083,107 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a
     }
     tree_levels_quad<kQuadLeafChunks>(sg, 0, ceil_log2(sg.nodes), buf);
     if (Fused) fused_levels(a, lds);
+}
+
+template <bool Fused>
+__global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a) {
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kQuadLeafLdsWords];
+    leaf_quad_wg<Fused>(a, blockIdx.x, lds);
+}
+
+// ---- one round of workgroups and a short tail ----------------------------------------
+// Just above T0 = 2^16 * K chunks, the lane-per-chunk leaf would put a further workgroup of
+// 256 * K chunks on some CUs beside one round of them, and those CUs would take a whole
+// workgroup's time longer. Here the chunks past T0 (at most 2^14: one quad workgroup per CU)
+// run on quads in the same launch: a quad workgroup hashes 64 chunks with 16 block steps of
+// ~273 VALU instructions per wave, against 256 * K chunks and 16 * K steps of ~680 per wave for
+// a lane workgroup, so it adds at most 40% (K = 1), 20% (K = 2) or 10% (K = 4) to a CU's issue
+// work instead of a whole round, and fills issue slots that the lone lane waves leave empty
+// (measured: 65 MiB 59.5 -> 49.1 us, 129 MiB 83.8 -> 68.7 us, 257 MiB 122.7 -> 112.4 us). The
+// static LDS is the quad leaf's 65 KiB, so a CU holds two workgroups: one of each. Its workgroups come
+// first in the grid, so that they are dispatched first and spread over the CUs. T0 is a power
+// of two, so the first T0 chunks are the left subtree of the message's tree and the tail the
+// right one (page "BLAKE3 on GPU", section "Merkle tree reduction": the left subtree holds the
+// largest power of two of chunks below the whole).
+template <uint32_t K>
+constexpr uint32_t split_lds_words() {
+    return kQuadLeafLdsWords > leaf_lds_words<K, false>() ? kQuadLeafLdsWords : leaf_lds_words<K, false>();
+}
+
+template <uint32_t K>
+__global__ __launch_bounds__(kLeafLanes) void leaf_split_kernel(SplitLeafArgs a) {
+    __shared__ __attribute__((aligned(16))) uint32_t lds[split_lds_words<K>()];
+    if (blockIdx.x < a.tail_wgs)
+        leaf_quad_wg<false>(a.tail, blockIdx.x, lds);
+    else
+        leaf_uniform_wg<K, false, false>(a.main, blockIdx.x - a.tail_wgs, lds);
+}
+
+// The two subtrees of leaf_split_kernel's message as two segments of one 512-lane tree: the
+// 256 main group CVs at positions 0..255, the tail's at 256..256 + tail_n - 1 (a position
+// that is a multiple of 256, so that every level pairs nodes of one segment only). Neither is
+// final: each segment's CV goes to LDS (`roots`) for the parent compression after the tree.
+struct SplitSegs {
+    uint32_t tail_n;
+    uint32_t key[8];
+    uint32_t mode_flag;
+    uint32_t *roots;  // LDS, 2 x 8 words
+
+    __device__ uint32_t used_positions() const { return kLevelLanes + tail_n; }
+    __device__ uint32_t root_bit() const { return 0u; }
+    __device__ int seg_of(uint32_t pos) const {
+        if (pos < kLevelLanes) return 0;
+        return pos - kLevelLanes < tail_n ? 1 : -1;
+    }
+    __device__ uint32_t start(int s) const { return s == 0 ? 0u : kLevelLanes; }
+    __device__ uint32_t count(int s) const { return s == 0 ? kLevelLanes : tail_n; }
+    __device__ bool final(int) const { return false; }
+    __device__ uint32_t mode() const { return mode_flag; }
+    __device__ void key_words(int, uint32_t (&kw)[8]) const {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) kw[w] = key[w];
+    }
+    __device__ void emit(int s, const uint32_t (&cv)[8]) const {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) roots[8 * s + w] = cv[w];
+    }
+    __device__ void emit_pair(int s, uint32_t j, uint32_t lo, uint32_t hi) const {
+        roots[8 * s + j] = lo;
+        roots[8 * s + 4 + j] = hi;
+    }
+};
+
+__global__ __launch_bounds__(2 * kLevelLanes) void level_split_root_kernel(SplitRootArgs a) {
+    __shared__ uint32_t buf[2][8][2 * kLevelLanes];
+    __shared__ __attribute__((aligned(16))) uint32_t roots[16];
+    const uint32_t lane = threadIdx.x;
+    SplitSegs sg{};
+    sg.tail_n = a.tail_n;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sg.key[w] = a.key[w];
+    sg.mode_flag = a.mode;
+    sg.roots = roots;
+    uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (lane < kLevelLanes)
+        load_cv(cv, a.main_cv + 8 * lane);
+    else if (lane - kLevelLanes < a.tail_n)
+        load_cv(cv, a.tail_cv + 8 * (lane - kLevelLanes));
+    tree_reduce<2 * kLevelLanes>(cv, sg, ceil_log2(kLevelLanes), buf);
+    __syncthreads();  // both subtree CVs are in `roots`
+    if (lane < 4) {   // their parent on one quad: words 0..7 the left CV, 8..15 the right one
+        const uint32_t j = lane;
+        uint32_t moff[28];
+#pragma unroll
+        for (int r = 0; r < 7; ++r)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) moff[4 * r + t] = (static_cast<uint32_t>(kQuadWord.at[r][t]) >> (4 * j)) & 15u;
+        uint32_t va = pick4(a.key[0], a.key[1], a.key[2], a.key[3], j);
+        uint32_t vb = pick4(a.key[4], a.key[5], a.key[6], a.key[7], j);
+        uint32_t vc = pick4(kIV[0], kIV[1], kIV[2], kIV[3], j);
+        uint32_t vd = j == 3u ? a.mode | kParent | a.root_flag : (j == 2u ? kBlockBytes : 0u);  // counter 0
+        compress_quad_lds(va, vb, vc, vd, roots, moff);
+        store_digest_pair(a.out, j, va ^ vc, vb ^ vd);
+    }
 }
 
 // Level segments that one workgroup reduces together (fused_batch_level): n of them, in
@@ -1508,6 +1620,23 @@ hipError_t launch_quad_leaf(const UniformLeafArgs &a, uint32_t grid, hipStream_t
         hipLaunchKernelGGL(leaf_quad_kernel<true>, dim3(grid), dim3(kLeafLanes), 0, s, a);
     else
         hipLaunchKernelGGL(leaf_quad_kernel<false>, dim3(grid), dim3(kLeafLanes), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_leaf(const SplitLeafArgs &a, uint32_t chunks_per_lane, hipStream_t s) {
+    const dim3 g(a.tail_wgs + a.main.groups), b(kLeafLanes);
+    switch (chunks_per_lane) {
+        case 1: hipLaunchKernelGGL(leaf_split_kernel<1>, g, b, 0, s, a); break;
+        case 2: hipLaunchKernelGGL(leaf_split_kernel<2>, g, b, 0, s, a); break;
+        case 4: hipLaunchKernelGGL(leaf_split_kernel<4>, g, b, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_split_root(const SplitRootArgs &a, hipStream_t s) {
+    if (a.tail_n == 0 || a.tail_n > kLevelLanes) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(level_split_root_kernel, dim3(1), dim3(2 * kLevelLanes), 0, s, a);
     return hipGetLastError();
 }
 

@@ -83,6 +83,7 @@ struct Options {
     std::atomic<int> fused_levels{-1};  // -1 the default choice, 0 never, 1 wherever the form exists
     std::atomic<bool> batch_table{false};
     std::atomic<bool> lds_staging{false};
+    std::atomic<bool> split_tail{true};
 };
 Options g_options;
 
@@ -117,6 +118,7 @@ void read_options() {
                          std::memory_order_relaxed);
     o.batch_table.store(env_is("BLAKE3_GPU_BATCH_TABLE", "1"), std::memory_order_relaxed);
     o.lds_staging.store(env_is("BLAKE3_GPU_STAGING", "lds"), std::memory_order_relaxed);
+    o.split_tail.store(!env_is("BLAKE3_GPU_SPLIT_TAIL", "0"), std::memory_order_relaxed);
 }
 
 struct ReadAtLoad {
@@ -171,6 +173,16 @@ uint32_t choose_single_chunks_per_lane(uint64_t chunks) {
         }
     }
     return best;
+}
+
+uint32_t split_tail_chunks_per_lane(uint64_t chunks) {
+    if (!g_options.split_tail.load(std::memory_order_relaxed)) return 0;
+    if (g_options.chunks_per_lane.load(std::memory_order_relaxed) != 0) return 0;  // a test forces K
+    for (uint32_t k = 4; k >= 1; k /= 2) {
+        const uint64_t t0 = (1ull << 16) * k;
+        if (chunks > t0 && chunks - t0 <= (1ull << 14)) return k;
+    }
+    return 0;
 }
 
 uint64_t quad_leaf_max_chunks() { return g_options.quad_leaf_max_chunks.load(std::memory_order_relaxed); }

@@ -141,6 +141,52 @@ def test_level_boundaries(b3, dev, monkeypatch, quad, fused):
     assert _digests_to_bytes(outs) == want
 
 
+@pytest.mark.parametrize("split", ["1", "0"])
+def test_one_round_and_a_quad_tail(b3, dev, monkeypatch, split):
+    # a message just above 2^16, 2^17 or 2^18 chunks hashes its first 2^16 (2^17, 2^18) chunks
+    # as one round of 256 leaf workgroups at one (two, four) chunks per lane and the tail past
+    # them, up to 2^14 chunks, on quad workgroups in the same launch; both subtrees and their
+    # parent in one more launch. Lengths around both ends of the three ranges, keyed and
+    # default mode; with BLAKE3_GPU_SPLIT_TAIL=0 the same lengths take the ordinary leaf.
+    monkeypatch.setenv("BLAKE3_GPU_SPLIT_TAIL", split)
+    from blake3_merkle_tree_amd import workloads
+    k16, k17, k18 = (1 << 16) * 1024, (1 << 17) * 1024, (1 << 18) * 1024
+    lengths = [k16 + 1, k16 + 3000, k16 + (16 << 20), k16 + (16 << 20) + 1,
+               k17 + 1, k17 + 1024, k17 + 1025, k17 + 64 * 1024, k17 + 64 * 1024 + 1, k17 + (8 << 20),
+               k17 + (16 << 20), k17 + (16 << 20) + 1,
+               k18 + 1, k18 + 777, k18 + (64 << 10) + 5, k18 + (16 << 20) - 3, k18 + (16 << 20),
+               k18 + (16 << 20) + 1]
+    buf = workloads.random_bytes(max(lengths), 25, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(26)[0].tolist())
+    _say("one round and a quad tail", len(lengths), "lengths, split", split)
+    outs = torch.empty((len(lengths), 32), dtype=torch.uint8, device=dev)
+    for i, L in enumerate(lengths):
+        b3.keyed_hash(buf[:L], key, out=outs[i])
+    want = oracle.hash_batch(host, [0] * len(lengths), lengths, key * len(lengths), nthreads=NTHREADS)
+    assert _digests_to_bytes(outs) == want
+    for L in (k17 + 1025, k18 + 777):
+        assert bytes(b3.hash(buf[:L]).cpu().tolist()) == oracle.hash_mt(host[:L], None, NTHREADS), L
+
+
+def test_quad_tail_subtree_cv_and_xof(b3, dev):
+    # the same split with root_flag 0: a subtree CV at a chunk base, and the extended output of
+    # a message whose right subtree (2^17 + 100 chunks) takes it
+    from blake3_merkle_tree_amd import workloads
+    L = ((1 << 18) + (1 << 17) + 100) * 1024 - 9
+    buf = workloads.random_bytes(L, 27, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(28)[0].tolist())
+    S = (1 << 17) * 1024 + 3000
+    base = 1 << 20
+    _say("quad tail subtree cv", S, "bytes, chunk base", base)
+    got = b3.subtree_cv(buf[:S], key, chunk_base=base).cpu().numpy().view(np.uint32).tolist()
+    assert got == oracle.subtree_cv(host[:S].tobytes(), base, key)
+    _say("quad tail xof", L, "bytes")
+    got = bytes(b3.hash_xof(buf, key, out_len=200).cpu().tolist())
+    assert got == oracle.hash_xof(host.tobytes(), key, out_len=200)
+
+
 def test_empty_and_dtypes_and_misaligned_views(b3, dev):
     from blake3_merkle_tree_amd import workloads
     key = bytes(workloads.key_bytes(25)[0].tolist())
