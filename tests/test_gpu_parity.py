@@ -6,7 +6,8 @@ copy of the same device bytes. Cases: brute force over chunk counts and tail len
 boundaries), the empty input, misaligned views, non-default streams, batches with gap
 bytes of 0xA5 between messages (an over-read changes the digest), split message ends and
 seeded random batches, every workload at full size in the launch configuration the
-benchmark times, extended output and subtree CVs (share roots of a 4 GiB and a 256 MiB
+benchmark times, single messages just above one round whose excess runs on quads in the
+same launch, extended output and subtree CVs (share roots of a 4 GiB and a 256 MiB
 input, hashed separately with their chunk bases, combine to the digest), and the library's
 scratch: a forced allocation failure, scratch of arbitrary prior contents, repeated runs,
 and calls shared between streams, host threads and a stream held behind long work; and graph
