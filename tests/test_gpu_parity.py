@@ -170,6 +170,25 @@ def test_one_round_and_a_quad_tail(b3, dev, monkeypatch, split):
         assert bytes(b3.hash(buf[:L]).cpu().tolist()) == oracle.hash_mt(host[:L], None, NTHREADS), L
 
 
+def test_random_single_sizes(b3, dev):
+    # seeded sizes, 12 spread log-uniformly from 1 B to 300 MiB and 28 uniformly from 32 MiB to
+    # 300 MiB, so that every leaf form meets arbitrary lengths: the quad leaf, one, two and
+    # four chunks per lane picked by the busiest-CU rule, and the split just above a round
+    from blake3_merkle_tree_amd import workloads
+    rng = np.random.default_rng(31)
+    lengths = sorted([int(x) for x in np.exp(rng.uniform(0.0, np.log(300 << 20), 12))] +
+                     [int(x) for x in rng.integers(32 << 20, 300 << 20, 28)])
+    buf = workloads.random_bytes(max(lengths), 32, dev)
+    host = _host(buf)
+    key = bytes(workloads.key_bytes(33)[0].tolist())
+    _say("random single sizes", lengths[:3], "...", lengths[-3:])
+    outs = torch.empty((len(lengths), 32), dtype=torch.uint8, device=dev)
+    for i, L in enumerate(lengths):
+        b3.keyed_hash(buf[:L], key, out=outs[i])
+    want = oracle.hash_batch(host, [0] * len(lengths), lengths, key * len(lengths), nthreads=NTHREADS)
+    assert _digests_to_bytes(outs) == want
+
+
 def test_quad_tail_subtree_cv_and_xof(b3, dev):
     # the same split with root_flag 0: a subtree CV at a chunk base, and the extended output of
     # a message whose right subtree (2^17 + 100 chunks) takes it
