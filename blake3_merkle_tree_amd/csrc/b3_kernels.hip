@@ -1098,10 +1098,12 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a
 // run on quads in the same launch: a quad workgroup hashes 64 chunks with 16 block steps of
 // ~273 VALU instructions per wave, against 256 * K chunks and 16 * K steps of ~680 per wave for
 // a lane workgroup, so it adds at most 40% (K = 1), 20% (K = 2) or 10% (K = 4) to a CU's issue
-// work instead of a whole round, and fills issue slots that the lone lane waves leave empty
-// (measured: 65 MiB 59.5 -> 49.1 us, 129 MiB 83.8 -> 68.7 us, 257 MiB 122.7 -> 112.4 us). The
-// static LDS is the quad leaf's 65 KiB, so a CU holds two workgroups: one of each. Its workgroups come
-// first in the grid, so that they are dispatched first and spread over the CUs. T0 is a power
+// work instead of a whole round (measured, the split adds 8-10 us to the time of the round
+// alone: 64 -> 65 MiB 40.3 -> 49.1 us, where the ordinary leaf takes 59.5 us; 128 -> 129 MiB
+// 60.3 -> 68.7 us against 83.8; 256 -> 257 MiB 103.4 -> 112.4 us against 122.7). The static
+// LDS is the quad leaf's 65 KiB, so a CU holds two workgroups: one of each. The quad
+// workgroups come first in the grid, so that they are dispatched first and spread over the
+// CUs. T0 is a power
 // of two, so the first T0 chunks are the left subtree of the message's tree and the tail the
 // right one (page "BLAKE3 on GPU", section "Merkle tree reduction": the left subtree holds the
 // largest power of two of chunks below the whole).
