@@ -799,6 +799,9 @@ __device__ __forceinline__ void uniform_common(UniformSegs &sg, const Args &a, u
 // loads find every CV of the group. The release/acquire form (an acquire-release ticket,
 // which adds an L2 write-back before it and an invalidation after it) gives the same
 // digests and measured 0.5-27% slower.
+// LDS words fused_levels needs at `lds`: the level tree's two buffers of 8 x 256 words.
+constexpr uint32_t kFusedLevelLdsWords = 2 * 8 * kLevelLanes;
+
 __device__ void fused_levels(const UniformLeafArgs &a, uint32_t *lds) {
     const uint32_t lane = threadIdx.x;
     auto buf = reinterpret_cast<uint32_t(*)[8][kLevelLanes]>(lds);
@@ -927,6 +930,7 @@ __device__ __forceinline__ void leaf_uniform_wg(const UniformLeafArgs &a, uint32
 
 template <uint32_t K, bool Staged, bool Fused>
 __global__ __launch_bounds__(kLeafLanes) void leaf_uniform_kernel(UniformLeafArgs a) {
+    static_assert(!Fused || leaf_lds_words<K, Staged>() >= kFusedLevelLdsWords, "the fused levels fit the LDS");
     __shared__ __attribute__((aligned(16))) uint32_t lds[leaf_lds_words<K, Staged>()];
     leaf_uniform_wg<K, Staged, Fused>(a, blockIdx.x, lds);
 }
@@ -976,15 +980,18 @@ __device__ __forceinline__ void for_each_block(F &&f) {
     for_each_block_of(f, std::make_integer_sequence<uint32_t, kBlocksPerChunk>{});
 }
 
-// Words per staged chunk row in LDS: 256 data words plus 4 of padding. Rows 256 words apart
-// would put the same word of every quad's chunk in one bank, and each message read of
-// the compression (four words per lane per round, a different quad per chunk) would be an
-// 8-way bank conflict per half-wave; at 260 it averages 1.8-way (3 at worst), the 64 lanes
-// of a wave spread over the 32 banks.
-constexpr uint32_t kQuadRowWords = kChunkBytes / 4 + 4;
+// Words per staged chunk row in LDS: a ring of two blocks (block b in slot b & 1; a slot is
+// written again two blocks later, after the quad's reads of it, which its wave performs in
+// order) plus 4 words of padding. Rows a multiple of 32 words apart would put the same word
+// of every quad's chunk in one bank, and each message read of the compression (four words
+// per lane per round, a different quad per chunk) would be an 8-way bank conflict per
+// half-wave; with rows 4 banks apart it averages 1.8-way (3 at worst), the 64 lanes of a wave
+// spread over the 32 banks.
+constexpr uint32_t kQuadRowWords = 2 * kBlockBytes / 4 + 4;
 
-// LDS of the quad leaf: the staged chunks (65 KiB); afterwards the tree's level buffers.
+// LDS of the quad leaf: the staged blocks (9 KiB); afterwards the tree's level buffers (4 KiB).
 constexpr uint32_t kQuadLeafLdsWords = kQuadLeafChunks * kQuadRowWords;
+static_assert(kQuadLeafLdsWords >= 2 * 8 * kQuadLeafChunks, "the tree's level buffers fit the staging rows");
 
 // One workgroup of the quad leaf: workgroup `block` of the grid that `a` describes, with
 // kQuadLeafLdsWords words of LDS at `lds` (Fused: `block` is the launch's own workgroup index).
@@ -1057,8 +1064,8 @@ __device__ __forceinline__ void leaf_quad_wg(const UniformLeafArgs &a, uint32_t 
             if (b < nb) {  // nb is the same for the quad's four lanes
                 // the partly valid piece replaces the zeros loaded for it (a second store by the
                 // same lane, so that the array is only ever indexed by constants)
-                reinterpret_cast<uint4 *>(mine)[4 * b + j] = piece[b];
-                if (tail_at == 64 * b + 16 * j) reinterpret_cast<uint4 *>(mine)[4 * b + j] = tail;
+                reinterpret_cast<uint4 *>(mine)[4 * (b & 1) + j] = piece[b];
+                if (tail_at == 64 * b + 16 * j) reinterpret_cast<uint4 *>(mine)[4 * (b & 1) + j] = tail;
                 // the quad reads what its own lanes wrote (same wave, LDS in order): keep
                 // the compiler from moving the reads above the writes
                 __builtin_amdgcn_wave_barrier();
@@ -1068,7 +1075,7 @@ __device__ __forceinline__ void leaf_quad_wg(const UniformLeafArgs &a, uint32_t 
                 const uint32_t blen = last ? clen - kBlockBytes * b : kBlockBytes;
                 uint32_t va = lo, vb = hi, vc = iv_j;
                 uint32_t vd = pick4(static_cast<uint32_t>(ctr), static_cast<uint32_t>(ctr >> 32), blen, flags, j);
-                compress_quad_lds(va, vb, vc, vd, mine + 16 * b, moff);
+                compress_quad_lds(va, vb, vc, vd, mine + 16 * (b & 1), moff);
                 lo = va ^ vc;
                 hi = vb ^ vd;
             }
@@ -1087,7 +1094,9 @@ __device__ __forceinline__ void leaf_quad_wg(const UniformLeafArgs &a, uint32_t 
 
 template <bool Fused>
 __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t lds[kQuadLeafLdsWords];
+    // the fused levels' buffers are larger than the staged blocks
+    constexpr uint32_t kWords = Fused && kFusedLevelLdsWords > kQuadLeafLdsWords ? kFusedLevelLdsWords : kQuadLeafLdsWords;
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kWords];
     leaf_quad_wg<Fused>(a, blockIdx.x, lds);
 }
 
