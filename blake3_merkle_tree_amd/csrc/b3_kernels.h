@@ -137,7 +137,7 @@ struct SplitLeafArgs {
 };
 hipError_t launch_split_leaf(const SplitLeafArgs &a, uint32_t chunks_per_lane, hipStream_t s);
 // Its levels and root in one workgroup: the 256 main group CVs reduce to the left subtree's
-// CV and the tail_n tail group CVs (1 .. 256) to the right one's, side by side; their parent,
+// CV and the tail_n tail group CVs (1 .. 512) to the right one's, side by side; their parent,
 // with root_flag (ROOT, or 0 for a subtree CV), is written to out (32 bytes).
 struct SplitRootArgs {
     const uint32_t *main_cv;

@@ -1103,16 +1103,16 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_quad_kernel(UniformLeafArgs a
 // ---- one round of workgroups and a short tail ----------------------------------------
 // Just above T0 = 2^16 * K chunks, the lane-per-chunk leaf would put a further workgroup of
 // 256 * K chunks on some CUs beside one round of them, and those CUs would take a whole
-// workgroup's time longer. Here the chunks past T0 (at most 2^14: one quad workgroup per CU)
+// workgroup's time longer. Here the chunks past T0 (at most 2^15: two quad workgroups per CU)
 // run on quads in the same launch: a quad workgroup hashes 64 chunks with 16 block steps of
 // ~273 VALU instructions per wave, against 256 * K chunks and 16 * K steps of ~680 per wave for
 // a lane workgroup, so it adds at most 40% (K = 1), 20% (K = 2) or 10% (K = 4) to a CU's issue
 // work instead of a whole round (measured, the split adds 8-10 us to the time of the round
 // alone: 64 -> 65 MiB 40.3 -> 49.1 us, where the ordinary leaf takes 59.5 us; 128 -> 129 MiB
-// 60.3 -> 68.7 us against 83.8; 256 -> 257 MiB 103.4 -> 112.4 us against 122.7). The static
-// LDS is the quad leaf's 65 KiB, so a CU holds two workgroups: one of each. The quad
+// 60.3 -> 68.7 us against 83.8; 256 -> 257 MiB 103.4 -> 112.4 us against 122.7). The quad
 // workgroups come first in the grid, so that they are dispatched first and spread over the
-// CUs. T0 is a power
+// CUs; with 130 VGPRs a SIMD holds three waves, so a CU with two quad workgroups takes one
+// lane workgroup of the round. T0 is a power
 // of two, so the first T0 chunks are the left subtree of the message's tree and the tail the
 // right one (page "BLAKE3 on GPU", section "Merkle tree reduction": the left subtree holds the
 // largest power of two of chunks below the whole).
@@ -1130,23 +1130,25 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_split_kernel(SplitLeafArgs a)
         leaf_uniform_wg<K, false, false>(a.main, blockIdx.x - a.tail_wgs, lds);
 }
 
-// The two subtrees of leaf_split_kernel's message as two segments of one 512-lane tree: the
-// 256 main group CVs at positions 0..255, the tail's at 256..256 + tail_n - 1 (a position
-// that is a multiple of 256, so that every level pairs nodes of one segment only). Neither is
-// final: each segment's CV goes to LDS (`roots`) for the parent compression after the tree.
+// The two subtrees of leaf_split_kernel's message as two segments of one tree of C lanes: the
+// 256 main group CVs at positions 0..255, the tail's tail_n <= C / 2 at C / 2 .. (a position
+// that is a multiple of the next power of two of tail_n, so that every level pairs nodes of
+// one segment only). Neither is final: each segment's CV goes to LDS (`roots`) for the
+// parent compression after the tree.
+template <uint32_t C>
 struct SplitSegs {
     uint32_t tail_n;
     uint32_t key[8];
     uint32_t mode_flag;
     uint32_t *roots;  // LDS, 2 x 8 words
 
-    __device__ uint32_t used_positions() const { return kLevelLanes + tail_n; }
+    __device__ uint32_t used_positions() const { return C / 2 + tail_n; }
     __device__ uint32_t root_bit() const { return 0u; }
     __device__ int seg_of(uint32_t pos) const {
         if (pos < kLevelLanes) return 0;
-        return pos - kLevelLanes < tail_n ? 1 : -1;
+        return pos >= C / 2 && pos - C / 2 < tail_n ? 1 : -1;
     }
-    __device__ uint32_t start(int s) const { return s == 0 ? 0u : kLevelLanes; }
+    __device__ uint32_t start(int s) const { return s == 0 ? 0u : C / 2; }
     __device__ uint32_t count(int s) const { return s == 0 ? kLevelLanes : tail_n; }
     __device__ bool final(int) const { return false; }
     __device__ uint32_t mode() const { return mode_flag; }
@@ -1164,11 +1166,13 @@ struct SplitSegs {
     }
 };
 
-__global__ __launch_bounds__(2 * kLevelLanes) void level_split_root_kernel(SplitRootArgs a) {
-    __shared__ uint32_t buf[2][8][2 * kLevelLanes];
+template <uint32_t C>
+__global__ __launch_bounds__(C) void level_split_root_kernel(SplitRootArgs a) {
+    static_assert(C / 2 >= kLevelLanes, "the main segment fits below the tail");
+    __shared__ uint32_t buf[2][8][C];
     __shared__ __attribute__((aligned(16))) uint32_t roots[16];
     const uint32_t lane = threadIdx.x;
-    SplitSegs sg{};
+    SplitSegs<C> sg{};
     sg.tail_n = a.tail_n;
 #pragma unroll
     for (int w = 0; w < 8; ++w) sg.key[w] = a.key[w];
@@ -1177,9 +1181,9 @@ __global__ __launch_bounds__(2 * kLevelLanes) void level_split_root_kernel(Split
     uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (lane < kLevelLanes)
         load_cv(cv, a.main_cv + 8 * lane);
-    else if (lane - kLevelLanes < a.tail_n)
-        load_cv(cv, a.tail_cv + 8 * (lane - kLevelLanes));
-    tree_reduce<2 * kLevelLanes>(cv, sg, ceil_log2(kLevelLanes), buf);
+    else if (lane >= C / 2 && lane - C / 2 < a.tail_n)
+        load_cv(cv, a.tail_cv + 8 * (lane - C / 2));
+    tree_reduce<C>(cv, sg, ceil_log2(a.tail_n > kLevelLanes ? a.tail_n : kLevelLanes), buf);
     __syncthreads();  // both subtree CVs are in `roots`
     if (lane < 4) {   // their parent on one quad: words 0..7 the left CV, 8..15 the right one
         const uint32_t j = lane;
@@ -1646,8 +1650,11 @@ hipError_t launch_split_leaf(const SplitLeafArgs &a, uint32_t chunks_per_lane, h
 }
 
 hipError_t launch_split_root(const SplitRootArgs &a, hipStream_t s) {
-    if (a.tail_n == 0 || a.tail_n > kLevelLanes) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(level_split_root_kernel, dim3(1), dim3(2 * kLevelLanes), 0, s, a);
+    if (a.tail_n == 0 || a.tail_n > 2 * kLevelLanes) return hipErrorInvalidValue;
+    if (a.tail_n <= kLevelLanes)
+        hipLaunchKernelGGL(level_split_root_kernel<2 * kLevelLanes>, dim3(1), dim3(2 * kLevelLanes), 0, s, a);
+    else
+        hipLaunchKernelGGL(level_split_root_kernel<4 * kLevelLanes>, dim3(1), dim3(4 * kLevelLanes), 0, s, a);
     return hipGetLastError();
 }
 

@@ -180,7 +180,7 @@ uint32_t split_tail_chunks_per_lane(uint64_t chunks) {
     if (g_options.chunks_per_lane.load(std::memory_order_relaxed) != 0) return 0;  // a test forces K
     for (uint32_t k = 4; k >= 1; k /= 2) {
         const uint64_t t0 = (1ull << 16) * k;
-        if (chunks > t0 && chunks - t0 <= (1ull << 14)) return k;
+        if (chunks > t0 && chunks - t0 <= (1ull << 15)) return k;
     }
     return 0;
 }

@@ -65,12 +65,13 @@ uint32_t choose_chunks_per_lane(uint64_t total_chunks);
 uint32_t choose_single_chunks_per_lane(uint64_t chunks);
 
 // A single message of `chunks` chunks just above a power of two T0 = 2^16 * K (K = 4, 2 or
-// 1), by at most 2^14 chunks (one quad workgroup per CU), hashes its first T0 chunks as one
+// 1), by at most 2^15 chunks (two quad workgroups per CU), hashes its first T0 chunks as one
 // round of 256 leaf workgroups and the rest on quads in the same launch: returns that K, or 0
 // for the ordinary leaf. Measured on MI355X (us, ordinary leaf / split): 65 MiB 59.5 / 49.1,
-// 80 MiB 59.4 / 50.1, 129 MiB 83.8 / 68.7, 144 MiB 84.7 / 69.5, 257 MiB 122.7 / 112.4,
-// 272 MiB 123.6 / 114.0; 64, 128 and 256 MiB unchanged. BLAKE3_GPU_SPLIT_TAIL=0 in the
-// environment turns it off; a forced K turns it off too.
+// 80 MiB 59.4 / 50.1, 96 MiB 59.7 / 59.8, 129 MiB 83.8 / 68.7, 144 MiB 84.7 / 69.5, 160 MiB
+// 84.9 / 80.2, 257 MiB 122.7 / 112.4, 272 MiB 123.6 / 114.0, 288 MiB 124.1 / 124.4; 64, 128 and
+// 256 MiB unchanged (a second quad workgroup per CU pays only at two chunks per lane).
+// BLAKE3_GPU_SPLIT_TAIL=0 in the environment turns it off; a forced K turns it off too.
 uint32_t split_tail_chunks_per_lane(uint64_t chunks);
 
 // Input path of full leaf waves: per-lane loads (default) or staged through LDS with

@@ -223,7 +223,7 @@ int blake3_gpu_group_cvs(const void *dev_in, uint64_t len, uint64_t chunk_base, 
 /* Chunks per leaf workgroup that the hash entry points use for an input of len bytes: 64
  * for inputs of at most 32768 chunks (four lanes per chunk; the environment variable
  * BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS moves that bound), else 256, 512 or 1024 (larger
- * inputs fold more chunks per lane before the workgroup tree). An input of at most 2^14
+ * inputs fold more chunks per lane before the workgroup tree). An input of at most 2^15
  * chunks more than 2^16, 2^17 or 2^18 chunks is hashed as that power of two in groups of
  * 256, 512 or 1024 chunks (the value returned) and the chunks past it in groups of 64, in
  * one launch; the digest is the same for any grouping. */

@@ -103,14 +103,14 @@ def test_group_cvs_argument_checks_and_leaf_group_size(monkeypatch):
     # that leaves the busiest of the 256 CUs the fewest chunks per lane (the largest among
     # equals): 64 MiB is one K = 1 workgroup per CU, 192 MiB is 3 K = 1 rounds against 4 chunks
     # per lane at K = 2 or 4, 256 MiB one K = 4 round, 320 MiB 5 K = 1 rounds, 384 MiB 6 at
-    # K = 2; K = 4 from 2 GiB. Up to 2^14 chunks above 2^16, 2^17 and 2^18 chunks (64 MiB + 1 B,
-    # 128 MiB + 1 B, 256 MiB + 16 MiB) the power of two is one round at K = 1, 2 and 4 and the
+    # K = 2; K = 4 from 2 GiB. Up to 2^15 chunks above 2^16, 2^17 and 2^18 chunks (64 MiB + 1 B,
+    # 128 MiB + 1 B, 256 MiB + 32 MiB) the power of two is one round at K = 1, 2 and 4 and the
     # rest runs on quads
     monkeypatch.delenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", raising=False)
     monkeypatch.delenv("BLAKE3_GPU_CHUNKS_PER_LANE", raising=False)
     assert [lib.blake3_gpu_leaf_group_chunks(n) for n in
             (0, 1 << 20, 32768 * 1024, 32768 * 1024 + 1, 64 << 20, (64 << 20) + 1, 128 << 20, (128 << 20) + 1,
-             192 << 20, 256 << 20, (256 << 20) + (16 << 20), (256 << 20) + (16 << 20) + 1, 320 << 20, 384 << 20,
+             192 << 20, 256 << 20, (256 << 20) + (32 << 20), (256 << 20) + (32 << 20) + 1, 320 << 20, 384 << 20,
              2 << 30, (4 << 30) + 1000)] == \
         [64, 64, 64, 256, 256, 256, 512, 512, 256, 1024, 1024, 256, 256, 512, 1024, 1024]
     monkeypatch.setenv("BLAKE3_GPU_QUAD_LEAF_MAX_CHUNKS", "0")

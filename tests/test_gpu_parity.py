@@ -146,17 +146,18 @@ def test_level_boundaries(b3, dev, monkeypatch, quad, fused):
 def test_one_round_and_a_quad_tail(b3, dev, monkeypatch, split):
     # a message just above 2^16, 2^17 or 2^18 chunks hashes its first 2^16 (2^17, 2^18) chunks
     # as one round of 256 leaf workgroups at one (two, four) chunks per lane and the tail past
-    # them, up to 2^14 chunks, on quad workgroups in the same launch; both subtrees and their
-    # parent in one more launch. Lengths around both ends of the three ranges, keyed and
+    # them, up to 2^15 chunks, on quad workgroups in the same launch; both subtrees and their
+    # parent in one more launch (up to 256 tail CVs in a 512-lane tree, more in a 1024-lane
+    # one). Lengths around both ends of the three ranges and across 2^14 tail chunks, keyed and
     # default mode; with BLAKE3_GPU_SPLIT_TAIL=0 the same lengths take the ordinary leaf.
     monkeypatch.setenv("BLAKE3_GPU_SPLIT_TAIL", split)
     from blake3_merkle_tree_amd import workloads
     k16, k17, k18 = (1 << 16) * 1024, (1 << 17) * 1024, (1 << 18) * 1024
-    lengths = [k16 + 1, k16 + 3000, k16 + (16 << 20), k16 + (16 << 20) + 1,
+    lengths = [k16 + 1, k16 + 3000, k16 + (16 << 20), k16 + (16 << 20) + 1, k16 + (32 << 20), k16 + (32 << 20) + 1,
                k17 + 1, k17 + 1024, k17 + 1025, k17 + 64 * 1024, k17 + 64 * 1024 + 1, k17 + (8 << 20),
-               k17 + (16 << 20), k17 + (16 << 20) + 1,
+               k17 + (16 << 20), k17 + (16 << 20) + 1, k17 + (24 << 20) + 5, k17 + (32 << 20) + 1,
                k18 + 1, k18 + 777, k18 + (64 << 10) + 5, k18 + (16 << 20) - 3, k18 + (16 << 20),
-               k18 + (16 << 20) + 1]
+               k18 + (16 << 20) + 1, k18 + (32 << 20), k18 + (32 << 20) + 1]
     buf = workloads.random_bytes(max(lengths), 25, dev)
     host = _host(buf)
     key = bytes(workloads.key_bytes(26)[0].tolist())
