@@ -528,6 +528,8 @@ struct BatchSegs {
     uint32_t *cv_out;
     uint8_t *digests;
     bool coherent;         // CVs are read by another workgroup of this launch: device-coherent stores
+    const uint32_t *pos_info;  // LDS, per lane position: its segment's info word (stage_segments)
+    const uint32_t *pos_key;   // LDS, per lane position: its segment's key, word w at w * kPosKeyStride
 
     __device__ uint32_t used_positions() const { return kLanes; }
     __device__ uint32_t root_bit() const { return kRoot; }
@@ -567,10 +569,11 @@ struct BatchSegs {
 };
 
 // Loads this workgroup's segments into LDS and maps every lane position to its segment
-// (or -1). Segments are sorted by lane start.
+// (or -1) and to that segment's info word, so that a tree level reads both at once rather
+// than one after the other. Segments are sorted by lane start.
 template <uint32_t C>
 __device__ __forceinline__ void stage_segments(const uint32_t *wg_first_seg, const Seg *segs, Seg *s_seg,
-                                               int *s_seg_of) {
+                                               int *s_seg_of, uint32_t *s_pos_info) {
     const uint32_t lane = threadIdx.x;
     const uint32_t first = wg_first_seg[blockIdx.x];
     const uint32_t nseg = wg_first_seg[blockIdx.x + 1] - first;
@@ -589,13 +592,105 @@ __device__ __forceinline__ void stage_segments(const uint32_t *wg_first_seg, con
         if (lane >= seg_lane(info) && lane < seg_lane(info) + seg_count(info)) s = static_cast<int>(lo);
     }
     s_seg_of[lane] = s;
+    s_pos_info[lane] = s >= 0 ? s_seg[s].info : 0u;
     __syncthreads();
+}
+
+// ---- a tree node position's segment ---------------------------------------------------
+
+// The segment of a node position as the tree levels use it: its index (-1: no segment),
+// first position and node count, and whether its result is a message's digest.
+struct NodeRef {
+    int s;
+    uint32_t start, n;
+    bool fin;
+};
+
+// Stride, in words, of a per-position key table (word w of position x at
+// w * kPosKeyStride + x): one word of padding spreads the eight words over LDS banks.
+constexpr uint32_t kPosKeyStride = kLanes + 1;
+constexpr uint32_t kPosKeyWords = 8 * kPosKeyStride;
+
+// Generic forms, from the Segs type's own lookups.
+template <class Segs>
+__device__ __forceinline__ NodeRef seg_node(const Segs &sg, uint32_t pos) {
+    const int s = sg.seg_of(pos);
+    if (s < 0) return NodeRef{-1, 0u, 0u, false};
+    return NodeRef{s, sg.start(s), sg.count(s), sg.final(s)};
+}
+template <class Segs>
+__device__ __forceinline__ void seg_key_words(const Segs &sg, const NodeRef &nd, uint32_t, uint32_t (&kw)[8]) {
+    sg.key_words(nd.s < 0 ? 0 : nd.s, kw);
+}
+
+// Batch segments: both lookups read the position tables, with no read waiting for another.
+__device__ __forceinline__ NodeRef seg_node(const BatchSegs &sg, uint32_t pos) {
+    const int s = sg.seg_of_pos[pos];
+    const uint32_t info = sg.pos_info[pos];
+    return NodeRef{s, seg_lane(info), seg_count(info), seg_final(info)};
+}
+__device__ __forceinline__ void seg_key_words(const BatchSegs &sg, const NodeRef &, uint32_t pos,
+                                              uint32_t (&kw)[8]) {
+    if (sg.keys) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) kw[w] = sg.pos_key[w * kPosKeyStride + pos];
+    } else {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) kw[w] = kIV[w];
+    }
+}
+
+// Words j and 4 + j of the key of the segment at pos (a quad lane's share).
+template <class Segs>
+__device__ __forceinline__ void seg_key_pair(const Segs &sg, const NodeRef &nd, uint32_t pos, uint32_t j,
+                                             uint32_t &lo, uint32_t &hi) {
+    uint32_t kw[8];
+    seg_key_words(sg, nd, pos, kw);
+    lo = pick4(kw[0], kw[1], kw[2], kw[3], j);
+    hi = pick4(kw[4], kw[5], kw[6], kw[7], j);
+}
+__device__ __forceinline__ void seg_key_pair(const BatchSegs &sg, const NodeRef &, uint32_t pos, uint32_t j,
+                                             uint32_t &lo, uint32_t &hi) {
+    if (sg.keys) {
+        lo = sg.pos_key[j * kPosKeyStride + pos];
+        hi = sg.pos_key[(4 + j) * kPosKeyStride + pos];
+    } else {
+        lo = pick4(kIV[0], kIV[1], kIV[2], kIV[3], j);
+        hi = pick4(kIV[4], kIV[5], kIV[6], kIV[7], j);
+    }
 }
 
 // compress_quad with this lane's message words read from LDS (src[moff[4r + t]] is its
 // t-th word of round r). The words of the first four rounds are read at once and those of
 // round r + 4 while round r runs (at most 16 reads in flight), so that no round waits for
-// LDS after the first; the compiler barrier keeps the reads in that order.
+// LDS after the first; the compiler barrier keeps the reads in that order. The same in two
+// parts, quad_msg_head and compress_quad_lds_rest, lets a caller issue the first reads
+// before other LDS reads that it waits for first. (compress_quad_lds stays one piece: the
+// compiler schedules its callers' chunk loops better that way, measured.)
+__device__ __forceinline__ void quad_msg_head(uint32_t (&m)[28], const uint32_t *src, const uint32_t (&moff)[28]) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) m[t] = src[moff[t]];
+}
+__device__ __forceinline__ void compress_quad_lds_rest(uint32_t &a, uint32_t &b, uint32_t &c, uint32_t &d,
+                                                       uint32_t (&m)[28], const uint32_t *src,
+                                                       const uint32_t (&moff)[28]) {
+#pragma unroll
+    for (int r = 0; r < 7; ++r) {
+        if (r + 4 < 7) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) m[4 * (r + 4) + t] = src[moff[4 * (r + 4) + t]];
+        }
+        asm volatile("" ::: "memory");
+        quarter(a, b, c, d, m[4 * r], m[4 * r + 1]);
+        b = quad_take<1>(b);
+        c = quad_take<2>(c);
+        d = quad_take<3>(d);
+        quarter(a, b, c, d, m[4 * r + 2], m[4 * r + 3]);
+        b = quad_take<3>(b);
+        c = quad_take<2>(c);
+        d = quad_take<1>(d);
+    }
+}
 __device__ __forceinline__ void compress_quad_lds(uint32_t &a, uint32_t &b, uint32_t &c, uint32_t &d,
                                                   const uint32_t *src, const uint32_t (&moff)[28]) {
     uint32_t m[28];
@@ -633,11 +728,20 @@ __device__ __forceinline__ uint32_t lane_levels(uint32_t used) {
     return l;
 }
 
-// One level of tree_levels_quad: level l's nodes are read from buffer Src (a
-// compile-time index, so that every message read is one LDS instruction with a constant
+// Segment kinds whose lookups are LDS reads (batch tables): their tree levels issue the
+// lookups, the key reads and the first message reads before waiting for any of them. The
+// others compute their lookups, and keep the order in which the compiler schedules them
+// best (measured: issuing the reads first there cost 2-3% at 1-4 MiB).
+template <class Segs>
+struct EarlyLevelReads : std::false_type {};
+template <>
+struct EarlyLevelReads<BatchSegs> : std::true_type {};
+
+// One level of tree_levels_quad for segment kinds whose lookups are computed: level l's
+// nodes are read from buffer Src (a compile-time index, so that every message read is one LDS instruction with a constant
 // offset) and level l + 1's written to the other buffer.
 template <uint32_t C, uint32_t Src, class Segs>
-__device__ __forceinline__ void quad_level(const Segs &sg, uint32_t l, uint32_t p, uint32_t j,
+__device__ __forceinline__ void quad_level_computed(const Segs &sg, uint32_t l, uint32_t p, uint32_t j,
                                            const uint32_t (&moff)[28], uint32_t (*buf)[8][C]) {
     const uint32_t pos = p << (l + 1);
     if (pos >= C) return;
@@ -667,6 +771,50 @@ __device__ __forceinline__ void quad_level(const Segs &sg, uint32_t l, uint32_t 
     dst[j * C + p] = lo;
     dst[(4 + j) * C + p] = hi;
     if (l + 1 == r) sg.emit_pair(s, j, lo, hi);
+}
+
+// One level of tree_levels_quad for the batch segment kinds: the same, with the node's
+// segment, its key words and the first sixteen message words read before any of them is
+// waited for.
+template <uint32_t C, uint32_t Src, class Segs>
+__device__ __forceinline__ void quad_level_early(const Segs &sg, uint32_t l, uint32_t p, uint32_t j,
+                                                 const uint32_t (&moff)[28], uint32_t (*buf)[8][C]) {
+    const uint32_t pos = p << (l + 1);
+    if (pos >= C) return;  // so p < C / 2: every message offset lies inside the level buffer
+    const uint32_t *src = &buf[Src][0][0];
+    const NodeRef nd = seg_node(sg, pos);
+    uint32_t m[28];
+    quad_msg_head(m, src, moff);
+    uint32_t klo, khi;
+    seg_key_pair(sg, nd, pos, j, klo, khi);
+    if (nd.s < 0) return;
+    const uint32_t r = ceil_log2(nd.n);
+    if (l >= r) return;  // segment already reduced to one node
+    // every condition above depends on p only: the quad's four lanes stay together
+    uint32_t lo, hi;
+    if ((((2 * p + 1) << l) - nd.start) < nd.n) {  // a right child exists
+        uint32_t a = klo, b = khi;
+        uint32_t c = pick4(kIV[0], kIV[1], kIV[2], kIV[3], j);
+        const uint32_t flags = sg.mode() | kParent | (nd.fin && l + 1 == r ? sg.root_bit() : 0u);
+        uint32_t d = j == 3u ? flags : (j == 2u ? kBlockBytes : 0u);  // counter 0, length 64
+        compress_quad_lds_rest(a, b, c, d, m, src, moff);
+        lo = a ^ c;
+        hi = b ^ d;
+    } else {  // carry node 2p up unchanged
+        lo = src[j * C + 2 * p];
+        hi = src[(4 + j) * C + 2 * p];
+    }
+    uint32_t *dst = &buf[1 - Src][0][0];
+    dst[j * C + p] = lo;
+    dst[(4 + j) * C + p] = hi;
+    if (l + 1 == r) sg.emit_pair(nd.s, j, lo, hi);
+}
+
+template <uint32_t C, uint32_t Src, class Segs>
+__device__ __forceinline__ void quad_level(const Segs &sg, uint32_t l, uint32_t p, uint32_t j,
+                                           const uint32_t (&moff)[28], uint32_t (*buf)[8][C]) {
+    if constexpr (EarlyLevelReads<Segs>::value) quad_level_early<C, Src>(sg, l, p, j, moff, buf);
+    else quad_level_computed<C, Src>(sg, l, p, j, moff, buf);
 }
 
 // Levels l .. levels-1 of the tree on quads, the level-l nodes being in buf[l & 1]
@@ -725,18 +873,14 @@ __device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs 
     }
     const uint32_t lane_lv = lane_levels(sg.used_positions());
     uint32_t l = 0;
-    for (; l < levels && l < lane_lv; ++l) {
-        __syncthreads();
-        const uint32_t pos = lane << (l + 1);  // first leaf position under output node `lane`
-        if (pos >= C) continue;
-        const int s = sg.seg_of(pos);
-        if (s < 0) continue;
-        const uint32_t start = sg.start(s), n = sg.count(s), r = ceil_log2(n);
-        if (l >= r) continue;  // segment already reduced to one node
-        const uint32_t(*src)[C] = buf[l & 1];
-        uint32_t node[8];
-        const bool has_right = (((2 * lane + 1) << l) - start) < n;
-        if (has_right) {
+    if constexpr (EarlyLevelReads<Segs>::value) {
+        for (; l < levels && l < lane_lv; ++l) {
+            __syncthreads();
+            const uint32_t pos = lane << (l + 1);  // first leaf position under output node `lane`
+            if (pos >= C) continue;                // so lane < C / 2: both children lie in the buffer
+            // the segment, the children and the key are read before any of them is waited for
+            const NodeRef nd = seg_node(sg, pos);
+            const uint32_t(*src)[C] = buf[l & 1];
             uint32_t m[16];
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
@@ -744,16 +888,53 @@ __device__ __forceinline__ void tree_reduce(const uint32_t (&cv)[8], const Segs 
                 m[w] = pr.x;
                 m[w + 8] = pr.y;
             }
-            sg.key_words(s, node);
-            const uint32_t flags = sg.mode() | kParent | (sg.final(s) && l + 1 == r ? sg.root_bit() : 0u);
-            compress(node, m, 0, 0, kBlockBytes, flags);
-        } else {
+            uint32_t node[8];
+            seg_key_words(sg, nd, pos, node);
+            if (nd.s < 0) continue;
+            const uint32_t r = ceil_log2(nd.n);
+            if (l >= r) continue;  // segment already reduced to one node
+            if ((((2 * lane + 1) << l) - nd.start) < nd.n) {  // a right child exists
+                const uint32_t flags = sg.mode() | kParent | (nd.fin && l + 1 == r ? sg.root_bit() : 0u);
+                compress(node, m, 0, 0, kBlockBytes, flags);
+            } else {  // carry the left child up unchanged
 #pragma unroll
-            for (int w = 0; w < 8; ++w) node[w] = src[w][2 * lane];
+                for (int w = 0; w < 8; ++w) node[w] = m[w];
+            }
+#pragma unroll
+            for (int w = 0; w < 8; ++w) buf[(l + 1) & 1][w][lane] = node[w];
+            if (l + 1 == r) sg.emit(nd.s, node);
         }
+    } else {
+        for (; l < levels && l < lane_lv; ++l) {
+            __syncthreads();
+            const uint32_t pos = lane << (l + 1);  // first leaf position under output node `lane`
+            if (pos >= C) continue;
+            const int s = sg.seg_of(pos);
+            if (s < 0) continue;
+            const uint32_t start = sg.start(s), n = sg.count(s), r = ceil_log2(n);
+            if (l >= r) continue;  // segment already reduced to one node
+            const uint32_t(*src)[C] = buf[l & 1];
+            uint32_t node[8];
+            const bool has_right = (((2 * lane + 1) << l) - start) < n;
+            if (has_right) {
+                uint32_t m[16];
 #pragma unroll
-        for (int w = 0; w < 8; ++w) buf[(l + 1) & 1][w][lane] = node[w];
-        if (l + 1 == r) sg.emit(s, node);
+                for (int w = 0; w < 8; ++w) {
+                    const uint2 pr = *reinterpret_cast<const uint2 *>(&src[w][2 * lane]);
+                    m[w] = pr.x;
+                    m[w + 8] = pr.y;
+                }
+                sg.key_words(s, node);
+                const uint32_t flags = sg.mode() | kParent | (sg.final(s) && l + 1 == r ? sg.root_bit() : 0u);
+                compress(node, m, 0, 0, kBlockBytes, flags);
+            } else {
+#pragma unroll
+                for (int w = 0; w < 8; ++w) node[w] = src[w][2 * lane];
+            }
+#pragma unroll
+            for (int w = 0; w < 8; ++w) buf[(l + 1) & 1][w][lane] = node[w];
+            if (l + 1 == r) sg.emit(s, node);
+        }
     }
     if (l < levels) tree_levels_quad<C, Segs, InLoop>(sg, l, levels, buf);
 }
@@ -1212,6 +1393,7 @@ struct LevelSlots {
     const uint32_t *keys;  // global, nullptr for default mode
     uint32_t *cv_out;
     uint8_t *digests;
+    const uint32_t *slot_key;  // LDS, kMaxSlots x 8 words: slot s's key at 8 * s (keyed mode)
 
     __device__ uint32_t used_positions() const { return n << lanes_log2; }
     __device__ uint32_t root_bit() const { return kRoot; }
@@ -1225,7 +1407,8 @@ struct LevelSlots {
     __device__ uint32_t mode() const { return keys ? kKeyedHash : 0u; }
     __device__ void key_words(int s, uint32_t (&kw)[8]) const {
         if (keys) {
-            load_cv(kw, keys + 8ull * seg[s].msg);
+#pragma unroll
+            for (int w = 0; w < 8; ++w) kw[w] = slot_key[8 * s + w];
         } else {
 #pragma unroll
             for (int w = 0; w < 8; ++w) kw[w] = kIV[w];
@@ -1241,6 +1424,16 @@ struct LevelSlots {
     }
 };
 
+template <>
+struct EarlyLevelReads<LevelSlots> : std::true_type {};
+
+// The slot of a position is pos >> lanes_log2 (below kMaxSlots for any position of the
+// workgroup), so its key is read without waiting for the segment's info.
+__device__ __forceinline__ void seg_key_words(const LevelSlots &sg, const NodeRef &, uint32_t pos,
+                                              uint32_t (&kw)[8]) {
+    sg.key_words(static_cast<int>(pos >> sg.lanes_log2), kw);
+}
+
 // Fused first level pass of a batch (BatchLeafArgs::up), called by the whole workgroup after
 // its leaf tree has written the CVs of its segments that are not whole messages, with
 // device-coherent stores. Each such CV belongs to one segment of the first level pass; its
@@ -1254,12 +1447,14 @@ struct LevelSlots {
 // round's largest segment (a ragged batch's level segments hold a few CVs each). The
 // ordering is that of fused_levels. `own` (256 words of LDS, free once the leaf tree is
 // done) lists the level segments this workgroup took last; `slots` (kMaxSlots entries)
-// holds a round's segments.
+// holds a round's segments, `slot_key` (8 * kMaxSlots words) their keys, and `round` four
+// words: the number of segments taken, then a round's slot count, width and tree depth.
 __device__ void fused_batch_level(const BatchLeafArgs &a, const Seg *s_seg, uint32_t nseg, uint32_t *lds,
-                                  uint32_t *own, uint32_t *own_n, Seg *slots) {
+                                  uint32_t *own, uint32_t *round, Seg *slots, uint32_t *slot_key) {
+    static_assert(kMaxSlots == kWaveLanes, "one wave plans a round, one lane per slot");
     const uint32_t lane = threadIdx.x;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's CV stores have completed
-    if (lane == 0) *own_n = 0;
+    if (lane == 0) round[0] = 0;
     __syncthreads();  // ... in every wave, and the leaf tree is done with the LDS
     if (lane < nseg) {
         const Seg g = s_seg[lane];
@@ -1270,36 +1465,62 @@ __device__ void fused_batch_level(const BatchLeafArgs &a, const Seg *s_seg, uint
             uint32_t *ticket = a.lvl_ctr + j;
             if (__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == inputs) {
                 __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                own[atomicAdd(own_n, 1u)] = j;
+                own[atomicAdd(&round[0], 1u)] = j;
             }
         }
     }
     __syncthreads();
-    const uint32_t owned = *own_n;
+    const uint32_t owned = round[0];
     auto buf = reinterpret_cast<uint32_t(*)[8][kLevelLanes]>(lds);
     for (uint32_t o = 0; o < owned;) {
-        // this round: as many of the next segments as fit in the workgroup in slots of equal
-        // power-of-two width, the smallest that holds the largest of them (at least
-        // kMinSlotLanes lanes, so at most kMaxSlots segments)
-        __syncthreads();  // the previous round is done with `slots` and the LDS
-        uint32_t r = 0, width_log2 = ceil_log2(kMinSlotLanes);
-        while (o + r < owned) {
-            const uint32_t need = ceil_log2(seg_count(a.lvl_segs[own[o + r]].info));
-            const uint32_t w = need > width_log2 ? need : width_log2;
-            if ((r + 1) << w > kLevelLanes) break;
-            width_log2 = w;
-            ++r;
+        __syncthreads();  // the previous round is done with `slots`, `slot_key`, `round` and the LDS
+        if (lane < kWaveLanes) {
+            // wave 0 plans this round: as many of the next segments as fit in the workgroup in
+            // slots of equal power-of-two width, the smallest that holds the largest of them (at
+            // least kMinSlotLanes lanes, so at most kMaxSlots segments). Lane i looks at the
+            // i-th next segment; running maxima of the widths and tree depths over the lanes
+            // then say which of them fit.
+            const uint32_t i = o + lane;
+            const bool valid = i < owned;
+            Seg g{0u, 0u, 0u, 0u};
+            uint32_t depth = 0;
+            if (valid) {
+                g = a.lvl_segs[own[i]];
+                depth = ceil_log2(seg_count(g.info));
+            }
+            uint32_t width = depth > ceil_log2(kMinSlotLanes) ? depth : ceil_log2(kMinSlotLanes);
+#pragma unroll
+            for (uint32_t d = 1; d < kWaveLanes; d <<= 1) {
+                const uint32_t w2 = __shfl_up(width, d), d2 = __shfl_up(depth, d);
+                if (lane >= d) {
+                    width = w2 > width ? w2 : width;
+                    depth = d2 > depth ? d2 : depth;
+                }
+            }
+            // (lane + 1) << width grows with the lane, so the lanes that fit are a prefix
+            const bool fits = valid && ((lane + 1) << width) <= kLevelLanes;
+            const uint32_t r = static_cast<uint32_t>(__popcll(__ballot(fits)));
+            if (lane < r) {
+                slots[lane] = g;
+                if (a.keys) {
+                    uint32_t kw[8];
+                    load_cv(kw, a.keys + 8ull * g.msg);
+#pragma unroll
+                    for (int w = 0; w < 8; ++w) slot_key[8 * lane + w] = kw[w];
+                }
+            }
+            if (lane + 1 == (r > 0 ? r : 1u)) {
+                round[1] = r;
+                round[2] = width;
+                round[3] = depth;
+            }
         }
-        if (lane < r) slots[lane] = a.lvl_segs[own[o + lane]];
         __syncthreads();
-        LevelSlots sg{slots, r, width_log2, a.keys, a.lvl_cv_out, a.digests};
+        const uint32_t r = round[1], levels = round[3];
+        if (r == 0) break;  // not reached: a level segment holds at most kLevelLanes CVs
+        LevelSlots sg{slots, r, round[2], a.keys, a.lvl_cv_out, a.digests, slot_key};
         const uint32_t s = lane >> sg.lanes_log2, x = lane - (s << sg.lanes_log2);
         uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        uint32_t levels = 0;
-        for (uint32_t k = 0; k < r; ++k) {
-            const uint32_t lv = ceil_log2(seg_count(slots[k].info));
-            levels = lv > levels ? lv : levels;
-        }
         if (s < r) {
             const Seg g = slots[s];
             const uint32_t cnt = seg_count(g.info);
@@ -1326,17 +1547,29 @@ __device__ void fused_batch_level(const BatchLeafArgs &a, const Seg *s_seg, uint
 
 // Fused: the first level pass runs in this launch (fused_batch_level); a separate
 // instantiation, so that its registers do not weigh on the default leaf.
+// LDS of the batch leaf: that of the leaf, and room beside the tree's level buffers for the
+// per-position key table, written once the chunk phase is done with the LDS (and in the
+// fused level pass, once the leaf tree is done with it, the slots' keys).
+template <uint32_t K, bool Staged>
+constexpr uint32_t batch_leaf_lds_words() {
+    constexpr uint32_t tree = 2 * 8 * kLanes + kPosKeyWords;
+    return leaf_lds_words<K, Staged>() > tree ? leaf_lds_words<K, Staged>() : tree;
+}
+
 template <uint32_t K, bool Staged, bool Fused>
 __global__ __launch_bounds__(kLeafLanes) void leaf_batch_kernel(BatchLeafArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t lds[leaf_lds_words<K, Staged>()];
+    __shared__ __attribute__((aligned(16))) uint32_t lds[batch_leaf_lds_words<K, Staged>()];
     __shared__ Seg s_seg[kLanes];
     __shared__ int s_seg_of[kLanes];
-    __shared__ uint32_t s_own_n;
+    __shared__ uint32_t s_pos_info[kLanes];
+    __shared__ uint32_t s_round[4];
     __shared__ Seg s_slots[Fused ? kMaxSlots : 1];
-    stage_segments<kLanes>(a.wg_first_seg, a.segs, s_seg, s_seg_of);
+    stage_segments<kLanes>(a.wg_first_seg, a.segs, s_seg, s_seg_of, s_pos_info);
     const uint32_t lane = threadIdx.x;
     const int s = s_seg_of[lane];
-    BatchSegs sg{s_seg, s_seg_of, a.keys, a.cv_out, a.digests, Fused};
+    static_assert(8 * kMaxSlots <= kPosKeyWords, "the fused level pass keeps its slots' keys in the key table");
+    uint32_t *pos_key = lds + 2 * 8 * kLanes;
+    BatchSegs sg{s_seg, s_seg_of, a.keys, a.cv_out, a.digests, Fused, s_pos_info, pos_key};
     uint32_t key[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const uint8_t *ptr = a.base;
@@ -1381,32 +1614,44 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_batch_kernel(BatchLeafArgs a)
         lane_subtree<K, true>(cv, ptr, nl, last_len, c0, key, sg.mode(), root);
     }
     __syncthreads();  // every wave is done with its stage buffer before the tree reuses it
+    if (a.keys && s >= 0) {  // the key table, read by the tree levels behind their first barrier
+#pragma unroll
+        for (int w = 0; w < 8; ++w) pos_key[w * kPosKeyStride + lane] = key[w];
+    }
     tree_reduce<kLanes>(cv, sg, a.wg_levels[blockIdx.x], reinterpret_cast<uint32_t(*)[8][kLanes]>(lds));
     if (Fused)
         fused_batch_level(a, s_seg, a.wg_first_seg[blockIdx.x + 1] - a.wg_first_seg[blockIdx.x], lds,
-                          reinterpret_cast<uint32_t *>(s_seg_of), &s_own_n, s_slots);
+                          reinterpret_cast<uint32_t *>(s_seg_of), s_round, s_slots, pos_key);
 }
 
 __global__ __launch_bounds__(kLevelLanes) void level_batch_kernel(BatchLevelArgs a) {
+    static_assert(kLevelLanes == kLanes, "the per-position key table is sized for kLanes positions");
     __shared__ uint32_t buf[2][8][kLevelLanes];
     __shared__ Seg s_seg[kLevelLanes];
     __shared__ int s_seg_of[kLevelLanes];
-    stage_segments<kLevelLanes>(a.wg_first_seg, a.segs, s_seg, s_seg_of);
+    __shared__ uint32_t s_pos_info[kLevelLanes];
+    __shared__ uint32_t s_pos_key[kPosKeyWords];
+    stage_segments<kLevelLanes>(a.wg_first_seg, a.segs, s_seg, s_seg_of, s_pos_info);
     const uint32_t lane = threadIdx.x;
     const int s = s_seg_of[lane];
     uint32_t cv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    BatchSegs sg{s_seg, s_seg_of, a.keys, a.cv_out, a.digests, false};
+    BatchSegs sg{s_seg, s_seg_of, a.keys, a.cv_out, a.digests, false, s_pos_info, s_pos_key};
     if (s >= 0) {
         const Seg g = s_seg[s];
         const uint32_t x = lane - seg_lane(g.info);
+        uint32_t key[8];
+        sg.key_words(s, key);
         load_cv(cv, a.cv_in + 8ull * (g.first + x));
+        if (a.keys) {  // the key table, read by the tree levels behind their first barrier
+#pragma unroll
+            for (int w = 0; w < 8; ++w) s_pos_key[w * kPosKeyStride + lane] = key[w];
+        }
         if (seg_pair(g.info) && x + 1 == seg_count(g.info)) {
             // the message's end was split in two subtrees in pass 0: this node is their parent
-            uint32_t left[8], key[8];
+            uint32_t left[8];
 #pragma unroll
             for (int w = 0; w < 8; ++w) left[w] = cv[w];
             load_cv(cv, a.cv_in + 8ull * (g.first + x + 1));
-            sg.key_words(s, key);
             parent_left(cv, left, key, sg.mode(), false);
         }
     }
