@@ -681,14 +681,7 @@ __device__ __forceinline__ void compress_quad_lds_rest(uint32_t &a, uint32_t &b,
             for (int t = 0; t < 4; ++t) m[4 * (r + 4) + t] = src[moff[4 * (r + 4) + t]];
         }
         asm volatile("" ::: "memory");
-        quarter(a, b, c, d, m[4 * r], m[4 * r + 1]);
-        b = quad_take<1>(b);
-        c = quad_take<2>(c);
-        d = quad_take<3>(d);
-        quarter(a, b, c, d, m[4 * r + 2], m[4 * r + 3]);
-        b = quad_take<3>(b);
-        c = quad_take<2>(c);
-        d = quad_take<1>(d);
+        quad_round_words(a, b, c, d, m[4 * r], m[4 * r + 1], m[4 * r + 2], m[4 * r + 3]);
     }
 }
 __device__ __forceinline__ void compress_quad_lds(uint32_t &a, uint32_t &b, uint32_t &c, uint32_t &d,
@@ -703,14 +696,7 @@ __device__ __forceinline__ void compress_quad_lds(uint32_t &a, uint32_t &b, uint
             for (int t = 0; t < 4; ++t) m[4 * (r + 4) + t] = src[moff[4 * (r + 4) + t]];
         }
         asm volatile("" ::: "memory");
-        quarter(a, b, c, d, m[4 * r], m[4 * r + 1]);
-        b = quad_take<1>(b);
-        c = quad_take<2>(c);
-        d = quad_take<3>(d);
-        quarter(a, b, c, d, m[4 * r + 2], m[4 * r + 3]);
-        b = quad_take<3>(b);
-        c = quad_take<2>(c);
-        d = quad_take<1>(d);
+        quad_round_words(a, b, c, d, m[4 * r], m[4 * r + 1], m[4 * r + 2], m[4 * r + 3]);
     }
 }
 
