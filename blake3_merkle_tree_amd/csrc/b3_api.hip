@@ -81,10 +81,11 @@ constexpr size_t kSlotMaxBytes = size_t(64) << 20;  // larger requests use the p
 // A scratch slot's event only marks when the device has passed the end of a call: the host
 // tests it before it reuses the memory, and other streams wait on it on the device. None of
 // that needs the system-scope cache write-back and invalidation that a recorded event
-// otherwise performs. Single messages and uniform batches record an event without it
-// (MI355X, back to back, one process per build: 1 MiB 26.0 -> 23.9 us, 64 MiB 42.8 -> 40.5
-// us, 256 MiB 105.2 -> 103.1 us); batches planned into a task table keep the fenced event,
-// which measured faster there (256 ragged messages 75.8 against 77.3 us).
+// otherwise performs, and which holds the next launch on the stream back by several
+// microseconds. Every call records its events without it (MI355X, back to back, one
+// process per build: 1 MiB 26.0 -> 23.9 us, 64 MiB 42.8 -> 40.5 us, 256 MiB 105.2 -> 103.1
+// us; 256 ragged messages 74.1 -> 71.0 us with the task table's upload event unfenced too,
+// 72.7 us with that one alone).
 constexpr unsigned kUnfencedEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
 // Each slot also holds the tickets of fused level passes: zeroed once, when the slot's
 // memory is allocated, and left at zero by every launch that uses them.
@@ -94,9 +95,7 @@ struct ScratchSlot {
     void *p = nullptr;
     size_t bytes = 0;
     uint32_t *tickets = nullptr;     // kSlotTicketWords words after the slot's `bytes`
-    hipEvent_t done = nullptr;       // recorded after the work of the slot's last call (one of the two below)
-    hipEvent_t unfenced = nullptr;   // the slot's event without the system-scope fence
-    hipEvent_t fenced = nullptr;     // and with it
+    hipEvent_t done = nullptr;       // recorded after the work of the slot's last call (kUnfencedEventFlags)
     hipStream_t last = nullptr;      // that call's stream (a preference only: every reuse waits on done)
     bool used = false;               // done has been recorded
     bool held = false;               // taken by a call that has not yet returned
@@ -129,20 +128,17 @@ int fill_scratch(void *p, size_t bytes, hipStream_t s) {
 // a stream-ordered allocation released in stream order on the caller's stream.
 class StreamScratch {
   public:
-    // fenced: the slot's end-of-call event performs the system-scope fence (task-table batches)
-    explicit StreamScratch(hipStream_t s, bool fenced = false) : s_(s), fenced_(fenced) {}
+    explicit StreamScratch(hipStream_t s) : s_(s) {}
     ~StreamScratch() {
         if (slot_ != nullptr) {
             std::lock_guard<std::mutex> lock(slots_->mu);
-            hipEvent_t ev = fenced_ ? slot_->fenced : slot_->unfenced;
-            if (hipEventRecord(ev, s_) != hipSuccess) {
+            if (hipEventRecord(slot_->done, s_) != hipSuccess) {
                 // the device could not be told when this call's work ends: never reuse the memory
                 (void)hipGetLastError();
                 slot_->p = nullptr;
                 slot_->bytes = 0;
                 slot_->used = false;
             } else {
-                slot_->done = ev;
                 slot_->last = s_;
                 slot_->used = true;
             }
@@ -209,14 +205,9 @@ class StreamScratch {
             // a slot last used on this stream needs no wait: the stream's order holds
             wait = sl->used && score == 1;
         }
-        if (sl->unfenced == nullptr && hipEventCreateWithFlags(&sl->unfenced, kUnfencedEventFlags) != hipSuccess) {
+        if (sl->done == nullptr && hipEventCreateWithFlags(&sl->done, kUnfencedEventFlags) != hipSuccess) {
             (void)hipGetLastError();
-            sl->unfenced = nullptr;
-            return release_unused(ds, sl);
-        }
-        if (sl->fenced == nullptr && hipEventCreateWithFlags(&sl->fenced, hipEventDisableTiming) != hipSuccess) {
-            (void)hipGetLastError();
-            sl->fenced = nullptr;
+            sl->done = nullptr;
             return release_unused(ds, sl);
         }
         if (sl->bytes < bytes) {  // grow an idle slot (its last call's work has finished)
@@ -272,7 +263,6 @@ class StreamScratch {
     }
 
     hipStream_t s_;
-    bool fenced_;
     void *p_ = nullptr;
     ScratchSlot *slot_ = nullptr;
     DeviceSlots *slots_ = nullptr;
@@ -348,8 +338,8 @@ int launched(hipError_t e) {
 // uploaded by a copy kernel on the caller's stream, which reads it over the bus: the
 // kernels after it wait for nothing but the stream's order, where a copy-engine transfer
 // from pageable memory left ~18 us between a batch's launches. The buffer's event,
-// recorded after that kernel, must have completed before the host writes the buffer
-// again. A call that finds no such buffer free builds its table in pageable memory and
+// recorded after that kernel (without the system-scope fence: it only has to show that the
+// kernel's reads are done), must have completed before the host writes the buffer again. A call that finds no such buffer free builds its table in pageable memory and
 // copies it with hipMemcpyAsync: the host never waits for the device here.
 constexpr int kStagesPerDevice = 16;
 constexpr size_t kStageArenaSlice = size_t(256) << 10;  // each buffer's first size, from one arena
@@ -432,7 +422,7 @@ class TableStage {
         }
         st_ = st;
         ds_ = &ds;
-        if (st->done == nullptr && hipEventCreateWithFlags(&st->done, hipEventDisableTiming) != hipSuccess) {
+        if (st->done == nullptr && hipEventCreateWithFlags(&st->done, kUnfencedEventFlags) != hipSuccess) {
             (void)hipGetLastError();
             st->done = nullptr;
             return release();
@@ -943,7 +933,7 @@ int hash_batch(const void *base, const uint64_t *offsets, const uint64_t *length
         lay[p].cv_out = at;
         at += align256(plan.passes[p].out_cvs * 32);
     }
-    StreamScratch scratch(s, true);
+    StreamScratch scratch(s);
     rc = scratch.alloc(at);
     if (rc != B3G_OK) return rc;
     uint8_t *d = scratch.get();
