@@ -68,6 +68,19 @@ __device__ __forceinline__ void compress_block_chained(const uint32_t (&s)[16], 
     compress_chained(s, m, lo, hi, kBlockBytes, flags, v);
 }
 
+// Issue-priority turns for waves that share a SIMD (Turns below). The SIMD issues from the
+// highest-priority wave that is ready, and among equals from the oldest, so of two waves
+// that start together the older one runs its whole chunk with the younger one only taking
+// the cycles it leaves idle, and the younger then runs alone, at the rate of a lone wave,
+// for most of its own chunk. Stepping a wave's priority down from 3 to 0 as it passes
+// blocks 4, 8 and 12 of its chunk lets the waves take turns every four blocks, so both keep
+// the SIMD busy until they end, together.
+__device__ __forceinline__ void turn_priority_at(uint32_t b) {
+    if (b == 4) __builtin_amdgcn_s_setprio(2);
+    else if (b == 8) __builtin_amdgcn_s_setprio(1);
+    else if (b == 12) __builtin_amdgcn_s_setprio(0);
+}
+
 // Full 1 KiB chunk with per-lane 16-byte loads (16-byte aligned). Blocks are handled in
 // pairs with two register sets, so the loads of a block are issued ahead of its
 // compression and no registers are copied between iterations; the reload of the even set
@@ -76,6 +89,7 @@ __device__ __forceinline__ void compress_block_chained(const uint32_t (&s)[16], 
 // (compress_chained), alternating between two arrays; the first block starts from the
 // state (cv, 0), whose fold is cv. `end_flags` go on the last block (CHUNK_END, plus ROOT
 // when the chunk is the whole message).
+template <bool Turns = false>
 __device__ __forceinline__ void hash_full_chunk(uint32_t (&cv)[8], const uint8_t *chunk, uint32_t ctr_lo,
                                                 uint32_t ctr_hi, uint32_t mode, uint32_t end_flags) {
     const uint4 *p = reinterpret_cast<const uint4 *>(chunk);
@@ -85,7 +99,9 @@ __device__ __forceinline__ void hash_full_chunk(uint32_t (&cv)[8], const uint8_t
 #pragma unroll
     for (int i = 0; i < 8; ++i) st[i] = cv[i], st[i + 8] = 0;
     Block even = load_block(p);
+    if (Turns) __builtin_amdgcn_s_setprio(3);
     for (uint32_t b = 0; b < kBlocksPerChunk; b += 2) {
+        if (Turns) turn_priority_at(b);
         const Block odd = load_block(p + 4 * (b + 1));
         compress_block_chained(st, even, ctr_lo, ctr_hi, mode | (b == 0 ? kChunkStart : 0u), su);
         const uint32_t next = b + 2 < kBlocksPerChunk ? b + 2 : kBlocksPerChunk - 2;
@@ -196,13 +212,16 @@ __device__ void hash_short_chunk(uint32_t (&cv)[8], const uint8_t *chunk, uint32
 // for memory every time. Every block but the last lies wholly inside the chunk; a lane's
 // loop runs its own block count and the wave's last blocks are compressed together, with
 // the piece holding the last byte substituted.
+template <bool Turns = false>
 __device__ void hash_short_chunk_ahead(uint32_t (&cv)[8], const uint8_t *chunk, uint32_t len, uint32_t ctr_lo,
                                        uint32_t ctr_hi, uint32_t mode, uint32_t end_flags) {
     const uint32_t nb = len == 0 ? 1u : (len + kBlockBytes - 1) / kBlockBytes;
     const uint4 tail = load_tail_piece(chunk, len);
     const uint32_t tail_off = len & ~15u;
     Block cur = load_block_or_zero(chunk, 0, len);
+    if (Turns) __builtin_amdgcn_s_setprio(3);
     for (uint32_t b = 0; b + 1 < nb; ++b) {
+        if (Turns) turn_priority_at(b);
         const Block next = load_block_or_zero(chunk, (b + 1) * kBlockBytes, len);
         compress_block(cv, cur, ctr_lo, ctr_hi, mode | (b == 0 ? kChunkStart : 0u));
         cur = next;
@@ -267,7 +286,7 @@ __device__ __forceinline__ void fold_chunk(uint32_t (&c)[8], uint32_t k, uint32_
 // per-lane and bounded by the byte count. The last chunk has last_len bytes (1024 unless
 // it ends the message). `root`: this node is the whole message, so its final compression
 // carries ROOT.
-template <uint32_t K, bool Ahead = false>
+template <uint32_t K, bool Ahead = false, bool Turns = false>
 __device__ __forceinline__ void lane_subtree(uint32_t (&c)[8], const uint8_t *ptr, uint32_t nl,
                                              uint32_t last_len, uint64_t ctr0, const uint32_t (&key)[8],
                                              uint32_t mode, bool root) {
@@ -281,7 +300,7 @@ __device__ __forceinline__ void lane_subtree(uint32_t (&c)[8], const uint8_t *pt
         const uint32_t end_flags = kChunkEnd | (root && nl == 1 ? kRoot : 0u);
         const uint8_t *chunk = ptr + static_cast<uint64_t>(k) * kChunkBytes;
         const uint32_t len = k + 1 == nl ? last_len : kChunkBytes;
-        if (Ahead) hash_short_chunk_ahead(c, chunk, len, lo, hi, mode, end_flags);
+        if (Ahead) hash_short_chunk_ahead<Turns>(c, chunk, len, lo, hi, mode, end_flags);
         else hash_short_chunk(c, chunk, len, lo, hi, mode, end_flags);
         if (K > 1) fold_chunk<K>(c, k, slot1c, slot2c, k + 1 < nl, fin_k, key, mode);
     }
@@ -299,7 +318,7 @@ __device__ __forceinline__ void lane_subtree(uint32_t (&c)[8], const uint8_t *pt
 // end, level by level: node i = parent(node 2i, node 2i+1). `root_flag` (ROOT or 0)
 // marks the lane's node as the whole message: its last compression carries it.
 // LineAhead: each chunk by hash_full_chunk_line_ahead rather than hash_full_chunk.
-template <uint32_t K, bool LineAhead>
+template <uint32_t K, bool LineAhead, bool Turns = false>
 __device__ __forceinline__ void direct_subtree(uint32_t (&c)[8], const uint8_t *ptr, uint64_t ctr0,
                                                const uint32_t (&key)[8], uint32_t mode, uint32_t root_flag,
                                                uint32_t *slots) {
@@ -322,7 +341,7 @@ __device__ __forceinline__ void direct_subtree(uint32_t (&c)[8], const uint8_t *
                                        step + 1 < K ? ptr + static_cast<uint64_t>((k + 1) % K) * kChunkBytes
                                                     : chunk + (kBlocksPerChunk - 2) * kBlockBytes);
         else
-            hash_full_chunk(c, ptr + static_cast<uint64_t>(k) * kChunkBytes, static_cast<uint32_t>(ctr),
+            hash_full_chunk<Turns>(c, ptr + static_cast<uint64_t>(k) * kChunkBytes, static_cast<uint32_t>(ctr),
                             static_cast<uint32_t>(ctr >> 32), mode, kChunkEnd | (K == 1 ? root_flag : 0u));
         if (K == 1) return;
 #pragma unroll
@@ -1592,13 +1611,14 @@ __global__ __launch_bounds__(kLeafLanes) void leaf_batch_kernel(BatchLeafArgs a)
             staged_subtree<K>(cv, rows, lds + (lane / kWaveLanes) * (kStageBytes / 4), c0, key, sg.mode(),
                               root ? kRoot : 0u);
         } else {
-            direct_subtree<K, false>(cv, ptr, c0, key, sg.mode(), root ? kRoot : 0u, lds + lane);
+            direct_subtree<K, false, K == 1>(cv, ptr, c0, key, sg.mode(), root ? kRoot : 0u, lds + lane);
         }
     } else if (nl > 0) {
         // the ends of a batch's messages: whole workgroups of them, often alone on their
         // SIMDs at the end of the grid, so their loads are issued a block ahead
-        lane_subtree<K, true>(cv, ptr, nl, last_len, c0, key, sg.mode(), root);
+        lane_subtree<K, true, K == 1>(cv, ptr, nl, last_len, c0, key, sg.mode(), root);
     }
+    if (K == 1) __builtin_amdgcn_s_setprio(0);  // the turns end with the chunks
     __syncthreads();  // every wave is done with its stage buffer before the tree reuses it
     if (a.keys && s >= 0) {  // the key table, read by the tree levels behind their first barrier
 #pragma unroll
