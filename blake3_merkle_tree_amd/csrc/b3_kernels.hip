@@ -76,9 +76,9 @@ __device__ __forceinline__ void compress_block_chained(const uint32_t (&s)[16], 
 // blocks 4, 8 and 12 of its chunk lets the waves take turns every four blocks, so both keep
 // the SIMD busy until they end, together.
 __device__ __forceinline__ void turn_priority_at(uint32_t b) {
-    if (b == 4) __builtin_amdgcn_s_setprio(2);
-    else if (b == 8) __builtin_amdgcn_s_setprio(1);
-    else if (b == 12) __builtin_amdgcn_s_setprio(0);
+    if (b == 8) __builtin_amdgcn_s_setprio(2);
+    else if (b == 12) __builtin_amdgcn_s_setprio(1);
+    else if (b == 14) __builtin_amdgcn_s_setprio(0);
 }
 
 // Full 1 KiB chunk with per-lane 16-byte loads (16-byte aligned). Blocks are handled in
