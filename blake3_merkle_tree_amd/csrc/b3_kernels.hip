@@ -1310,10 +1310,18 @@ constexpr uint32_t split_lds_words() {
 template <uint32_t K>
 __global__ __launch_bounds__(kLeafLanes) void leaf_split_kernel(SplitLeafArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t lds[split_lds_words<K>()];
-    if (blockIdx.x < a.tail_wgs)
+    if (blockIdx.x < a.tail_wgs) {
         leaf_quad_wg<false>(a.tail, blockIdx.x, lds);
-    else
+    } else {
+        // At four chunks per lane the lane workgroups run four times as long as the quads
+        // beside them and set the time, but the quad workgroups, dispatched first, are the
+        // older waves and would be issued first; a higher priority for the lane workgroups
+        // lets the quads fill the cycles they leave (257 MiB 112.7 -> 110.1 us on MI355X; at
+        // one or two chunks per lane the tail is as long as the round and it lost: 65 MiB
+        // 48.3 -> 50.2 us, 129 MiB 68.3 -> 69.0 us).
+        if (K == 4) __builtin_amdgcn_s_setprio(1);
         leaf_uniform_wg<K, false, false>(a.main, blockIdx.x - a.tail_wgs, lds);
+    }
 }
 
 // The two subtrees of leaf_split_kernel's message as two segments of one tree of C lanes: the
