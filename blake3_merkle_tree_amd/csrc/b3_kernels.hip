@@ -73,8 +73,10 @@ __device__ __forceinline__ void compress_block_chained(const uint32_t (&s)[16], 
 // that start together the older one runs its whole chunk with the younger one only taking
 // the cycles it leaves idle, and the younger then runs alone, at the rate of a lone wave,
 // for most of its own chunk. Stepping a wave's priority down from 3 to 0 as it passes
-// blocks 4, 8 and 12 of its chunk lets the waves take turns every four blocks, so both keep
-// the SIMD busy until they end, together.
+// blocks 8, 12 and 14 of its chunk lets the waves take turns (over eight blocks, then four,
+// then two), so both keep the SIMD busy until they end, close together: the last phase,
+// where the older wave goes first again, is two blocks long (steps at 4, 8 and 12 left four,
+// and measured slower).
 __device__ __forceinline__ void turn_priority_at(uint32_t b) {
     if (b == 8) __builtin_amdgcn_s_setprio(2);
     else if (b == 12) __builtin_amdgcn_s_setprio(1);
